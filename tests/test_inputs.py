@@ -1,0 +1,45 @@
+"""Seeded input generator: determinism, shapes, ranges, poisoning."""
+
+import numpy as np
+import torch
+
+from transformer_attention_gqa_amd import inputs
+
+
+def test_lengths_are_seeded_and_in_range():
+    w = inputs.GQA_RAGGED_BF16
+    a = inputs.draw_lengths(w.B, *w.lens, w.seed)
+    b = inputs.draw_lengths(w.B, *w.lens, w.seed)
+    assert torch.equal(a, b) and a.dtype == torch.int32
+    assert int(a.min()) >= 1024 and int(a.max()) <= 4096
+    assert len(set(a.tolist())) > 1
+
+
+def test_decode_inputs_shapes_and_determinism():
+    w = inputs.DecodeWorkload("t", B=3, h_q=4, n_kv=2, d_h=64, S_max=40, q_dtype="bf16", kv_dtype="bf16",
+                              lens=(5, 40), seed=11)
+    a = inputs.make_decode_inputs(w)
+    b = inputs.make_decode_inputs(w)
+    assert a.q.shape == (3, 4, 64) and a.k.shape == (3, 2, 40, 64) and a.q.dtype == torch.bfloat16
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v) and torch.equal(a.q, b.q)
+    c = inputs.make_decode_inputs(w, seed=12)
+    assert not torch.equal(a.k, c.k)
+
+
+def test_fp8_inputs_have_finite_codes_and_positive_scales():
+    w = inputs.DecodeWorkload("t8", B=2, h_q=8, n_kv=2, d_h=128, S_max=33, q_dtype="bf16", kv_dtype="fp8",
+                              lens=(33, 33), seed=3)
+    x = inputs.make_decode_inputs(w)
+    for codes in (x.k, x.v):
+        c = codes.numpy()
+        assert c.dtype == np.uint8
+        assert not np.any((c & 0x7F) == 0x7F)  # no NaN codes
+    assert torch.all(x.k_scale > 0) and torch.all(x.v_scale > 0)
+
+
+def test_poisoned_tails():
+    w = inputs.DecodeWorkload("tp", B=2, h_q=2, n_kv=1, d_h=64, S_max=16, q_dtype="bf16", kv_dtype="bf16",
+                              lens=(3, 16), seed=5)
+    x = inputs.make_decode_inputs(w, seq_lens=[3, 16], poison_tail=True)
+    assert torch.isnan(x.k[0, :, 3:].float()).all() and not torch.isnan(x.k[0, :, :3].float()).any()
+    assert not torch.isnan(x.v[1].float()).any()

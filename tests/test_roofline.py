@@ -1,0 +1,56 @@
+"""Byte/flop accounting against the worked numbers the pages print."""
+
+import json
+import os
+
+import pytest
+
+from transformer_attention_gqa_amd import inputs, roofline
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_cache_sizes.json")))
+
+
+def test_mha_layer_and_model_totals():
+    g = GOLD["mha_70b_layer"]
+    per_layer = roofline.mha_kv_cache_bytes_per_layer(g["S"], 64, g["D"] // 64, g["bytes_per_elem"])
+    assert per_layer == g["bytes_per_layer"] == g["printed_MB_per_layer"] * 2 ** 20
+    # the general formula with n_kv = h, one layer, one sequence gives the same
+    assert roofline.kv_cache_bytes(2, 1, 64, 128, g["S"], 1) == per_layer
+    total = roofline.kv_cache_bytes(2, g["layers"], 64, 128, g["S"], 1)
+    assert total == g["bytes_total"] == g["printed_GB_total"] * 2 ** 30
+
+
+def test_mqa_and_gqa_fractions():
+    m = GOLD["mqa_vs_mha_h64"]
+    f = roofline.kv_fraction_of_mha(m["n_kv"], m["h"])
+    assert f == m["fraction"]
+    assert round(100 * (1 - f), 1) == m["printed_reduction_pct"]
+    g = GOLD["gqa_g8_of_64"]
+    assert roofline.kv_fraction_of_mha(g["n_kv"], g["h"]) == g["fraction"]
+    for n_kv, pct in GOLD["comparison_table_h64"]["rows"]:
+        assert round(100 * roofline.kv_fraction_of_mha(n_kv, 64), 2) == pytest.approx(pct, abs=0.006)
+    t = GOLD["mla_table_h128"]
+    full = t["h"] * t["head_dim"]
+    for name, dim, pct in t["rows"]:
+        assert round(100 * dim / full, 2) == pytest.approx(pct, abs=0.03)
+    assert GOLD["mla_table_h128"]["rows"][1][1] == 8 * 128  # GQA(g=8): 8 heads of 128
+    q = GOLD["mqa_32_heads"]
+    assert 1 / roofline.kv_fraction_of_mha(q["n_kv"], q["h"]) == q["reduction_factor"]
+
+
+def test_workload_byte_and_flop_counts():
+    w = inputs.MQA_TINY_F32
+    assert roofline.decode_kv_bytes("f32", w.n_kv, w.d_h, [128, 128]) == 131072
+    w = inputs.MQA_LONG_BF16
+    assert roofline.decode_kv_bytes("bf16", w.n_kv, w.d_h, [8192] * 64) == 268435456
+    assert roofline.decode_flops(w.h_q, w.d_h, [8192] * 64) == 8589934592
+    w = inputs.GQA_FP8KV
+    assert roofline.decode_kv_bytes("fp8", w.n_kv, w.d_h, [32768] * 32) == 2147483648
+    assert roofline.decode_scale_bytes("fp8", w.n_kv, [32768] * 32) == 67108864
+    w = inputs.GQA_PREFILL_BF16
+    fl = roofline.prefill_causal_flops(w.B, w.S, w.h_q, w.d_h)
+    assert fl == 4 * 4 * 32 * 128 * 4096 * 4097 // 2
+    assert abs(fl - 5.4989e11) / 5.4989e11 < 1e-4
+    w = inputs.GQA_RAGGED_BF16
+    lens = inputs.draw_lengths(w.B, *w.lens, w.seed)
+    assert roofline.decode_kv_bytes("bf16", w.n_kv, w.d_h, lens.tolist()) == 4096 * int(lens.sum())

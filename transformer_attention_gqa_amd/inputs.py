@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the decode and causal-prefill workloads.
+
+This module only draws random numbers and stores them in the element formats
+the library consumes.  It holds none of the attention arithmetic, and it is the
+one piece the GPU path, the tests and the CPU oracle all share.
+
+Recipe (every workload is synthetic):
+  * values: standard normal float32 draws from a `torch.Generator` seeded per
+    workload, drawn on the device that will hold the tensor;
+  * bf16 tensors: round-to-nearest-even of those draws (torch's float32 ->
+    bfloat16 cast);
+  * fp8 KV cache: per (batch, kv-head, token) row, scale = max|x| / 448 in
+    float32 (1.0 for an all-zero row), code = e4m3fn(clamp(x / scale, +-448))
+    via torch's round-to-nearest-even cast -- the "quantization-aware scaling
+    factors" reading of the KV-cache quantisation passage of the
+    "Multi-Query Attention (MQA)" glossary page;
+  * ragged lengths: integers drawn uniformly from [lo, hi] inclusive from a CPU
+    generator, so a workload's lengths are the same whichever device holds the
+    tensors;
+  * optional tail poisoning: cache rows at positions >= L_b set to NaN, so a
+    kernel that reads past a sequence's end is caught.
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import torch
+
+DTYPES = ("f32", "bf16", "fp8")
+FP8_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    h_q: int
+    n_kv: int
+    d_h: int
+    S_max: int
+    q_dtype: str  # "f32" | "bf16"
+    kv_dtype: str  # "f32" | "bf16" | "fp8"
+    lens: Tuple[int, int]  # inclusive range of L_b; (S, S) for fixed length
+    seed: int
+
+    @property
+    def G(self):
+        return self.h_q // self.n_kv
+
+    @property
+    def scale(self):
+        return 1.0 / float(self.d_h) ** 0.5
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    S: int
+    h_q: int
+    n_kv: int
+    d_h: int
+    seed: int
+    dtype: str = "bf16"
+
+    @property
+    def G(self):
+        return self.h_q // self.n_kv
+
+    @property
+    def scale(self):
+        return 1.0 / float(self.d_h) ** 0.5
+
+
+# The five synthetic workloads the library is measured on.
+MQA_TINY_F32 = DecodeWorkload("mqa_decode_tiny_f32", B=2, h_q=8, n_kv=1, d_h=64, S_max=128,
+                              q_dtype="f32", kv_dtype="f32", lens=(128, 128), seed=1)
+GQA_RAGGED_BF16 = DecodeWorkload("gqa_decode_ragged_bf16", B=16, h_q=64, n_kv=8, d_h=128, S_max=4096,
+                                 q_dtype="bf16", kv_dtype="bf16", lens=(1024, 4096), seed=2)
+MQA_LONG_BF16 = DecodeWorkload("mqa_decode_long_bf16", B=64, h_q=32, n_kv=1, d_h=128, S_max=8192,
+                               q_dtype="bf16", kv_dtype="bf16", lens=(8192, 8192), seed=3)
+GQA_PREFILL_BF16 = PrefillWorkload("gqa_prefill_causal_bf16", B=4, S=4096, h_q=32, n_kv=8, d_h=128, seed=4)
+GQA_FP8KV = DecodeWorkload("gqa_decode_fp8kv", B=32, h_q=64, n_kv=8, d_h=128, S_max=32768,
+                           q_dtype="bf16", kv_dtype="fp8", lens=(32768, 32768), seed=5)
+
+DECODE_WORKLOADS = {w.name: w for w in (MQA_TINY_F32, GQA_RAGGED_BF16, MQA_LONG_BF16, GQA_FP8KV)}
+PREFILL_WORKLOADS = {GQA_PREFILL_BF16.name: GQA_PREFILL_BF16}
+
+
+def _torch_dtype(tag):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[tag]
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def draw_lengths(B, lo, hi, seed):
+    """Ragged lengths, uniform integers in [lo, hi], from a CPU generator."""
+    g = _gen("cpu", seed * 7919 + 17)
+    if lo == hi:
+        return torch.full((B,), lo, dtype=torch.int32)
+    return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def quantize_e4m3_rows(x):
+    """float32 [..., d] -> (uint8 codes [..., d], float32 scales [...])."""
+    x = x.float()
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).float()
+    y = (x / scale[..., None]).clamp(-FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+@dataclass
+class DecodeInputs:
+    wl: DecodeWorkload
+    q: torch.Tensor  # [B, h_q, d] f32/bf16
+    k: torch.Tensor  # [B, n_kv, S_max, d] f32/bf16 or uint8 codes
+    v: torch.Tensor
+    seq_lens: torch.Tensor  # [B] int32, same device
+    k_scale: Optional[torch.Tensor] = None  # [B, n_kv, S_max] f32 (fp8 only)
+    v_scale: Optional[torch.Tensor] = None
+    extra: dict = field(default_factory=dict)
+
+
+def make_decode_inputs(wl, device="cpu", seq_lens=None, poison_tail=False, seed=None):
+    """Draw q, K/V cache (and fp8 scales) for a decode workload.
+
+    seq_lens overrides the workload's length rule (list/tensor of B ints).
+    """
+    seed = wl.seed if seed is None else seed
+    g = _gen(device, seed)
+    B, h_q, n_kv, d, S = wl.B, wl.h_q, wl.n_kv, wl.d_h, wl.S_max
+    if seq_lens is None:
+        lens = draw_lengths(B, wl.lens[0], wl.lens[1], seed)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int32).reshape(B)
+    q = torch.randn((B, h_q, d), generator=g, device=device, dtype=torch.float32).to(_torch_dtype(wl.q_dtype))
+    if wl.kv_dtype == "fp8":
+        k = torch.empty((B, n_kv, S, d), dtype=torch.uint8, device=device)
+        v = torch.empty((B, n_kv, S, d), dtype=torch.uint8, device=device)
+        ks = torch.empty((B, n_kv, S), dtype=torch.float32, device=device)
+        vs = torch.empty((B, n_kv, S), dtype=torch.float32, device=device)
+        for b in range(B):  # per batch entry to bound temporary memory
+            xk = torch.randn((n_kv, S, d), generator=g, device=device, dtype=torch.float32)
+            k[b], ks[b] = quantize_e4m3_rows(xk)
+            del xk
+            xv = torch.randn((n_kv, S, d), generator=g, device=device, dtype=torch.float32)
+            v[b], vs[b] = quantize_e4m3_rows(xv)
+            del xv
+        inp = DecodeInputs(wl, q, k, v, lens.to(device), ks, vs)
+    else:
+        dt = _torch_dtype(wl.kv_dtype)
+        k = torch.empty((B, n_kv, S, d), dtype=dt, device=device)
+        v = torch.empty((B, n_kv, S, d), dtype=dt, device=device)
+        for b in range(B):
+            k[b] = torch.randn((n_kv, S, d), generator=g, device=device, dtype=torch.float32).to(dt)
+            v[b] = torch.randn((n_kv, S, d), generator=g, device=device, dtype=torch.float32).to(dt)
+        inp = DecodeInputs(wl, q, k, v, lens.to(device))
+    if poison_tail:
+        poison_cache_tails(inp)
+    return inp
+
+
+def poison_cache_tails(inp):
+    """Fill cache rows at positions >= L_b with NaN (codes 0x7F for fp8)."""
+    S = inp.wl.S_max
+    for b in range(inp.wl.B):
+        n = int(min(max(int(inp.seq_lens[b]), 0), S))
+        if n >= S:
+            continue
+        if inp.wl.kv_dtype == "fp8":
+            inp.k[b, :, n:, :] = 0x7F
+            inp.v[b, :, n:, :] = 0x7F
+            inp.k_scale[b, :, n:] = float("nan")
+            inp.v_scale[b, :, n:] = float("nan")
+        else:
+            inp.k[b, :, n:, :] = float("nan")
+            inp.v[b, :, n:, :] = float("nan")
+
+
+@dataclass
+class PrefillInputs:
+    wl: PrefillWorkload
+    q: torch.Tensor  # [B, S, h_q, d] bf16
+    k: torch.Tensor  # [B, S, n_kv, d] bf16
+    v: torch.Tensor
+
+
+def make_prefill_inputs(wl, device="cpu", seed=None):
+    seed = wl.seed if seed is None else seed
+    g = _gen(device, seed)
+    dt = _torch_dtype(wl.dtype)
+    q = torch.randn((wl.B, wl.S, wl.h_q, wl.d_h), generator=g, device=device, dtype=torch.float32).to(dt)
+    k = torch.randn((wl.B, wl.S, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32).to(dt)
+    v = torch.randn((wl.B, wl.S, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32).to(dt)
+    return PrefillInputs(wl, q, k, v)
+
+
+def stored_numpy(t):
+    """A tensor's stored encoding as a numpy array: bf16 -> uint16 bit patterns,
+    fp8 codes stay uint8, float32/int32 as is.  (Bit views, no arithmetic.)"""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()
