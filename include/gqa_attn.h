@@ -1,0 +1,162 @@
+/*
+ * gqa_attn.h -- exact grouped-query attention on AMD MI355X (gfx950).
+ *
+ * C ABI of libgqa_attn.so.  Plain pointers and sizes only.
+ *
+ * The operation ("Evolution of AI Attention Mechanisms: A Complete Guide from
+ * MHA to MLA and Flash Attention", sections "MHA Mathematical Formulation" and
+ * "GQA Implementation"; "Multi-query attention", section "Formulation"):
+ * each of h_q query heads attends to one of n_kv shared K/V heads.  Query head
+ * j uses K/V head j / G, where G = h_q / n_kv is the group size: the GQA module
+ * repeats K/V head g for query heads g*G .. g*G+G-1.  G = 1 is MHA and
+ * G = h_q is MQA.  For each query row,
+ *
+ *     out = softmax(scale * q . K^T) V        (over the visible keys)
+ *
+ * computed exactly (up to floating-point rounding order) with a running max
+ * and running sum, so the score matrix is never written to memory ("Flash
+ * Attention Principle" on the first page).
+ *
+ * Conventions shared by every call
+ *  - Every tensor pointer is caller-owned device memory on the current HIP
+ *    device, densely packed in the stated layout (innermost index last), and
+ *    aligned to 16 bytes.  The library never allocates, frees or synchronises,
+ *    and keeps no pointer after the call returns.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and runs
+ *    asynchronously; the call returns once the kernels are enqueued.
+ *  - Arguments are checked on the host before any HIP call.  A bad argument
+ *    returns a status code and enqueues nothing.  A launch failure returns
+ *    GQA_ERR_HIP (gqa_last_hip_error() gives the HIP message).  Faults inside
+ *    a kernel surface at the caller's next synchronisation.
+ *  - Calls are stateless and may run concurrently on different streams as
+ *    long as each decode call has its own workspace.
+ *  - `out` must not overlap any input or the workspace.
+ *  - Supported head dimensions: d_h = 64 or 128.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same definition as in hip_runtime_api.h; repeating an identical typedef is
+ * valid C11/C++, so this header stands alone for plain C callers. */
+typedef struct ihipStream_t* hipStream_t;
+
+/* Element types. */
+enum {
+  GQA_F32 = 0,      /* IEEE binary32                                        */
+  GQA_BF16 = 1,     /* bfloat16 (upper half of binary32)                    */
+  GQA_FP8_E4M3 = 2  /* OCP 8-bit float E4M3 ("e4m3fn": bias 7, max 448,     */
+                    /* no infinities, NaN = S.1111.111)                     */
+};
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  GQA_ERR_SHAPE = 2,     /* a dimension <= 0, h_q % n_kv != 0, bad d_h, ...   */
+  GQA_ERR_DTYPE = 3,     /* unsupported element-type combination              */
+  GQA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
+  GQA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
+  GQA_ERR_HIP = 6        /* a HIP launch or query failed                      */
+} gqa_status;
+
+/* ---------------------------------------------------------------- decode --
+ * One autoregressive step over a KV cache.  The new token's K/V has already
+ * been written into the cache, so it attends to itself: the GQA and MHA
+ * modules concatenate the cache before attention ("GQA Implementation").
+ * The decode step is softmax(Q_all K_shared^T) V_shared for the heads of a
+ * group ("Multi-Query Attention (MQA)" glossary, "Kernel Optimization").
+ *
+ * Shapes (row-major, innermost last):
+ *   q        [B, h_q, d_h]             q_dtype (F32 or BF16)
+ *   k_cache  [B, n_kv, S_max, d_h]     kv_dtype -- the cache layout after the
+ *   v_cache  [B, n_kv, S_max, d_h]     modules' view(B,S,n_kv,d).transpose(1,2)
+ *   k_scale  [B, n_kv, S_max] float32  FP8 cache only: one dequantisation
+ *   v_scale  [B, n_kv, S_max] float32  factor per (token, kv-head) row;
+ *                                      value = e4m3(code) * scale ("KV cache
+ *                                      quantization" in the MQA glossary).
+ *                                      NULL for F32/BF16 caches.
+ *   seq_lens [B] int32 (device)        L_b = visible cache positions 0..L_b-1
+ *                                      of sequence b.  Read on the device
+ *                                      only: values are clamped to [0, S_max];
+ *                                      L_b = 0 yields a zero output row.
+ *   out      [B, h_q, d_h]             q_dtype
+ * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ * Accumulation is float32 throughout.
+ *
+ * Sequence split: the keys of each (sequence, kv-head) are cut into n_split
+ * chunks processed in parallel; each chunk leaves an unnormalised partial
+ * (O_s, m_s, l_s) in the workspace and a combine kernel merges them:
+ *   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+ */
+typedef struct gqa_decode_desc {
+  int32_t B, h_q, n_kv, S_max, d_h;
+  int32_t q_dtype, kv_dtype; /* GQA_F32 / GQA_BF16 / GQA_FP8_E4M3           */
+  int32_t n_split;           /* 0: library heuristic.  > 0: requested number
+                                of sequence chunks (rounded so that each chunk
+                                is a whole number of 32-token tiles; the
+                                effective count is attn_decode_num_splits()). */
+} gqa_decode_desc;
+
+/* Effective number of sequence chunks for this descriptor, or -1 if the
+ * descriptor is invalid.  Host-only, deterministic. */
+int32_t attn_decode_num_splits(const gqa_decode_desc* d);
+
+/* Bytes of device workspace attn_decode needs for this descriptor (0 if the
+ * descriptor is invalid).  Host-only, deterministic. */
+size_t attn_decode_workspace_bytes(const gqa_decode_desc* d);
+
+/* Full decode step: split kernel then combine kernel, both on `stream`.
+ * workspace: caller-owned device memory of at least
+ * attn_decode_workspace_bytes(d) bytes; it must stay untouched until the
+ * stream reaches the end of this call's work. */
+gqa_status attn_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two halves of attn_decode, for callers that want to place other work
+ * between them -- e.g. exchange partials between devices that each hold a
+ * slice of a long sequence before combining.  attn_decode_partials writes the
+ * per-chunk partials into `workspace`; attn_decode_combine reads them and
+ * writes `out`.  Both take the same descriptor, seq_lens and workspace. */
+gqa_status attn_decode_partials(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                                const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+gqa_status attn_decode_combine(const gqa_decode_desc* d, const int32_t* seq_lens, const void* workspace,
+                               size_t workspace_bytes, void* out, hipStream_t stream);
+
+/* ------------------------------------------------------- causal prefill --
+ * Causal self-attention over whole prompts, the mode of the library call
+ * flash_attn_func(q, k, v, causal=True, softmax_scale=...) in "Flash
+ * Attention Usage": query row r sees keys 0..r (diagonal included).
+ *
+ * Shapes (token-major, the layout handed to flash_attn_func):
+ *   q, out   [B, S, h_q, d_h]   bfloat16
+ *   k, v     [B, S, n_kv, d_h]  bfloat16
+ * dtype must be GQA_BF16.  QK^T and PV run on bf16 matrix cores with float32
+ * accumulation; the running max and sum are float32; out is rounded to bf16.
+ */
+typedef struct gqa_prefill_desc {
+  int32_t B, S, h_q, n_kv, d_h;
+  int32_t dtype; /* GQA_BF16 */
+} gqa_prefill_desc;
+
+gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const void* k, const void* v, float scale,
+                               void* out, hipStream_t stream);
+
+/* ------------------------------------------------------------- errors --- */
+/* Static, human-readable name of a status code. */
+const char* gqa_status_string(gqa_status s);
+/* Message of the last HIP error seen by this thread's calls ("" if none). */
+const char* gqa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,92 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the oracle on
+the same seeded inputs and compare element by element."""
+
+import numpy as np
+import torch
+
+import oracle
+from transformer_attention_gqa_amd import binding, inputs
+
+# max-abs-error bars, by the K/V element type the path reads
+TOL = {"f32": 1e-3, "bf16": 2e-2, "fp8": 5e-2}
+
+
+def to_f64(t):
+    """Stored tensor -> exact float64 numpy values (via the oracle's decoders)."""
+    arr = inputs.stored_numpy(t)
+    if arr.dtype == np.uint16:
+        return oracle.bf16_bits_to_f64(arr)
+    if arr.dtype == np.float32:
+        return arr.astype(np.float64)
+    raise TypeError(arr.dtype)
+
+
+def cache_f64(inp, b, g):
+    """K/V slab (b, g) of a decode input as float64 values [S_max, d] each."""
+    if inp.wl.kv_dtype == "fp8":
+        k = oracle.dequantize_fp8_cache(inputs.stored_numpy(inp.k[b, g]), inputs.stored_numpy(inp.k_scale[b, g]))
+        v = oracle.dequantize_fp8_cache(inputs.stored_numpy(inp.v[b, g]), inputs.stored_numpy(inp.v_scale[b, g]))
+        return k, v
+    return to_f64(inp.k[b, g]), to_f64(inp.v[b, g])
+
+
+def run_decode(inp, n_split=0, out=None, workspace=None):
+    wl = inp.wl
+    return binding.attn_decode(inp.q, inp.k, inp.v, inp.seq_lens, wl.scale, out=out, k_scale=inp.k_scale,
+                               v_scale=inp.v_scale, workspace=workspace, n_split=n_split)
+
+
+def oracle_decode_pairs(inp, pairs):
+    """Oracle outputs for the (b, j) pairs, building float64 slabs only as needed."""
+    wl = inp.wl
+    q = to_f64(inp.q)
+    lens = inp.seq_lens.cpu().tolist()
+    G = wl.G
+    cache = {}
+    rows = []
+    for b, j in pairs:
+        g = j // G
+        if (b, g) not in cache:
+            cache[(b, g)] = cache_f64(inp, b, g)
+        k, v = cache[(b, g)]
+        n = int(min(max(lens[b], 0), wl.S_max))
+        rows.append(oracle.attend_one_row(q[b, j], k[:n], v[:n], wl.scale))
+    return np.stack(rows)
+
+
+def oracle_decode_full(inp):
+    wl = inp.wl
+    pairs = [(b, j) for b in range(wl.B) for j in range(wl.h_q)]
+    return oracle_decode_pairs(inp, pairs).reshape(wl.B, wl.h_q, wl.d_h)
+
+
+def max_err(gpu_out, ref):
+    got = gpu_out.detach().float().cpu().double().numpy()
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    return float(np.max(np.abs(got - ref))) if ref.size else 0.0
+
+
+def prefill_f64(inp):
+    return to_f64(inp.q), to_f64(inp.k), to_f64(inp.v)
+
+
+def sample_pairs(B, h_q, n, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(b, int(rng.integers(h_q))) for b in range(B)}
+    pairs |= {(0, 0), (B - 1, h_q - 1)}
+    while len(pairs) < n:
+        pairs.add((int(rng.integers(B)), int(rng.integers(h_q))))
+    return sorted(pairs)
+
+
+def sample_rows(B, S, h_q, n, seed):
+    rng = np.random.default_rng(seed)
+    trip = {(0, 0, 0), (B - 1, S - 1, h_q - 1), (0, S - 1, 0), (B - 1, 63, h_q // 2), (0, 64, 1 % h_q)}
+    while len(trip) < n:
+        trip.add((int(rng.integers(B)), int(rng.integers(S)), int(rng.integers(h_q))))
+    return sorted(trip)
+
+
+def sync():
+    torch.cuda.synchronize()

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_attention_gqa_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+ALIGNED = 0x10000          # fake, never dereferenced: validation fails first
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+|gqa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def dd(B=2, h_q=8, n_kv=2, S=64, d=128, qt=1, kt=1, ns=0):
+    return binding.gqa_decode_desc(B, h_q, n_kv, S, d, qt, kt, ns)
+
+
+def call_decode(lib, desc, q=ALIGNED, k=ALIGNED, v=ALIGNED, ks=None, vs=None, lens=ALIGNED, out=ALIGNED,
+                ws=ALIGNED, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(ctypes.byref(desc)) if desc is not None else 0
+    p = ctypes.byref(desc) if desc is not None else None
+    return lib.attn_decode(p, q, k, v, ks, vs, lens, 1.0, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(B=0), 2), (dict(h_q=-1), 2), (dict(n_kv=0), 2), (dict(S=0), 2), (dict(d=96), 2), (dict(d=256), 2),
+    (dict(h_q=12, n_kv=8), 2), (dict(ns=-1), 2),
+    (dict(qt=0, kt=1), 3), (dict(qt=1, kt=0), 3), (dict(qt=0, kt=2), 3), (dict(qt=2, kt=2), 3), (dict(qt=7), 3),
+])
+def test_decode_descriptor_errors(lib, bad, code):
+    desc = dd(**bad)
+    assert call_decode(lib, desc) == code
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(desc)) == 0
+    assert lib.attn_decode_num_splits(ctypes.byref(desc)) == -1
+
+
+def test_decode_pointer_errors(lib):
+    assert call_decode(lib, None) == 1
+    assert call_decode(lib, dd(), q=None) == 1
+    assert call_decode(lib, dd(), lens=None) == 1
+    assert call_decode(lib, dd(), out=None) == 1
+    assert call_decode(lib, dd(kt=2), ks=None, vs=ALIGNED) == 1   # fp8 cache needs scales
+    assert call_decode(lib, dd(), k=MISALIGNED) == 4
+    assert call_decode(lib, dd(), out=MISALIGNED) == 4
+    assert call_decode(lib, dd(), lens=ALIGNED + 2) == 4
+    assert call_decode(lib, dd(kt=2), ks=MISALIGNED, vs=ALIGNED) == 4
+
+
+def test_decode_workspace_errors(lib):
+    desc = dd()
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(desc))
+    assert need > 0
+    assert call_decode(lib, desc, ws=None) == 5
+    assert call_decode(lib, desc, ws_bytes=need - 1) == 5
+    assert call_decode(lib, desc, ws=MISALIGNED) == 4
+    assert lib.attn_decode_partials(ctypes.byref(desc), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
+                                    ALIGNED, need - 4, None) == 5
+    assert lib.attn_decode_combine(ctypes.byref(desc), ALIGNED, ALIGNED, need - 4, ALIGNED, None) == 5
+    assert lib.attn_decode_combine(ctypes.byref(desc), ALIGNED, ALIGNED, need, None, None) == 1
+
+
+def test_split_plan_is_deterministic_and_honours_requests(lib):
+    base = dd(B=16, h_q=64, n_kv=8, S=4096)
+    a = lib.attn_decode_workspace_bytes(ctypes.byref(base))
+    assert a == lib.attn_decode_workspace_bytes(ctypes.byref(base))
+    for req in (1, 2, 7, 128, 100000):
+        desc = dd(B=16, h_q=64, n_kv=8, S=4096, ns=req)
+        ns = lib.attn_decode_num_splits(ctypes.byref(desc))
+        assert 1 <= ns <= min(req, 4096 // 32)
+        # each chunk is a whole number of 32-token tiles and the chunks cover S_max
+        chunk = -(-4096 // ns)
+        assert ns * chunk >= 4096
+        ws = lib.attn_decode_workspace_bytes(ctypes.byref(desc))
+        assert ws >= 16 * 64 * ns * (128 + 2) * 4
+
+
+def test_prefill_errors(lib):
+    def pd(B=1, S=16, h_q=4, n_kv=2, d=128, dt=1):
+        return binding.gqa_prefill_desc(B, S, h_q, n_kv, d, dt)
+
+    def call(desc, q=ALIGNED, k=ALIGNED, v=ALIGNED, out=ALIGNED):
+        return lib.attn_prefill_causal(ctypes.byref(desc) if desc is not None else None, q, k, v, 0.1, out, None)
+
+    assert call(None) == 1
+    assert call(pd(S=0)) == 2
+    assert call(pd(h_q=6, n_kv=4)) == 2
+    assert call(pd(d=80)) == 2
+    assert call(pd(dt=0)) == 3
+    assert call(pd(dt=2)) == 3
+    assert call(pd(), v=None) == 1
+    assert call(pd(), out=MISALIGNED) == 4
+
+
+def test_status_strings(lib):
+    for code, name in binding.STATUS.items():
+        assert lib.gqa_status_string(code).decode().startswith(name)
+    assert lib.gqa_last_hip_error().decode() == ""
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library.__wrapped__(str(tmp_path / "nope.so")) if hasattr(binding.load_library, "__wrapped__") \
+            else _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = binding._lib
+    binding._lib = None
+    try:
+        return binding.load_library(path)
+    finally:
+        binding._lib = saved

@@ -1,0 +1,195 @@
+"""ctypes binding of libgqa_attn.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks tensor metadata, fills the descriptor struct,
+passes raw device pointers and the current HIP stream, and raises GqaError on a
+non-zero status.  PyTorch provides device memory and the stream.
+
+The library is loaded from this package directory.  If it is missing the import
+of the functions still works, but every call raises: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_NAME = "libgqa_attn.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE", 4: "GQA_ERR_ALIGN",
+          5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP"}
+EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
+            "attn_decode_combine", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+class gqa_decode_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("S_max", ctypes.c_int32), ("d_h", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+
+
+class gqa_prefill_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and return the ctypes handle; raises if the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{LIB_NAME} is not built ({path} missing); run "
+                           "`python -m transformer_attention_gqa_amd.build` first")
+    lib = ctypes.CDLL(path)
+    vp, cp, i32, f32, sz = ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    dd, pd = ctypes.POINTER(gqa_decode_desc), ctypes.POINTER(gqa_prefill_desc)
+    lib.attn_decode_num_splits.argtypes, lib.attn_decode_num_splits.restype = [dd], i32
+    lib.attn_decode_workspace_bytes.argtypes, lib.attn_decode_workspace_bytes.restype = [dd], sz
+    lib.attn_decode.argtypes = [dd, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_partials.argtypes = [dd, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
+    lib.attn_decode_partials.restype = ctypes.c_int
+    lib.attn_decode_combine.argtypes = [dd, vp, vp, sz, vp, vp]
+    lib.attn_decode_combine.restype = ctypes.c_int
+    lib.attn_prefill_causal.argtypes = [pd, vp, vp, vp, f32, vp, vp]
+    lib.attn_prefill_causal.restype = ctypes.c_int
+    lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [ctypes.c_int], cp
+    lib.gqa_last_hip_error.argtypes, lib.gqa_last_hip_error.restype = [], cp
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        lib = load_library()
+        msg = lib.gqa_status_string(status).decode()
+        if status == 6:
+            msg += ": " + lib.gqa_last_hip_error().decode()
+        raise GqaError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return GQA_F32
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return GQA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _require(t, name, ndim):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def decode_desc(q, k_cache, n_split=0):
+    """Descriptor for q [B, h_q, d] and cache [B, n_kv, S_max, d]."""
+    B, h_q, d = q.shape
+    n_kv, s_max = k_cache.shape[1], k_cache.shape[2]
+    return gqa_decode_desc(B, h_q, n_kv, s_max, d, _dtype_code(q), _dtype_code(k_cache), n_split)
+
+
+def attn_decode_num_splits(desc):
+    return load_library().attn_decode_num_splits(ctypes.byref(desc))
+
+
+def attn_decode_workspace_bytes(desc):
+    return load_library().attn_decode_workspace_bytes(ctypes.byref(desc))
+
+
+def _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale):
+    _require(q, "q", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have the same shape and dtype")
+    if k_cache.shape[0] != q.shape[0] or k_cache.shape[3] != q.shape[2]:
+        raise ValueError("cache [B, n_kv, S_max, d] does not match q [B, h_q, d]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
+    if _dtype_code(k_cache) == GQA_FP8_E4M3:
+        for name, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None or s.dtype != torch.float32 or tuple(s.shape) != tuple(k_cache.shape[:3]) \
+                    or not s.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 tensor of shape [B, n_kv, S_max]")
+
+
+def _workspace(desc, device, workspace):
+    need = attn_decode_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def attn_decode(q, k_cache, v_cache, seq_lens, scale, out=None, k_scale=None, v_scale=None, workspace=None,
+                n_split=0, stream=None):
+    """out[B, h_q, d] = GQA decode step (split + combine kernels)."""
+    _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
+    desc = decode_desc(q, k_cache, n_split)
+    if out is None:
+        out = torch.empty_like(q)
+    workspace, ws_bytes = _workspace(desc, q.device, workspace)
+    _check(load_library().attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                      _ptr(v_scale), _ptr(seq_lens), float(scale), _ptr(out), _ptr(workspace),
+                                      ws_bytes, _stream(stream)))
+    return out
+
+
+def attn_decode_partials(q, k_cache, v_cache, seq_lens, scale, workspace, k_scale=None, v_scale=None, n_split=0,
+                         stream=None):
+    """Split kernel only: per-chunk partials into `workspace`."""
+    _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
+    desc = decode_desc(q, k_cache, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().attn_decode_partials(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                               _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens), float(scale),
+                                               _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def attn_decode_combine(q, k_cache, seq_lens, workspace, out, n_split=0, stream=None):
+    """Combine kernel only: partials in `workspace` -> out.  q/k_cache give shapes."""
+    desc = decode_desc(q, k_cache, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().attn_decode_combine(ctypes.byref(desc), _ptr(seq_lens), _ptr(workspace), ws_bytes,
+                                              _ptr(out), _stream(stream)))
+    return out
+
+
+def attn_prefill_causal(q, k, v, scale, out=None, stream=None):
+    """out[B, S, h_q, d] = causal GQA attention over q [B,S,h_q,d], k/v [B,S,n_kv,d] (bf16)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, 4)
+    B, S, h_q, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != S or k.shape[3] != d:
+        raise ValueError("k/v must be [B, S, n_kv, d] matching q [B, S, h_q, d]")
+    desc = gqa_prefill_desc(B, S, h_q, k.shape[2], d, _dtype_code(q))
+    if out is None:
+        out = torch.empty_like(q)
+    _check(load_library().attn_prefill_causal(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(scale),
+                                              _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 attention kernels.
+//
+// Register layouts of the bf16 matrix-core instructions used here (verified on
+// gfx950 hardware, lane l of a 64-wide wavefront):
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds A[l % 16][8*(l/16) .. 8*(l/16)+7]
+//     B: lane l holds B[8*(l/16) .. +7][l % 16]
+//     D: lane l holds D[4*(l/16) + i][l % 16], i = 0..3
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l % 32][8*(l/32) .. +7]
+//     B: lane l holds B[8*(l/32) .. +7][l % 32]
+//     D: lane l holds D[8*(r/4) + 4*(l/32) + r%4][l % 32], r = 0..15
+// ds_read_b64_tr_b16 (LDS transpose read): within each group of 16 lanes,
+//   if lane i reads the 8 bytes E[i][0..3] at its address, lane i receives
+//   element j = E[4*j + i/4][i % 4].  So when lane s of the group points at
+//   row (r0 + s/4), columns c0 + 4*(s%4) .. +3 of a row-major bf16 tile, lane i
+//   receives column c0 + i of rows r0 .. r0+3: a 4x16 block read transposed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+
+// Two float32 -> packed bf16x2 (round to nearest even; lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Four OCP e4m3 codes (one dword) -> four bf16 values (exact: every e4m3 value
+// is a bf16 value).  Returns two dwords of packed bf16.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+  u32x2 r;
+  r[0] = __builtin_bit_cast(uint32_t, lo);
+  r[1] = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+
+// LDS pointer helpers.
+template <typename T>
+__device__ __forceinline__ T lds_load(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(void* p, const T& v) {
+  *reinterpret_cast<T*>(p) = v;
+}
+
+// 4 bf16 of a column block, read transposed (see the layout note above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Compiler-only barrier for LDS traffic private to one wavefront: a wave's LDS
+// instructions execute in issue order, so keeping the compiler from moving
+// them across this point is all that is needed.
+__device__ __forceinline__ void wave_lds_fence() { __asm__ __volatile__("" ::: "memory"); }
+
+__device__ __forceinline__ u32x4 load_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+}  // namespace gqa

@@ -1,0 +1,281 @@
+// Causal prefill kernel (bf16 in, float32 statistics, bf16 out).
+//
+// Computes, for every batch entry b, query head j (K/V head g = j / G) and
+// query row r, softmax over keys 0..r of scale * q_r . k_c, applied to V --
+// the causal mode of the flash_attn_func call in "Flash Attention Usage"
+// ("Evolution of AI Attention Mechanisms"), token-major [B, S, H, d] layout.
+// The score matrix is never written to memory: K and V move through LDS in
+// 64-key tiles, the scores live in registers, and a running max / running sum
+// per query row rescales the output accumulator ("Flash Attention Principle":
+// tiled computation, softmax on chip, only the final O written back).
+//
+// Work decomposition (MI355X-specific, not the pages' GPU):
+//  * a workgroup of 4 wavefronts serves HC query heads of ONE K/V group over
+//    32*(4/HC) query rows, so every K/V tile it stages in LDS feeds 4 waves
+//    (GQA: the G heads of a group read the same K/V);
+//  * each wave owns 32 query rows of one head: S^T[key][query] = K Q^T and
+//    O^T[d][query] += V^T P^T on v_mfma_f32_32x32x16_bf16.  The key order in
+//    the PV product is permuted so the score accumulator registers are the B
+//    operand as they stand, and V is read transposed with ds_read_b64_tr_b16;
+//    every per-row statistic is then lane-local except one exchange with the
+//    lane 32 apart;
+//  * K/V tiles are double-buffered: the next tile's global loads are in flight
+//    while the current one feeds the matrix cores;
+//  * key tiles entirely above the diagonal are never visited (about half the
+//    work of the dense product); only tiles crossing it apply the mask;
+//  * workgroups are numbered so that each of the 8 XCDs (own L2 each) works
+//    through a contiguous range of (batch, K/V head) groups -- their K/V then
+//    stays in that XCD's L2 -- and within a group the longest (latest) query
+//    blocks start first.
+#include "gqa_device.h"
+#include "gqa_launch.h"
+
+namespace gqa {
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float qk_scale_log2;
+  int B, S, h_q, n_kv;
+  int n_qb, n_hc, n_wg, n_wg_pad;
+};
+
+constexpr int kBN = 64;  // keys per tile
+constexpr int kNumXcd = 8;
+
+template <int D, int HC>
+__global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs a) {
+  constexpr int RB = 4 / HC;     // 32-row blocks per head in one workgroup
+  constexpr int BM = 32 * RB;    // query rows per workgroup
+  constexpr int CH = D / 8;      // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;     // k-steps of the score product
+  constexpr int NT = D / 32;     // 32-wide d tiles of the PV product
+  constexpr int TILE_BYTES = kBN * D * 2;
+  constexpr int NLD = TILE_BYTES / (256 * 16);  // 16-byte loads per thread per tensor
+  constexpr int LROWS = 256 / CH;               // rows covered by one load instruction
+  __shared__ __attribute__((aligned(16))) char sk[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sv[2][TILE_BYTES];
+
+  // ---- XCD-aware, heavy-first workgroup -> work mapping
+  const int n = blockIdx.x;
+  const int per_xcd = a.n_wg_pad / kNumXcd;
+  const int wl = (n % kNumXcd) * per_xcd + n / kNumXcd;
+  if (wl >= a.n_wg) return;
+  const int grp = wl / a.n_qb;
+  const int qb = a.n_qb - 1 - (wl - grp * a.n_qb);
+  const int hc = grp % a.n_hc;
+  const int g = (grp / a.n_hc) % a.n_kv;
+  const int b = grp / (a.n_hc * a.n_kv);
+  const int G = a.h_q / a.n_kv;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int h2 = lane >> 5;
+  const int head = g * G + hc * HC + wave / RB;
+  const int row0 = qb * BM + (wave % RB) * 32;
+  const int qrow = row0 + l32;  // this lane's query row
+  const int S = a.S;
+  const size_t q_row_stride = (size_t)a.h_q * D;   // elements between consecutive tokens of q/out
+  const size_t kv_row_stride = (size_t)a.n_kv * D;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): Q[qrow][16ks + 8h2 .. +7]
+  u32x4 qf[KS];
+  {
+    const uint16_t* qp = a.q + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow < S) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      qf[ks] = v;
+    }
+  }
+
+  const int row_end = min(qb * BM + BM, S);        // exclusive, over the whole workgroup
+  const int n_tiles = (row_end - 1) / kBN + 1;     // key tiles 0 .. n_tiles-1
+  const int wave_last_row = min(row0 + 31, S - 1);
+
+  const uint16_t* kbase = a.k + (size_t)b * S * kv_row_stride + (size_t)g * D;
+  const uint16_t* vbase = a.v + (size_t)b * S * kv_row_stride + (size_t)g * D;
+  const int ld_row = tid / CH;
+  const int ld_chunk = tid % CH;
+
+  u32x4 kreg[NLD], vreg[NLD];
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int key = j * kBN + u * LROWS + ld_row;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < S) {
+        const size_t off = (size_t)key * kv_row_stride + ld_chunk * 8;
+        kv = *reinterpret_cast<const u32x4*>(kbase + off);
+        vv = *reinterpret_cast<const u32x4*>(vbase + off);
+      }
+      kreg[u] = kv;
+      vreg[u] = vv;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int r = u * LROWS + ld_row;
+      const int pc = ld_chunk ^ (r % CH);
+      lds_store(sk[buf] + r * (2 * D) + (pc << 4), kreg[u]);
+      lds_store(sv[buf] + r * (2 * D) + (pc << 4), vreg[u]);
+    }
+  };
+
+  f32x16 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
+  float m = kNegInf, l = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const int key0 = j * kBN;
+    // this wave's rows all precede the tile: nothing to do but keep in step
+    if (key0 <= wave_last_row) {
+      const char* kt = sk[buf];
+      const char* vt = sv[buf];
+      // ---- S^T for the two 32-key halves
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
+        const int krow = 32 * kh + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kf = lds_load<u32x4>(kt + krow * (2 * D) + (((2 * ks + h2) ^ (krow % CH)) << 4));
+          sacc[kh] = mfma32(kf, qf[ks], sacc[kh]);
+        }
+      }
+      // ---- online softmax (row = this lane's query; keys split with lane^32)
+      const bool diag = key0 + kBN - 1 > row0;
+      float mt = kNegInf;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kh][r] * a.qk_scale_log2;
+          if (diag) {
+            const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            x = key > qrow ? kNegInf : x;
+          }
+          sacc[kh][r] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = wave_max_xor(mt, 32);
+      const float m_new = fmaxf(m, mt);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(sacc[kh][r] - m_use);
+          sacc[kh][r] = p;
+          psum += p;
+        }
+      l = l * alpha + psum;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+      // ---- O^T += V^T P^T, 4 k-steps of 16 keys
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f32x16& sp = sacc[p >> 1];
+        const int rb = 8 * (p & 1);
+        const u32x4 pf = {pack_bf16x2(sp[rb + 0], sp[rb + 1]), pack_bf16x2(sp[rb + 2], sp[rb + 3]),
+                          pack_bf16x2(sp[rb + 4], sp[rb + 5]), pack_bf16x2(sp[rb + 6], sp[rb + 7])};
+        const int gi = lane >> 4, s16 = lane & 15;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = 32 * nt + 16 * (gi & 1) + 4 * (s16 & 3);
+          const int c = col >> 3, w = col & 7;
+          const int ra = 16 * p + 4 * h2 + (s16 >> 2);
+          const int rbw = ra + 8;
+          const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ (ra % CH)) << 4) + 2 * w);
+          const u32x2 vb = lds_read_tr16(vt + rbw * (2 * D) + ((c ^ (rbw % CH)) << 4) + 2 * w);
+          const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
+          o[nt] = mfma32(vf, pf, o[nt]);
+        }
+      }
+    }
+    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l -> bf16, rows < S only
+  const float lt = l + __shfl_xor(l, 32, 64);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qrow < S) {
+    uint16_t* op = a.out + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * nt + 8 * rq + 4 * h2;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[nt][4 * rq + 0] * inv, o[nt][4 * rq + 1] * inv);
+        w[1] = pack_bf16x2(o[nt][4 * rq + 2] * inv, o[nt][4 * rq + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d0) = w;
+      }
+  }
+}
+
+static int gcd_int(int x, int y) {
+  while (y) {
+    const int t = x % y;
+    x = y;
+    y = t;
+  }
+  return x;
+}
+
+hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
+                                 int S, int h_q, int n_kv, int D, hipStream_t stream) {
+  const int G = h_q / n_kv;
+  const int HC = gcd_int(G, 4);
+  const int BM = 32 * (4 / HC);
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.qk_scale_log2 = qk_scale_log2;
+  a.B = B;
+  a.S = S;
+  a.h_q = h_q;
+  a.n_kv = n_kv;
+  a.n_qb = (S + BM - 1) / BM;
+  a.n_hc = G / HC;
+  a.n_wg = B * n_kv * a.n_hc * a.n_qb;
+  a.n_wg_pad = (a.n_wg + kNumXcd - 1) / kNumXcd * kNumXcd;
+  const dim3 grid(a.n_wg_pad), block(256);
+#define GQA_LAUNCH_PREFILL(DD, HH) hipLaunchKernelGGL((gqa_prefill_causal_kernel<DD, HH>), grid, block, 0, stream, a)
+  if (D == 128) {
+    if (HC == 4) GQA_LAUNCH_PREFILL(128, 4);
+    else if (HC == 2) GQA_LAUNCH_PREFILL(128, 2);
+    else GQA_LAUNCH_PREFILL(128, 1);
+  } else {
+    if (HC == 4) GQA_LAUNCH_PREFILL(64, 4);
+    else if (HC == 2) GQA_LAUNCH_PREFILL(64, 2);
+    else GQA_LAUNCH_PREFILL(64, 1);
+  }
+#undef GQA_LAUNCH_PREFILL
+  return hipGetLastError();
+}
+
+}  // namespace gqa
