@@ -1,0 +1,466 @@
+"""Benchmark of the GQA attention library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only-main]
+                    [--no-cpu-baseline] [--no-graph]
+
+A step is one attn_decode call (split kernel + combine kernel) over the whole
+gqa_decode_ragged_bf16 workload (B=16, h_q=64, n_kv=8, d_h=128, ragged
+L_b in [1024, 4096]); with inputs resident in HBM the timed region replays a
+HIP graph of K such steps, bracketed by device synchronisations.  The KV cache
+is held in several copies that the steps rotate through, so the 256 MB
+Infinity Cache cannot serve one step's reads from the previous step.
+
+value    = KV bytes per step / step time  (KV bytes = 2 * b * n_kv * d_h * sum L_b)
+roofline = the split kernel alone: KV bytes / its mean launch duration, timed
+           with HIP events recorded on the stream the kernel runs on, against
+           the 8 TB/s HBM peak.
+Also reported (same JSON line, "workloads"): the other decode workloads and
+the causal prefill (TFLOP/s against the 2.5 PFLOP/s bf16 matrix peak), each
+with its own roofline, and the fp64 CPU oracle timed on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from transformer_attention_gqa_amd import binding, inputs, roofline  # noqa: E402
+
+METRIC = "GQA decode achieved HBM GB/s (% peak) + causal prefill TFLOP/s (% MFMA peak)"
+MAIN = "gqa_decode_ragged_bf16"
+MALL_BYTES = 256 << 20
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_attention_gqa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter runs, or None if absent
+    or taken on a different kernel source."""
+    try:
+        data = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    ent = data.get("kernels", {}).get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def front_load():
+    # keep the GPU busy while the host enqueues the event-timed launches, so
+    # no host gap lands between an event and the kernel it brackets
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(20_000_000)
+
+
+def time_graph(step_fn, steps, warmup):
+    """Warm up eagerly, capture `steps` steps into one graph, replay it timed."""
+    for i in range(warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step_fn(i)
+    torch.cuda.synchronize()
+    g.replay()  # untimed replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps
+
+
+def time_eager(step_fn, steps, warmup):
+    for i in range(warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def bench_decode(wl, steps, warmup, use_graph=True):
+    dev = torch.device("cuda")
+    x = inputs.make_decode_inputs(wl, device=dev)
+    lens = x.seq_lens.cpu().tolist()
+    kv_bytes = roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens)
+    cache_bytes = x.k.numel() * x.k.element_size() * 2
+    ncopies = min(16, max(2, math.ceil(4 * MALL_BYTES / cache_bytes) + 1))
+    ks, vs = [x.k], [x.v]
+    kss, vss = [x.k_scale], [x.v_scale]
+    for _ in range(ncopies - 1):
+        ks.append(x.k.clone())
+        vs.append(x.v.clone())
+        kss.append(None if x.k_scale is None else x.k_scale.clone())
+        vss.append(None if x.v_scale is None else x.v_scale.clone())
+    desc = binding.decode_desc(x.q, x.k)
+    n_split = binding.attn_decode_num_splits(desc)
+    ws = torch.empty(binding.attn_decode_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x.q)
+
+    def partials(i):
+        c = i % ncopies
+        binding.attn_decode_partials(x.q, ks[c], vs[c], x.seq_lens, wl.scale, ws, k_scale=kss[c], v_scale=vss[c])
+
+    def combine(i):
+        binding.attn_decode_combine(x.q, x.k, x.seq_lens, ws, out)
+
+    def step(i):
+        partials(i)
+        combine(i)
+
+    ms_step = time_graph(step, steps, warmup) if use_graph else time_eager(step, steps, warmup)
+
+    # per-kernel durations: HIP events on the launch stream around each kernel
+    n_ev = min(steps, 100)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    front_load()
+    for i in range(n_ev):
+        ev[i][0].record()
+        partials(i)
+        ev[i][1].record()
+        combine(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / n_ev
+    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / n_ev
+
+    key = f"decode_split_{wl.kv_dtype}:{wl.name}"
+    achieved = kv_bytes / (split_ms * 1e-3) / 1e9
+    traffic = measured_traffic(key)
+    return {
+        "workload": wl.name,
+        "value": kv_bytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "ms_per_step": ms_step,
+        "pct_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / roofline.HBM_PEAK_GBPS,
+        "kv_bytes": kv_bytes,
+        "scale_bytes": roofline.decode_scale_bytes(wl.kv_dtype, wl.n_kv, lens),
+        "sum_L": int(sum(lens)),
+        "n_split": n_split,
+        "kv_copies_rotated": ncopies,
+        "split_kernel_ms": split_ms,
+        "combine_kernel_ms": comb_ms,
+        "roofline": {"bound": "hbm", "kernel": "gqa_decode_split_mfma" if wl.kv_dtype != "f32"
+                     else "gqa_decode_split_f32", "achieved": achieved, "peak": roofline.HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / roofline.HBM_PEAK_GBPS, "traffic": traffic},
+        "dtype": wl.kv_dtype,
+        "config": {"workload": wl.name, "B": wl.B, "h_q": wl.h_q, "n_kv": wl.n_kv, "d_h": wl.d_h,
+                   "S_max": wl.S_max, "q_dtype": wl.q_dtype, "kv_dtype": wl.kv_dtype, "seed": wl.seed},
+    }
+
+
+def bench_prefill(wl, steps, warmup, use_graph=True):
+    dev = torch.device("cuda")
+    x = inputs.make_prefill_inputs(wl, device=dev)
+    out = torch.empty_like(x.q)
+    flops = roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h)
+
+    def step(i):
+        binding.attn_prefill_causal(x.q, x.k, x.v, wl.scale, out=out)
+
+    ms_step = time_graph(step, steps, warmup) if use_graph else time_eager(step, steps, warmup)
+    n_ev = min(steps, 50)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    front_load()
+    for i in range(n_ev):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / n_ev
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    peak = roofline.MFMA_PEAK_TFLOPS["bf16"]
+    return {
+        "workload": wl.name,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_step": ms_step,
+        "pct_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / peak,
+        "causal_flops": flops,
+        "io_bytes": roofline.prefill_io_bytes(wl.B, wl.S, wl.h_q, wl.n_kv, wl.d_h),
+        "kernel_ms": k_ms,
+        "roofline": {"bound": "mfma", "kernel": "gqa_prefill_causal_kernel", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(f"prefill_causal:{wl.name}")},
+        "dtype": "bf16",
+        "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "h_q": wl.h_q, "n_kv": wl.n_kv, "d_h": wl.d_h,
+                   "seed": wl.seed},
+    }
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain elementwise kernel of known traffic (reads nbytes, writes nbytes)
+    for scaling hardware byte counters: dst = -src over float32."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "reps": reps}
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle, as it stands, on the host cores: full passes over the
+    decode workload (stored-value decoding included), repeated until about
+    `budget_s` seconds have elapsed; mean seconds per pass."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    x = inputs.make_decode_inputs(wl, device="cpu")
+    lens = x.seq_lens.tolist()
+    kv_bytes = roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens)
+    with threadpool_limits(limits=cores):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            q = oracle.bf16_bits_to_f64(inputs.stored_numpy(x.q))
+            k = oracle.bf16_bits_to_f64(inputs.stored_numpy(x.k))
+            v = oracle.bf16_bits_to_f64(inputs.stored_numpy(x.v))
+            oracle.decode(q, k, v, lens, wl.scale)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or passes >= 50:
+                break
+    sec = el / passes
+    return {"value": kv_bytes / sec / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"whole {wl.name} workload (B={wl.B}, h_q={wl.h_q}, sum L={sum(lens)}), bf16->fp64 "
+                      f"decoding included; {passes} pass(es), {sec:.3f} s/pass; host cores available: {cores}",
+            "seconds_per_pass": sec}
+
+
+# ----------------------------------------------------------------------------
+# rocprofv3 output -> profiles/
+# ----------------------------------------------------------------------------
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -T -d <out>/prof_trace -o run --output-format csv -- "
+             "python3 bench.py --steps 20 --warmup 2 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace -T -d <out>/prof_fetch -o run --output-format csv -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-graph --copy-calibration",
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace -T -d <out>/prof_write -o run --output-format csv -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-graph --copy-calibration",
+}
+CALIB_GRID = (1 << 30) // 16  # threads of the calibration kernel (4 floats per thread)
+
+
+def _workload_launches():
+    """(kernel-name prefix, grid threads) -> (counter key, workload, algorithmic bytes or flops)."""
+    out = {}
+    for wl in inputs.DECODE_WORKLOADS.values():
+        qd = torch.empty((wl.B, wl.h_q, wl.d_h), dtype={"f32": torch.float32, "bf16": torch.bfloat16}[wl.q_dtype],
+                         device="meta")
+        kd = torch.empty((wl.B, wl.n_kv, wl.S_max, wl.d_h), device="meta",
+                         dtype={"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.kv_dtype])
+        desc = binding.decode_desc(qd, kd)
+        ns = binding.attn_decode_num_splits(desc)
+        G = wl.h_q // wl.n_kv
+        hpc = 16 if (wl.kv_dtype == "f32" or G <= 16) else 32
+        nh = -(-G // hpc)
+        grid = ns * wl.n_kv * nh * wl.B * 256
+        lens = inputs.draw_lengths(wl.B, *wl.lens, wl.seed).tolist()
+        kernel = "gqa_decode_split_f32" if wl.kv_dtype == "f32" else "gqa_decode_split_mfma"
+        out[(kernel, grid)] = (f"decode_split_{wl.kv_dtype}:{wl.name}", wl.name,
+                               roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens), "bytes")
+        out[("gqa_decode_combine", ((wl.B * wl.h_q + 3) // 4) * 256)] = (f"decode_combine:{wl.name}", wl.name, None,
+                                                                        None)
+    for wl in inputs.PREFILL_WORKLOADS.values():
+        G = wl.h_q // wl.n_kv
+        hc = math.gcd(G, 4)
+        bm = 32 * (4 // hc)
+        n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S // bm))
+        grid = -(-n_wg // 8) * 8 * 256
+        out[("gqa_prefill_causal_kernel", grid)] = (f"prefill_causal:{wl.name}", wl.name,
+                                                    roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h), "flops")
+    return out
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
+    import csv
+    import statistics
+
+    def base(name):
+        return name.split("(")[0].split("<")[0].replace("void ", "").split("::")[-1].strip()
+
+    def rows(d, suffix):
+        for f in os.listdir(d):
+            if f.endswith(suffix):
+                return list(csv.DictReader(open(os.path.join(d, f))))
+        raise FileNotFoundError(f"no *{suffix} in {d}")
+
+    launches = _workload_launches()
+    dur = {}
+    for r in rows(trace_dir, "kernel_trace.csv"):
+        key = (base(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        if key in launches:
+            dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    counters = {}
+    for kind, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        calib = []
+        for r in rows(d, "counter_collection.csv"):
+            key = (base(r["Kernel_Name"]), int(r["Grid_Size"]))
+            v = float(r["Counter_Value"])
+            if key[0] == "vectorized_elementwise_kernel" and key[1] == CALIB_GRID and v > 1024:
+                calib.append(v)
+            elif key in launches:
+                counters.setdefault((kind, key), []).append(v)
+        counters[(kind, "scale")] = (1 << 20) / statistics.median(calib)  # KiB expected / KiB counted
+    digest = source_digest()
+    summary = {"source_digest": digest, "fetch_scale": counters[("FETCH_SIZE", "scale")],
+               "write_scale": counters[("WRITE_SIZE", "scale")], "kernels": {}}
+    os.makedirs(dest, exist_ok=True)
+    for key, (ckey, wname, algo, algo_unit) in sorted(launches.items(), key=lambda kv: kv[1][0]):
+        if key not in dur:
+            continue
+        d = sorted(dur[key])
+        fetch = counters.get(("FETCH_SIZE", key))
+        write = counters.get(("WRITE_SIZE", key))
+        fb = statistics.median(fetch) * 1024 * summary["fetch_scale"] if fetch else None
+        wb = statistics.median(write) * 1024 * summary["write_scale"] if write else None
+        ent = {"kernel": key[0], "workload": wname, "grid_threads": key[1], "launches": len(d),
+               "mean_us": statistics.mean(d), "median_us": statistics.median(d), "min_us": d[0], "max_us": d[-1],
+               "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+               "hbm_bytes_per_launch": (fb + wb) if fb is not None and wb is not None else None,
+               "source_digest": digest}
+        if algo_unit == "bytes":
+            ent["algorithmic_bytes"] = algo
+            ent["achieved_GBps_at_mean"] = algo / (ent["mean_us"] * 1e-6) / 1e9
+            if fb:
+                ent["fetch_over_algorithmic"] = fb / algo
+        elif algo_unit == "flops":
+            ent["algorithmic_flops"] = algo
+            ent["achieved_TFLOPs_at_mean"] = algo / (ent["mean_us"] * 1e-6) / 1e12
+        summary["kernels"][ckey] = ent
+        fname = os.path.join(dest, f"{key[0]}__{wname}.txt")
+        with open(fname, "w") as f:
+            f.write(f"kernel: {key[0]}   workload: {wname}   grid threads: {key[1]}\n")
+            f.write("commands (run from the repository root on one MI355X; <out> = output directory):\n")
+            for k in ("trace", "fetch", "write"):
+                f.write(f"  {PROFILE_COMMANDS[k]}\n")
+            f.write(f"kernel source digest: {digest}\n\n")
+            f.write(f"kernel-trace: {len(d)} launches, mean {ent['mean_us']:.2f} us, median {ent['median_us']:.2f} us, "
+                    f"min {ent['min_us']:.2f} us, max {ent['max_us']:.2f} us\n")
+            if fb is not None:
+                f.write(f"FETCH_SIZE: median {statistics.median(fetch):.0f} KiB/launch x scale "
+                        f"{summary['fetch_scale']:.4f} = {fb / 1e6:.2f} MB\n")
+            if wb is not None:
+                f.write(f"WRITE_SIZE: median {statistics.median(write):.0f} KiB/launch x scale "
+                        f"{summary['write_scale']:.4f} = {wb / 1e6:.2f} MB\n")
+            f.write("(scales: a 1 GiB-read / 1 GiB-write elementwise kernel in the same runs, expected KiB / counted "
+                    "KiB)\n")
+            if algo_unit == "bytes":
+                f.write(f"algorithmic KV bytes: {algo / 1e6:.2f} MB -> {ent['achieved_GBps_at_mean']:.0f} GB/s at the "
+                        f"mean duration ({ent['achieved_GBps_at_mean'] / roofline.HBM_PEAK_GBPS * 100:.1f}% of 8 TB/s)\n")
+                if fb:
+                    f.write(f"fetched / algorithmic bytes: {fb / algo:.4f}\n")
+            elif algo_unit == "flops":
+                f.write(f"causal flops: {algo:.4e} -> {ent['achieved_TFLOPs_at_mean']:.0f} TFLOP/s at the mean "
+                        f"duration ({ent['achieved_TFLOPs_at_mean'] / 2500 * 100:.1f}% of 2.5 PFLOP/s bf16)\n")
+    json.dump(summary, open(os.path.join(dest, "counters.json"), "w"), indent=1)
+    return summary
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=MAIN, choices=sorted(inputs.DECODE_WORKLOADS) + sorted(
+        inputs.PREFILL_WORKLOADS))
+    ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 output directories into profiles/ summaries and exit")
+    args = ap.parse_args(argv)
+    if args.summarize:
+        s = summarize_profiles(*args.summarize, dest=os.path.join(ROOT, "profiles"))
+        print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk in ("mean_us", "hbm_bytes_per_launch")}
+                          for k, v in s["kernels"].items()}, indent=1))
+        return 0
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (each GPU would run its own "
+              "share of sequences/heads independently); run with --gpus 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.load_library()
+    props = torch.cuda.get_device_properties(0)
+    use_graph = not args.no_graph
+    if args.copy_calibration:
+        print(f"[bench] copy calibration {copy_calibration()}", file=sys.stderr, flush=True)
+
+    def run(name, steps, warmup):
+        print(f"[bench] {name} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+        if name in inputs.PREFILL_WORKLOADS:
+            return bench_prefill(inputs.PREFILL_WORKLOADS[name], steps, warmup, use_graph)
+        return bench_decode(inputs.DECODE_WORKLOADS[name], steps, warmup, use_graph)
+
+    main_res = run(args.workload, args.steps, args.warmup)
+    others = {}
+    if not args.only_main:
+        for name in list(inputs.DECODE_WORKLOADS) + list(inputs.PREFILL_WORKLOADS):
+            if name == args.workload:
+                continue
+            others[name] = run(name, max(5, min(args.steps, 20)), 2)
+            torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC,
+        "value": main_res["value"],
+        "unit": main_res["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["dtype"],
+        "data": "synthetic",
+        "config": main_res["config"],
+        "roofline": main_res["roofline"],
+        "timing": "hip-graph replay of K steps" if use_graph else "eager launches",
+        "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+        "main": {k: v for k, v in main_res.items() if k not in ("config", "roofline")},
+        "workloads": others,
+    }
+    if not args.no_cpu_baseline and args.workload in inputs.DECODE_WORKLOADS:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inputs.DECODE_WORKLOADS[args.workload])
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
