@@ -102,7 +102,7 @@ def time_eager(step_fn, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def bench_decode(wl, steps, warmup, use_graph=True):
+def bench_decode(wl, steps, warmup, use_graph=True, n_split=0):
     dev = torch.device("cuda")
     x = inputs.make_decode_inputs(wl, device=dev)
     lens = x.seq_lens.cpu().tolist()
@@ -116,17 +116,19 @@ def bench_decode(wl, steps, warmup, use_graph=True):
         vs.append(x.v.clone())
         kss.append(None if x.k_scale is None else x.k_scale.clone())
         vss.append(None if x.v_scale is None else x.v_scale.clone())
-    desc = binding.decode_desc(x.q, x.k)
+    desc = binding.decode_desc(x.q, x.k, n_split)
+    n_split_req = n_split
     n_split = binding.attn_decode_num_splits(desc)
     ws = torch.empty(binding.attn_decode_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x.q)
 
     def partials(i):
         c = i % ncopies
-        binding.attn_decode_partials(x.q, ks[c], vs[c], x.seq_lens, wl.scale, ws, k_scale=kss[c], v_scale=vss[c])
+        binding.attn_decode_partials(x.q, ks[c], vs[c], x.seq_lens, wl.scale, ws, k_scale=kss[c], v_scale=vss[c],
+                                     n_split=n_split_req)
 
     def combine(i):
-        binding.attn_decode_combine(x.q, x.k, x.seq_lens, ws, out)
+        binding.attn_decode_combine(x.q, x.k, x.seq_lens, ws, out, n_split=n_split_req)
 
     def step(i):
         partials(i)
@@ -393,6 +395,7 @@ def main(argv=None):
     ap.add_argument("--workload", default=MAIN, choices=sorted(inputs.DECODE_WORKLOADS) + sorted(
         inputs.PREFILL_WORKLOADS))
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
+    ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -423,7 +426,7 @@ def main(argv=None):
         print(f"[bench] {name} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
         if name in inputs.PREFILL_WORKLOADS:
             return bench_prefill(inputs.PREFILL_WORKLOADS[name], steps, warmup, use_graph)
-        return bench_decode(inputs.DECODE_WORKLOADS[name], steps, warmup, use_graph)
+        return bench_decode(inputs.DECODE_WORKLOADS[name], steps, warmup, use_graph, args.n_split)
 
     main_res = run(args.workload, args.steps, args.warmup)
     others = {}

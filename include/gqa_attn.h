@@ -89,22 +89,25 @@ typedef enum gqa_status {
  * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
  * Accumulation is float32 throughout.
  *
- * Sequence split: the keys of each (sequence, kv-head) are cut into n_split
- * chunks processed in parallel; each chunk leaves an unnormalised partial
- * (O_s, m_s, l_s) in the workspace and a combine kernel merges them:
+ * Sequence split: the 32-token tiles (64 on the F32 path) of every
+ * (sequence, kv-head) are concatenated and cut into n_split equal ranges, one
+ * per workgroup, so ragged lengths are balanced across the GPU.  Each range
+ * leaves an unnormalised partial (O_s, m_s, l_s) per head for every
+ * (sequence, kv-head) it touches, and a combine kernel merges them:
  *   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
  */
 typedef struct gqa_decode_desc {
   int32_t B, h_q, n_kv, S_max, d_h;
   int32_t q_dtype, kv_dtype; /* GQA_F32 / GQA_BF16 / GQA_FP8_E4M3           */
-  int32_t n_split;           /* 0: library heuristic.  > 0: requested number
-                                of sequence chunks (rounded so that each chunk
-                                is a whole number of 32-token tiles; the
-                                effective count is attn_decode_num_splits()). */
+  int32_t n_split;           /* 0: one workgroup per compute unit of an MI355X
+                                (256).  > 0: number of workgroups / key ranges,
+                                capped at the number of tiles of a full cache
+                                and at 65536 (the effective count is
+                                attn_decode_num_splits()).                    */
 } gqa_decode_desc;
 
-/* Effective number of sequence chunks for this descriptor, or -1 if the
- * descriptor is invalid.  Host-only, deterministic. */
+/* Effective number of key ranges (= decode workgroups) for this descriptor,
+ * or -1 if the descriptor is invalid.  Host-only, deterministic. */
 int32_t attn_decode_num_splits(const gqa_decode_desc* d);
 
 /* Bytes of device workspace attn_decode needs for this descriptor (0 if the

@@ -87,15 +87,21 @@ def test_split_plan_is_deterministic_and_honours_requests(lib):
     base = dd(B=16, h_q=64, n_kv=8, S=4096)
     a = lib.attn_decode_workspace_bytes(ctypes.byref(base))
     assert a == lib.attn_decode_workspace_bytes(ctypes.byref(base))
+    assert lib.attn_decode_num_splits(ctypes.byref(base)) == 256  # one workgroup per MI355X compute unit
+    n_slabs = 16 * 8  # G = 8 <= 16: one head chunk per K/V head
+    max_tiles = n_slabs * (4096 // 32)
     for req in (1, 2, 7, 128, 100000):
         desc = dd(B=16, h_q=64, n_kv=8, S=4096, ns=req)
         ns = lib.attn_decode_num_splits(ctypes.byref(desc))
-        assert 1 <= ns <= min(req, 4096 // 32)
-        # each chunk is a whole number of 32-token tiles and the chunks cover S_max
-        chunk = -(-4096 // ns)
-        assert ns * chunk >= 4096
+        assert ns == min(req, max_tiles, 65536)
+        # one partial slot per (workgroup, slab) pair a balanced range can touch
         ws = lib.attn_decode_workspace_bytes(ctypes.byref(desc))
-        assert ws >= 16 * 64 * ns * (128 + 2) * 4
+        assert ws >= (ns + n_slabs) * 16 * (128 + 2) * 4
+    # the float32 path plans in 64-token tiles, the matrix-core paths in 32-token tiles
+    tiny = dd(B=2, h_q=8, n_kv=1, S=128, d=64, qt=0, kt=0)
+    assert lib.attn_decode_num_splits(ctypes.byref(tiny)) == 2 * 2
+    big_g = dd(B=2, h_q=64, n_kv=1, S=64, qt=1, kt=1)  # G = 64 -> two chunks of 32 heads
+    assert lib.attn_decode_num_splits(ctypes.byref(big_g)) == 2 * 2 * 2
 
 
 def test_prefill_errors(lib):

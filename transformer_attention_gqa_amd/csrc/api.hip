@@ -14,14 +14,12 @@ namespace gqa {
 namespace {
 
 constexpr double kLog2e = 1.4426950408889634;
-constexpr int kWaves = 4;
 constexpr int kTileMfma = 32;
 constexpr int kTileF32 = 64;
-// Split heuristic: aim for this many workgroups over the whole call, but keep
-// each chunk long enough that the per-chunk partial (heads x (d+2) floats,
-// written once and read once) stays a small fraction of the chunk's K/V bytes.
-constexpr long kTargetWorkgroups = 1024;
-constexpr double kMaxPartialFraction = 1.0 / 32.0;
+// Default number of decode workgroups: one per compute unit of an MI355X
+// (256 CUs); each runs 8 wavefronts and owns 1/256 of all key tiles.
+constexpr long kDefaultWorkgroups = 256;
+constexpr long kMaxWorkgroups = 65536;
 
 thread_local char g_last_hip_error[256] = "";
 
@@ -37,10 +35,10 @@ struct DecodePlan {
   int kind;             // 0 f32, 1 bf16 K/V, 2 fp8 K/V
   int tile;             // tokens per wave tile
   int hb;               // 16-head blocks per workgroup (matrix-core paths)
-  int heads_per_chunk;  // query heads one workgroup serves
-  int n_hchunk;         // workgroups along the head axis of one group
-  int chunk;            // tokens per sequence chunk (multiple of tile)
-  int n_split;          // chunks covering S_max
+  int heads_per_chunk;  // query heads one workgroup serves at a time
+  int n_hchunk;         // head chunks per K/V group
+  long n_slabs;         // B * n_kv * n_hchunk
+  int W;                // workgroups launched (balanced key ranges)
 };
 
 gqa_status validate_decode_desc(const gqa_decode_desc* d) {
@@ -56,6 +54,7 @@ gqa_status validate_decode_desc(const gqa_decode_desc* d) {
   // index arithmetic inside the kernels: B*h_q rows, B*n_kv*S_max cache rows
   if ((int64_t)d->B * d->h_q > (int64_t)1 << 30) return GQA_ERR_SHAPE;
   if ((int64_t)d->B * d->n_kv * d->S_max > (int64_t)1 << 40) return GQA_ERR_SHAPE;
+  if (d->S_max > (1 << 30)) return GQA_ERR_SHAPE;
   return GQA_OK;
 }
 
@@ -73,34 +72,18 @@ DecodePlan plan_decode(const gqa_decode_desc* d) {
     p.heads_per_chunk = 16 * p.hb;
   }
   p.n_hchunk = (G + p.heads_per_chunk - 1) / p.heads_per_chunk;
-  const int heads_eff = G < p.heads_per_chunk ? G : p.heads_per_chunk;
-  const long max_tiles = (d->S_max + p.tile - 1) / p.tile;
-  long n_split;
-  if (d->n_split > 0) {
-    n_split = d->n_split;
-  } else {
-    const long units = (long)d->B * d->n_kv * p.n_hchunk;
-    n_split = (kTargetWorkgroups + units - 1) / units;
-    // floor on the chunk length from the partial-traffic bound
-    const int elem = p.kind == 0 ? 4 : (p.kind == 1 ? 2 : 1);
-    const double partial_bytes = (double)heads_eff * (d->d_h + 2) * 4.0 * 2.0;  // written + read
-    const double bytes_per_token = 2.0 * d->d_h * elem;
-    long min_chunk = (long)(partial_bytes / (kMaxPartialFraction * bytes_per_token));
-    const long wave_round = (long)kWaves * p.tile;
-    min_chunk = (min_chunk + wave_round - 1) / wave_round * wave_round;
-    const long max_split_by_len = (d->S_max + min_chunk - 1) / min_chunk;
-    if (n_split > max_split_by_len) n_split = max_split_by_len;
-  }
-  if (n_split < 1) n_split = 1;
-  if (n_split > max_tiles) n_split = max_tiles;
-  long chunk_tiles = (max_tiles + n_split - 1) / n_split;
-  p.chunk = (int)(chunk_tiles * p.tile);
-  p.n_split = (int)((d->S_max + p.chunk - 1) / p.chunk);
+  p.n_slabs = (long)d->B * d->n_kv * p.n_hchunk;
+  const long max_tiles = p.n_slabs * ((d->S_max + p.tile - 1) / p.tile);
+  long W = d->n_split > 0 ? (long)d->n_split : kDefaultWorkgroups;
+  if (W > max_tiles) W = max_tiles;
+  if (W > kMaxWorkgroups) W = kMaxWorkgroups;
+  if (W < 1) W = 1;
+  p.W = (int)W;
   return p;
 }
 
 size_t workspace_layout(const gqa_decode_desc* d, const DecodePlan& p, size_t* ml_offset) {
-  const size_t rows = (size_t)d->B * d->h_q * p.n_split;
+  const size_t rows = (size_t)(p.W + p.n_slabs) * p.heads_per_chunk;
   const size_t o_bytes = rows * d->d_h * sizeof(float);
   const size_t ml_off = (o_bytes + 255) & ~(size_t)255;
   if (ml_offset) *ml_offset = ml_off;
@@ -132,14 +115,13 @@ gqa_status do_partials(const gqa_decode_desc* d, const DecodePlan& p, const void
   a.part_o = static_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
   a.qk_scale_log2 = (float)((double)scale * kLog2e);
+  a.B = d->B;
   a.h_q = d->h_q;
   a.n_kv = d->n_kv;
   a.S_max = d->S_max;
-  a.chunk = p.chunk;
-  a.n_split = p.n_split;
   a.n_hchunk = p.n_hchunk;
   a.heads_per_chunk = p.heads_per_chunk;
-  hipError_t e = launch_decode_split(a, d->B, d->d_h, p.hb, p.kind, stream);
+  hipError_t e = launch_decode_split(a, d->d_h, p.hb, p.kind, p.W, stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;
@@ -151,10 +133,20 @@ gqa_status do_combine(const gqa_decode_desc* d, const DecodePlan& p, const int32
                       void* out, hipStream_t stream) {
   size_t ml_off = 0;
   workspace_layout(d, p, &ml_off);
-  const float* part_o = static_cast<const float*>(ws);
-  const float* part_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ml_off);
-  hipError_t e = launch_decode_combine(part_o, part_ml, seq_lens, out, d->q_dtype == GQA_BF16, d->B, d->h_q,
-                                       d->S_max, d->d_h, p.chunk, p.n_split, stream);
+  CombineArgs c;
+  c.part_o = static_cast<const float*>(ws);
+  c.part_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ml_off);
+  c.seq_lens = seq_lens;
+  c.out = out;
+  c.B = d->B;
+  c.h_q = d->h_q;
+  c.n_kv = d->n_kv;
+  c.S_max = d->S_max;
+  c.n_hchunk = p.n_hchunk;
+  c.heads_per_chunk = p.heads_per_chunk;
+  c.tile = p.tile;
+  c.W = p.W;
+  hipError_t e = launch_decode_combine(c, d->d_h, d->q_dtype == GQA_BF16, stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;
@@ -171,7 +163,7 @@ extern "C" {
 
 int32_t attn_decode_num_splits(const gqa_decode_desc* d) {
   if (validate_decode_desc(d) != GQA_OK) return -1;
-  return plan_decode(d).n_split;
+  return plan_decode(d).W;
 }
 
 size_t attn_decode_workspace_bytes(const gqa_decode_desc* d) {

@@ -8,15 +8,19 @@
 // Attention (MQA)" glossary).  Decode moves the whole cache through memory
 // once per step and does Theta(h d_h S) flops ("Multi-query attention",
 // "Why this is a bandwidth argument, not a FLOP argument"), so the kernels are
-// built around reading every K/V byte exactly once:
+// built around reading every K/V byte exactly once, evenly over the chip:
 //
-//  * one workgroup owns a chunk of keys of one (sequence, kv-head) pair and
-//    serves every query head of the group (up to 32) from that single read;
-//  * 4 wavefronts per workgroup take interleaved 32-token tiles; each tile
-//    arrives through 128-bit non-temporal loads (a quarter-wave covers one
-//    contiguous 256-byte cache row), is written once to the wave's private
-//    LDS slab with an XOR chunk swizzle, and is consumed from there by the
-//    matrix cores, while the next tile is already in flight in registers;
+//  * the launch is one wide workgroup per compute unit (persistent); the
+//    32-token tiles of all (sequence, kv-head) slabs are concatenated and cut
+//    into equal ranges, one per workgroup, so ragged sequence lengths cost no
+//    load imbalance and no tail of lone workgroups (schedule: gqa_launch.h);
+//  * a workgroup serves every query head of the slab's group (up to 32) from a
+//    single read of each K/V tile;
+//  * its wavefronts take interleaved tiles; each tile arrives through 128-bit
+//    non-temporal loads (16 lanes cover one contiguous 256-byte cache row), is
+//    written once to the wave's private LDS slab with an XOR chunk swizzle,
+//    and is consumed from there by the matrix cores while the next tile is
+//    already in flight in registers;
 //  * scores S^T[token][head] = K Q^T and O^T[d][head] += V^T P^T run on
 //    v_mfma_f32_16x16x32_bf16; the token order inside the PV product is
 //    permuted so that the score layout produced by the first product is
@@ -25,8 +29,9 @@
 //  * softmax is online: per head a running max m (log2 domain) and running
 //    sum l; a tile rescales O and l by 2^(m_old - m_new) ("Flash Attention
 //    Principle": running max and running sum, write only the final result);
-//  * each workgroup leaves an unnormalised partial (O, m, l) per head; the
-//    combine kernel merges the partials of all chunks.
+//  * at the end of each slab segment the waves merge their (O, m, l) through
+//    LDS and the workgroup writes one unnormalised partial per head; the
+//    combine kernel merges the partials of a slab.
 // The fp8 path reads e4m3 codes (half the bytes), converts them to bf16
 // exactly in registers and folds the per-token scales into the score (K) and
 // into the probability (V).  The fp32 path keeps float32 end to end on the
@@ -36,63 +41,196 @@
 
 namespace gqa {
 
-constexpr int kDecodeWaves = 4;
-constexpr int kTile = 32;      // tokens per wave tile (matrix-core paths)
-constexpr int kTileF32 = 64;   // tokens per wave tile (float32 path)
+constexpr int kTile = 32;     // tokens per wave tile (matrix-core paths)
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
+constexpr int kTileF32 = 64;  // tokens per wave tile (float32 path)
+constexpr int kWavesF32 = 4;
 
 // ------------------------------------------------------------------------
-// Matrix-core decode: bf16 Q; bf16 or e4m3 K/V.  HB blocks of 16 heads.
+// Balanced schedule helpers.  All are wave-uniform: every lane returns the
+// same values, so every wave of a workgroup can evaluate them on its own.
+// Sequences are visited 64 at a time, one per lane.
 // ------------------------------------------------------------------------
-template <int D, int HB, bool FP8>
-__global__ __launch_bounds__(256, 2) void gqa_decode_split_mfma(DecodeArgs a) {
-  constexpr int CH = D / 8;             // 16-byte bf16 chunks per row
-  constexpr int KK = D / 32;            // k-steps of the score product
-  constexpr int NT = D / 16;            // 16-wide d tiles of the PV product
-  constexpr int TILE_BYTES = kTile * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[kDecodeWaves][2][TILE_BYTES];
-  __shared__ float sm_ml[kDecodeWaves][HB * 16][2];
+__device__ __forceinline__ int clamp_len(int L, int S_max) { return min(max(L, 0), S_max); }
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / a.n_hchunk;
-  const int hc = blockIdx.y - g * a.n_hchunk;
-  const int b = blockIdx.z;
-  const int L = min(max(a.seq_lens[b], 0), a.S_max);
-  const int t_begin = s * a.chunk;
-  if (t_begin >= L) return;  // uniform over the workgroup
-  const int t_end = min(t_begin + a.chunk, L);
+__device__ __forceinline__ int seq_tiles(const int32_t* seq_lens, int b, int S_max, int tile) {
+  return (clamp_len(seq_lens[b], S_max) + tile - 1) / tile;
+}
+
+// Wave-uniform values produced by cross-lane operations live in VGPRs unless
+// told otherwise; these move them to scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform(long long v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Tiles of all slabs of sequences 0 .. n-1 (n = B gives the total T).
+__device__ long long tiles_before(const int32_t* seq_lens, int n, int S_max, int tile, int spb, int lane) {
+  long long acc = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int b = base + lane;
+    acc += wave_sum_ll(b < n ? (long long)seq_tiles(seq_lens, b, S_max, tile) * spb : 0);
+  }
+  return acc;
+}
+
+// Lengths of sequences 0..63 held one per lane (B <= 64, the common case):
+// the schedule then needs a single load of seq_lens per wave.
+struct LaneLens {
+  int len;    // clamped length of sequence `lane` (0 past B)
+  bool fits;  // B <= 64
+};
+
+__device__ __forceinline__ LaneLens load_lane_lens(const int32_t* seq_lens, int B, int S_max, int lane) {
+  LaneLens r;
+  r.fits = B <= 64;
+  r.len = (r.fits && lane < B) ? clamp_len(seq_lens[lane], S_max) : 0;
+  return r;
+}
+
+__device__ __forceinline__ long long total_tiles_cached(const LaneLens& ll, const int32_t* seq_lens, int B, int S_max,
+                                                        int tile, int spb, int lane) {
+  if (!ll.fits) return tiles_before(seq_lens, B, S_max, tile, spb, lane);
+  return wave_sum_ll((long long)((ll.len + tile - 1) / tile) * spb);
+}
+
+// The sequence whose slabs contain global tile t (0 <= t < T): its index, the
+// global index of its first tile, its tiles per slab and its clamped length.
+__device__ void locate_tile(const int32_t* seq_lens, int B, int S_max, int tile, int spb, long long t, int lane,
+                            int& b_out, long long& base_out, int& nt_out, int& len_out) {
+  long long acc = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int len = b < B ? clamp_len(seq_lens[b], S_max) : 0;
+    const int nt = (len + tile - 1) / tile;
+    long long incl = (long long)nt * spb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long u = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += u;
+    }
+    const long long tot = __shfl(incl, 63, 64);
+    if (t < acc + tot) {
+      const unsigned long long mask = __ballot(acc + incl > t);
+      const int first = __ffsll((long long)mask) - 1;
+      b_out = base + first;
+      nt_out = __shfl(nt, first, 64);
+      len_out = __shfl(len, first, 64);
+      base_out = acc + __shfl(incl, first, 64) - (long long)nt_out * spb;
+      return;
+    }
+    acc += tot;
+  }
+  b_out = B;
+  base_out = acc;
+  nt_out = 0;
+  len_out = 0;
+}
+
+__device__ void locate_tile_cached(const LaneLens& ll, const int32_t* seq_lens, int B, int S_max, int tile, int spb,
+                                   long long t, int lane, int& b_out, long long& base_out, int& nt_out, int& len_out) {
+  if (!ll.fits) {
+    locate_tile(seq_lens, B, S_max, tile, spb, t, lane, b_out, base_out, nt_out, len_out);
+    return;
+  }
+  const int nt = (ll.len + tile - 1) / tile;
+  long long incl = (long long)nt * spb;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  const unsigned long long mask = __ballot(incl > t);
+  const int first = __ffsll((long long)mask) - 1;
+  b_out = first;
+  nt_out = __shfl(nt, first, 64);
+  len_out = __shfl(ll.len, first, 64);
+  base_out = __shfl(incl, first, 64) - (long long)nt_out * spb;
+}
+
+// ------------------------------------------------------------------------
+// Matrix-core decode: bf16 Q; bf16 or e4m3 K/V.  HB blocks of 16 heads,
+// NW wavefronts per workgroup.
+// ------------------------------------------------------------------------
+// One contiguous piece of a workgroup's tile range that lies in a single slab.
+struct Segment {
+  int b, g, hc;        // sequence, kv-head, head chunk
+  int ntile;           // tiles of the segment
+  int t_begin, t_end;  // token range [t_begin, t_end) inside the sequence
+  int nh, head0;       // heads served and the global index of the first
+  size_t slab;         // cache row of token 0 of (b, g)
+  long long slot;      // partial slot
+};
+
+template <int TILE>
+__device__ __forceinline__ Segment make_segment(const DecodeArgs& a, const LaneLens& ll, long long t, long long hi,
+                                                int w, int spb, int hpc, int lane) {
+  int b, nt, L;
+  long long base;
+  locate_tile_cached(ll, a.seq_lens, a.B, a.S_max, TILE, spb, t, lane, b, base, nt, L);
+  b = uniform(b);
+  nt = uniform(nt);
+  L = uniform(L);
+  base = uniform(base);
+  const long long local = t - base;
+  const int slab_in_b = (int)(local / nt);
+  const int tile0 = (int)(local - (long long)slab_in_b * nt);
+  Segment s;
+  s.b = b;
+  s.g = slab_in_b / a.n_hchunk;
+  s.hc = slab_in_b - s.g * a.n_hchunk;
+  s.ntile = (int)min(hi - t, (long long)(nt - tile0));
+  s.t_begin = tile0 * TILE;
+  s.t_end = min((tile0 + s.ntile) * TILE, L);
   const int G = a.h_q / a.n_kv;
-  const int hloc0 = hc * a.heads_per_chunk;
-  const int nh = min(a.heads_per_chunk, G - hloc0);
-  const int head0 = g * G + hloc0;  // global index of local head 0
+  s.nh = min(hpc, G - s.hc * hpc);
+  s.head0 = s.g * G + s.hc * hpc;
+  s.slab = ((size_t)b * a.n_kv + s.g) * (size_t)a.S_max;
+  s.slot = w + (long long)b * spb + slab_in_b;
+  return s;
+}
 
-  const int wave = threadIdx.x >> 6;
+template <int D, int HB, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
+  constexpr int CH = D / 8;   // 16-byte bf16 chunks per row
+  constexpr int KK = D / 32;  // k-steps of the score product
+  constexpr int NT = D / 16;  // 16-wide d tiles of the PV product
+  constexpr int TILE_BYTES = kTile * D * 2;
+  constexpr int HPC = 16 * HB;
+  static_assert(HPC * D * 4 <= 2 * TILE_BYTES, "partial O does not fit the wave slab");
+  constexpr int QCH = (HPC * CH + NW * 64 - 1) / (NW * 64);  // 16-byte query chunks per thread
+  __shared__ __attribute__((aligned(16))) char smem[NW][2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sq[HPC * D * 2];  // the segment's query rows, bf16, swizzled
+  __shared__ float sm_ml[NW][HPC][2];
+  __shared__ int s_next_tile;  // next unclaimed tile of the current segment
+
+  const int W = gridDim.x;
+  const int w = blockIdx.x;
+  const int wave = uniform((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4;
   const int r16 = lane & 15;
+  const int spb = a.n_kv * a.n_hchunk;
+
+  const LaneLens ll = load_lane_lens(a.seq_lens, a.B, a.S_max, lane);
+  const long long T = uniform(total_tiles_cached(ll, a.seq_lens, a.B, a.S_max, kTile, spb, lane));
+  long long lo = (long long)w * T / W;
+  const long long hi = (long long)(w + 1) * T / W;
+  if (lo >= hi) return;  // uniform over the workgroup
 
   char* kt = smem[wave][0];
   char* vt = smem[wave][1];
+  float* ow = reinterpret_cast<float*>(smem[wave][0]);
 
-  // ---- Q fragments: B operand of S^T = K Q^T: lane holds Q[head r16][32kk + 8q4 .. +7]
-  u32x4 qf[HB][KK];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int hl = hb * 16 + r16;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hl < nh) {
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.h_q + head0 + hl) * D + 32 * kk + 8 * q4;
-        v = *reinterpret_cast<const u32x4*>(qp);
-      }
-      qf[hb][kk] = v;
-    }
-  }
-
-  const size_t slab = ((size_t)b * a.n_kv + g) * (size_t)a.S_max;  // row index of token 0
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-
-  // ---- per-lane load assignment.  bf16: a load instruction covers 64/CH rows,
+  // per-lane load assignment.  bf16: a load instruction covers 64/CH rows,
   // each row by CH consecutive lanes.  fp8: rows of D bytes, D/16 lanes per row.
   constexpr int NLD = FP8 ? (kTile * D) / (64 * 16) : (kTile * D * 2) / (64 * 16);
   constexpr int LPR = FP8 ? D / 16 : CH;  // lanes per row
@@ -101,441 +239,577 @@ __global__ __launch_bounds__(256, 2) void gqa_decode_split_mfma(DecodeArgs a) {
   const int ld_chunk = lane % LPR;
 
   u32x4 kreg[NLD], vreg[NLD];
-  float ksc[2][4], vsc[2][4];  // fp8: scales of the lane's 8 score tokens (next tile)
+  float ksc[2][4], vsc[2][4];
 
-  auto issue_loads = [&](int tile) {
-    const int t0 = t_begin + tile * kTile;
+  // loads of tile `tile` of segment s into kreg/vreg (and its fp8 scales).
+  // Branch-free: rows past the segment end re-read its last row (in bounds)
+  // and are zeroed at staging, so no NaN of a cache tail reaches the MFMA.
+  // loads of tile `tile` of segment s into kreg/vreg (and its fp8 scales).
+  // A full tile is addressed as a wave-uniform base plus a per-lane constant;
+  // the segment's last tile re-reads its last valid row for the rows past the
+  // end (in bounds), which staging then zeroes, so no NaN of a cache tail can
+  // reach the matrix cores.
+  constexpr int ROWB = FP8 ? D : 2 * D;  // bytes per cache row
+  const int lane_off = ld_row * ROWB + ld_chunk * 16;
+  auto issue_loads = [&](const Segment& s, int tile) {
+    const int tt0 = s.t_begin + tile * kTile;
+    const char* kb = static_cast<const char*>(a.k) + (s.slab + tt0) * ROWB;
+    const char* vb = static_cast<const char*>(a.v) + (s.slab + tt0) * ROWB;
+    if (tt0 + kTile <= s.t_end) {
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int t = t0 + u * RPL + ld_row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (t < t_end) {
-        const size_t off = (slab + t) * (size_t)(FP8 ? D : 2 * D) + ld_chunk * 16;
-        kv = load_nt(static_cast<const char*>(a.k) + off);
-        vv = load_nt(static_cast<const char*>(a.v) + off);
+      for (int u = 0; u < NLD; ++u) {
+        kreg[u] = load_nt(kb + lane_off + u * RPL * ROWB);
+        vreg[u] = load_nt(vb + lane_off + u * RPL * ROWB);
       }
-      kreg[u] = kv;
-      vreg[u] = vv;
+    } else {
+      const int last = s.t_end - 1 - tt0;
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const int off = min(u * RPL + ld_row, last) * ROWB + ld_chunk * 16;
+        kreg[u] = load_nt(kb + off);
+        vreg[u] = load_nt(vb + off);
+      }
     }
     if constexpr (FP8) {
+      const float* ksb = a.k_scale + s.slab + tt0;
+      const float* vsb = a.v_scale + s.slab + tt0;
+      const int nvalid = s.t_end - tt0;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * h + 4 * q4 + i;
-          ksc[h][i] = t < t_end ? a.k_scale[slab + t] : 0.f;
-          vsc[h][i] = t < t_end ? a.v_scale[slab + t] : 0.f;
+          const int r = 16 * h + 4 * q4 + i;
+          ksc[h][i] = r < nvalid ? ksb[r] : 0.f;
+          vsc[h][i] = r < nvalid ? vsb[r] : 0.f;
         }
     }
   };
-
-  auto stage_to_lds = [&]() {
+  struct QRows {
+    u32x4 v[QCH];
+  };
+  auto load_q = [&](const Segment& s) {
+    QRows r;
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int r = u * RPL + ld_row;
-      if constexpr (FP8) {
-        // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
-        const int c0 = 2 * ld_chunk;
-        u32x4 klo, khi, vlo, vhi;
-        u32x2 t0 = e4m3x4_to_bf16x4(kreg[u][0]), t1 = e4m3x4_to_bf16x4(kreg[u][1]);
-        u32x2 t2 = e4m3x4_to_bf16x4(kreg[u][2]), t3 = e4m3x4_to_bf16x4(kreg[u][3]);
-        klo = u32x4{t0[0], t0[1], t1[0], t1[1]};
-        khi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-        t0 = e4m3x4_to_bf16x4(vreg[u][0]); t1 = e4m3x4_to_bf16x4(vreg[u][1]);
-        t2 = e4m3x4_to_bf16x4(vreg[u][2]); t3 = e4m3x4_to_bf16x4(vreg[u][3]);
-        vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
-        vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-        const int sw = r % CH;
-        lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), klo);
-        lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
-        lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
-        lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
-      } else {
-        const int pc = ld_chunk ^ (r % CH);
-        lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
-        lds_store(vt + r * (2 * D) + (pc << 4), vreg[u]);
-      }
+    for (int i = 0; i < QCH; ++i) {
+      const int e = threadIdx.x + i * NW * 64;
+      const int hl = e / CH, c = e % CH;
+      r.v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (e < HPC * CH && hl < s.nh)
+        r.v[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                 ((size_t)s.b * a.h_q + s.head0 + hl) * D + 8 * c);
+    }
+    return r;
+  };
+  auto store_q = [&](const QRows& r) {
+#pragma unroll
+    for (int i = 0; i < QCH; ++i) {
+      const int e = threadIdx.x + i * NW * 64;
+      const int hl = e / CH, c = e % CH;
+      if (e < HPC * CH) lds_store(sq + hl * (2 * D) + ((c ^ (hl % CH)) << 4), r.v[i]);
     }
   };
 
-  // ---- running state (per lane: head r16 of every head block)
-  f32x4 o[HB][NT];
-  float m[HB], l[HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    m[hb] = kNegInf;
-    l[hb] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) o[hb][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  // Tiles of a segment are handed out dynamically: wave i starts with tile i,
+  // then claims the next unclaimed one from an LDS counter, so waves whose
+  // loads are served faster take more tiles and all reach the segment's merge
+  // at about the same time.
+  auto claim_tile = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_next_tile, 1);
+    return uniform(__shfl(v, 0, 64));
+  };
 
-  int tile = wave;
-  if (tile < n_tiles) issue_loads(tile);
-  for (; tile < n_tiles; tile += kDecodeWaves) {
-    float kscur[2][4], vscur[2][4];
-    if constexpr (FP8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { kscur[h][i] = ksc[h][i]; vscur[h][i] = vsc[h][i]; }
-    }
-    wave_lds_fence();
-    stage_to_lds();
-    wave_lds_fence();
-    if (tile + kDecodeWaves < n_tiles) issue_loads(tile + kDecodeWaves);
+  Segment cur = make_segment<kTile>(a, ll, lo, hi, w, spb, HPC, lane);
+  if (wave < cur.ntile) issue_loads(cur, wave);
+  wave_lds_fence();
+  store_q(load_q(cur));
+  if (threadIdx.x == 0) s_next_tile = NW;
+  __syncthreads();
 
-    const int t0 = t_begin + tile * kTile;
-    // ---- scores S^T[token][head]: two 16-token halves
-    f32x4 sc[2][HB];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 16 * h + r16;
-      u32x4 kf[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ (row % CH)) << 4));
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) acc = mfma16(kf[kk], qf[hb][kk], acc);
-        sc[h][hb] = acc;
-      }
+  for (;;) {
+    const bool has_next = lo + cur.ntile < hi;
+    Segment nxt = cur;
+    QRows q_next = {};
+    if (has_next) {
+      nxt = make_segment<kTile>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
+      q_next = load_q(nxt);  // used at the segment switch, long after it lands
     }
-    // ---- V fragments (A operand of O^T = V^T P^T), shared by all head blocks
-    u32x4 vf[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      u32x2 lo, hi;
-      {
-        const int row = 4 * q4 + (r16 >> 2);
-        const int col = 16 * nt + 4 * (r16 & 3);  // bf16 column
-        const int c = col >> 3, w = col & 7;
-        lo = lds_read_tr16(vt + row * (2 * D) + ((c ^ (row % CH)) << 4) + 2 * w);
-      }
-      {
-        const int row = 16 + 4 * q4 + (r16 >> 2);
-        const int col = 16 * nt + 4 * (r16 & 3);
-        const int c = col >> 3, w = col & 7;
-        hi = lds_read_tr16(vt + row * (2 * D) + ((c ^ (row % CH)) << 4) + 2 * w);
-      }
-      vf[nt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-    wave_lds_fence();
+    const int t_begin = cur.t_begin, t_end = cur.t_end;
 
-    // ---- online softmax per head block and PV
+    // ---- running state (per lane: head r16 of every head block)
+    f32x4 o[HB][NT];
+    float m[HB], l[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      float sv[2][4];
-      float mt = kNegInf;
+      m[hb] = kNegInf;
+      l[hb] = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * h + 4 * q4 + i;
-          float x = sc[h][hb][i] * a.qk_scale_log2;
-          if constexpr (FP8) x *= kscur[h][i];
-          x = t < t_end ? x : kNegInf;
-          sv[h][i] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = wave_max_xor(mt, 16);
-      mt = wave_max_xor(mt, 32);
-      const float m_new = fmaxf(m[hb], mt);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m[hb] - m_use);
-      m[hb] = m_new;
-      float psum = 0.f;
-      float p[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[h][i] = fast_exp2(sv[h][i] - m_use);
-          psum += p[h][i];
-        }
-      l[hb] = l[hb] * alpha + psum;
+      for (int n = 0; n < NT; ++n) o[hb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int tile = wave; tile < cur.ntile;) {
+      float kscur[2][4], vscur[2][4];
       if constexpr (FP8) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[h][i] *= vscur[h][i];
+          for (int i = 0; i < 4; ++i) {
+            kscur[h][i] = ksc[h][i];
+            vscur[h][i] = vsc[h][i];
+          }
       }
-      const u32x4 pf = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
-                        pack_bf16x2(p[1][2], p[1][3])};
+      const int tt0 = t_begin + tile * kTile;
+      wave_lds_fence();
+      // ---- stage the landed tile into the wave's LDS slab
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        o[hb][nt] *= alpha;
-        o[hb][nt] = mfma16(vf[nt], pf, o[hb][nt]);
-      }
-    }
-  }
-
-  // ---- merge the 4 waves of the workgroup, write one partial per head
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float lt = wave_sum_xor(l[hb], 16);
-    lt = wave_sum_xor(lt, 32);
-    l[hb] = lt;
-  }
-  wave_lds_fence();
-  // O^T[d = 16nt + 4q4 + i][head r16] -> ow[head][d] (float32), reusing the tile slab
-  float* ow = reinterpret_cast<float*>(smem[wave][0]);
-  static_assert(HB * 16 * D * 4 <= 2 * TILE_BYTES, "partial O does not fit the wave slab");
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lds_store(ow + (hb * 16 + r16) * D + 16 * nt + 4 * q4, o[hb][nt]);
-    if (q4 == 0) {
-      sm_ml[wave][hb * 16 + r16][0] = m[hb];
-      sm_ml[wave][hb * 16 + r16][1] = l[hb];
-    }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < nh * D; e += 256) {
-    const int hl = e / D, d = e - hl * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_ml[w][hl][0]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float mw = sm_ml[w][hl][0];
-      const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-      acc += f * reinterpret_cast<const float*>(smem[w][0])[hl * D + d];
-      lsum += f * sm_ml[w][hl][1];
-    }
-    const size_t row = ((size_t)b * a.h_q + head0 + hl) * a.n_split + s;
-    a.part_o[row * D + d] = acc;
-    if (d == 0) {
-      a.part_ml[row * 2 + 0] = M;
-      a.part_ml[row * 2 + 1] = lsum;
-    }
-  }
-}
-
-// ------------------------------------------------------------------------
-// float32 decode on the vector ALUs (16 heads per workgroup).
-// ------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256, 2) void gqa_decode_split_f32(DecodeArgs a) {
-  constexpr int HPC = 16;
-  constexpr int DL = D / 64;  // d columns per lane in the PV product
-  __shared__ __attribute__((aligned(16))) float sq[HPC][D];
-  __shared__ float sp[kDecodeWaves][kTileF32][HPC];
-  __shared__ __attribute__((aligned(16))) float so[kDecodeWaves][HPC][D];
-  __shared__ float sm_ml[kDecodeWaves][HPC][2];
-
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / a.n_hchunk;
-  const int hc = blockIdx.y - g * a.n_hchunk;
-  const int b = blockIdx.z;
-  const int L = min(max(a.seq_lens[b], 0), a.S_max);
-  const int t_begin = s * a.chunk;
-  if (t_begin >= L) return;
-  const int t_end = min(t_begin + a.chunk, L);
-  const int G = a.h_q / a.n_kv;
-  const int hloc0 = hc * HPC;
-  const int nh = min(HPC, G - hloc0);
-  const int head0 = g * G + hloc0;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-
-  const float* qg = static_cast<const float*>(a.q);
-  for (int e = threadIdx.x; e < HPC * D; e += 256) {
-    const int hl = e / D, d = e - hl * D;
-    sq[hl][d] = hl < nh ? qg[((size_t)b * a.h_q + head0 + hl) * D + d] : 0.f;
-  }
-  __syncthreads();
-
-  const float* kg = static_cast<const float*>(a.k);
-  const float* vg = static_cast<const float*>(a.v);
-  const size_t slab = ((size_t)b * a.n_kv + g) * (size_t)a.S_max;
-  const int n_tiles = (t_end - t_begin + kTileF32 - 1) / kTileF32;
-
-  float m[HPC], l[HPC], o[HPC][DL];
-#pragma unroll
-  for (int h = 0; h < HPC; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < DL; ++c) o[h][c] = 0.f;
-  }
-
-  for (int tile = wave; tile < n_tiles; tile += kDecodeWaves) {
-    const int t0 = t_begin + tile * kTileF32;
-    const int t = t0 + lane;
-    const bool valid = t < t_end;
-    float sc[HPC];
-#pragma unroll
-    for (int h = 0; h < HPC; ++h) sc[h] = 0.f;
-    if (valid) {
-      const float4* kr = reinterpret_cast<const float4*>(kg + (slab + t) * D);
-      for (int d4 = 0; d4 < D / 4; ++d4) {
-        const float4 kv = kr[d4];
-#pragma unroll
-        for (int h = 0; h < HPC; ++h) {
-          const float4 qv = *reinterpret_cast<const float4*>(&sq[h][4 * d4]);
-          sc[h] = fmaf(qv.x, kv.x, sc[h]);
-          sc[h] = fmaf(qv.y, kv.y, sc[h]);
-          sc[h] = fmaf(qv.z, kv.z, sc[h]);
-          sc[h] = fmaf(qv.w, kv.w, sc[h]);
+      for (int u = 0; u < NLD; ++u) {
+        const int r = u * RPL + ld_row;
+        if (tt0 + r >= t_end) {  // past the segment end: zero (a cache tail may hold NaN)
+          kreg[u] = u32x4{0u, 0u, 0u, 0u};
+          vreg[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (FP8) {
+          // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
+          const int c0 = 2 * ld_chunk;
+          u32x2 t0 = e4m3x4_to_bf16x4(kreg[u][0]), t1 = e4m3x4_to_bf16x4(kreg[u][1]);
+          u32x2 t2 = e4m3x4_to_bf16x4(kreg[u][2]), t3 = e4m3x4_to_bf16x4(kreg[u][3]);
+          const u32x4 klo = u32x4{t0[0], t0[1], t1[0], t1[1]};
+          const u32x4 khi = u32x4{t2[0], t2[1], t3[0], t3[1]};
+          t0 = e4m3x4_to_bf16x4(vreg[u][0]);
+          t1 = e4m3x4_to_bf16x4(vreg[u][1]);
+          t2 = e4m3x4_to_bf16x4(vreg[u][2]);
+          t3 = e4m3x4_to_bf16x4(vreg[u][3]);
+          const u32x4 vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
+          const u32x4 vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
+          const int sw = r % CH;
+          lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), klo);
+          lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
+          lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
+          lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
+        } else {
+          const int pc = ld_chunk ^ (r % CH);
+          lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
+          lds_store(vt + r * (2 * D) + (pc << 4), vreg[u]);
         }
       }
+      wave_lds_fence();
+      // ---- keep one tile in flight: the next claimed tile of this segment, or
+      // this wave's first tile of the next segment
+      const int next_tile = claim_tile();
+      if (next_tile < cur.ntile) issue_loads(cur, next_tile);
+      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
+
+      // ---- scores S^T[token][head]: two 16-token halves
+      f32x4 sc[2][HB];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * h + r16;
+        u32x4 kf[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ (row % CH)) << 4));
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          // B operand of S^T = K Q^T: lane holds Q[head 16hb + r16][32kk + 8q4 .. +7]
+          const int qrow = 16 * hb + r16;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ (qrow % CH)) << 4)), acc);
+          sc[h][hb] = acc;
+        }
+      }
+      // ---- online softmax per head block -> bf16 probabilities (B operand of PV).
+      // The reference max moves only when a tile's max exceeds it by more than
+      // kRescaleSlack (log2 units): O and l always share the same reference, so
+      // the result is unchanged, p stays <= 2^kRescaleSlack, and the rescale of
+      // O is skipped on almost every tile.
+      const bool tail = tt0 + kTile > t_end;
+      u32x4 pf[HB];
+      bool any_grow = false;
+      float alpha[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float sv[2][4];
+        float mt = kNegInf;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sc[h][hb][i] * a.qk_scale_log2;
+            if constexpr (FP8) x *= kscur[h][i];
+            sv[h][i] = x;
+          }
+        if (tail) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[h][i] = tt0 + 16 * h + 4 * q4 + i < t_end ? sv[h][i] : kNegInf;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sv[h][i]);
+        mt = wave_max_xor(mt, 16);
+        mt = wave_max_xor(mt, 32);
+        const bool grow = mt > m[hb] + kRescaleSlack;
+        const float m_new = grow ? mt : m[hb];
+        alpha[hb] = grow ? fast_exp2(m[hb] - m_new) : 1.0f;
+        any_grow = any_grow || grow;
+        m[hb] = m_new;
+        float psum = 0.f;
+        float p[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[h][i] = fast_exp2(sv[h][i] - m_new);
+            psum += p[h][i];
+          }
+        l[hb] = l[hb] * alpha[hb] + psum;
+        if constexpr (FP8) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[h][i] *= vscur[h][i];
+        }
+        pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                       pack_bf16x2(p[1][2], p[1][3])};
+      }
+      if (__builtin_amdgcn_ballot_w64(any_grow)) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) o[hb][n] *= alpha[hb];
+      }
+      // ---- O^T += V^T P^T: one 16-wide d tile of V at a time, shared by all head blocks
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int col = 16 * n + 4 * (r16 & 3);  // bf16 column
+        const int c = col >> 3, wsub = col & 7;
+        const int row_lo = 4 * q4 + (r16 >> 2);
+        const int row_hi = 16 + row_lo;
+        const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ (row_lo % CH)) << 4) + 2 * wsub);
+        const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ (row_hi % CH)) << 4) + 2 * wsub);
+        const u32x4 vf = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
+      }
+      tile = next_tile;
     }
-    float alpha[HPC];
+    // a wave with no tile in this segment starts its next-segment tile now
+    if (wave >= cur.ntile && has_next && wave < nxt.ntile) issue_loads(nxt, wave);
+
+    // ---- merge the waves of the workgroup, write one partial per head
 #pragma unroll
-    for (int h = 0; h < HPC; ++h) {
-      const float x = valid ? sc[h] * a.qk_scale_log2 : kNegInf;
-      float mt = x;
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) mt = wave_max_xor(mt, msk);
-      const float m_new = fmaxf(m[h], mt);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      alpha[h] = fast_exp2(m[h] - m_use);
-      m[h] = m_new;
-      const float p = fast_exp2(x - m_use);
-      l[h] = l[h] * alpha[h] + p;
-      sp[wave][lane][h] = p;
+    for (int hb = 0; hb < HB; ++hb) {
+      float lt = wave_sum_xor(l[hb], 16);
+      lt = wave_sum_xor(lt, 32);
+      l[hb] = lt;
     }
     wave_lds_fence();
-    const int nvalid = min(kTileF32, t_end - t0);
+    // O^T[d = 16n + 4q4 + i][head r16] -> ow[head][d] (float32), reusing the wave slab
 #pragma unroll
-    for (int h = 0; h < HPC; ++h)
+    for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-      for (int c = 0; c < DL; ++c) o[h][c] *= alpha[h];
-    for (int tt = 0; tt < nvalid; ++tt) {
-      const float* vr = vg + (slab + t0 + tt) * D;
-      float vv[DL];
-#pragma unroll
-      for (int c = 0; c < DL; ++c) vv[c] = vr[lane + 64 * c];
-#pragma unroll
-      for (int h = 0; h < HPC; ++h) {
-        const float p = sp[wave][tt][h];
-#pragma unroll
-        for (int c = 0; c < DL; ++c) o[h][c] = fmaf(p, vv[c], o[h][c]);
+      for (int n = 0; n < NT; ++n) lds_store(ow + (hb * 16 + r16) * D + 16 * n + 4 * q4, o[hb][n]);
+      if (q4 == 0) {
+        sm_ml[wave][hb * 16 + r16][0] = m[hb];
+        sm_ml[wave][hb * 16 + r16][1] = l[hb];
       }
     }
-    wave_lds_fence();
-  }
+    __syncthreads();
+    for (int e = threadIdx.x; e < cur.nh * D; e += NW * 64) {
+      const int hl = e / D, d = e - hl * D;
+      float M = kNegInf;
 #pragma unroll
-  for (int h = 0; h < HPC; ++h) {
-    float lt = l[h];
+      for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, sm_ml[wv][hl][0]);
+      float acc = 0.f, lsum = 0.f;
 #pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) lt = wave_sum_xor(lt, msk);
-#pragma unroll
-    for (int c = 0; c < DL; ++c) so[wave][h][lane + 64 * c] = o[h][c];
-    if (lane == 0) {
-      sm_ml[wave][h][0] = m[h];
-      sm_ml[wave][h][1] = lt;
+      for (int wv = 0; wv < NW; ++wv) {
+        const float mw = sm_ml[wv][hl][0];
+        const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+        acc += f * reinterpret_cast<const float*>(smem[wv][0])[hl * D + d];
+        lsum += f * sm_ml[wv][hl][1];
+      }
+      const size_t row = (size_t)cur.slot * HPC + hl;
+      a.part_o[row * D + d] = acc;
+      if (d == 0) {
+        a.part_ml[row * 2 + 0] = M;
+        a.part_ml[row * 2 + 1] = lsum;
+      }
     }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < nh * D; e += 256) {
-    const int hl = e / D, d = e - hl * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, sm_ml[w][hl][0]);
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float mw = sm_ml[w][hl][0];
-      const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-      acc += f * so[w][hl][d];
-      lsum += f * sm_ml[w][hl][1];
-    }
-    const size_t row = ((size_t)b * a.h_q + head0 + hl) * a.n_split + s;
-    a.part_o[row * D + d] = acc;
-    if (d == 0) {
-      a.part_ml[row * 2 + 0] = M;
-      a.part_ml[row * 2 + 1] = lsum;
-    }
+    if (!has_next) break;
+    store_q(q_next);  // sq is not read by the merge
+    if (threadIdx.x == 0) s_next_tile = NW;  // every wave is past its last claim
+    __syncthreads();  // slabs, sq and the tile counter ready for the next segment
+    lo += cur.ntile;
+    cur = nxt;
   }
 }
 
 // ------------------------------------------------------------------------
-// Combine: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.  One wave per
-// (sequence, query head); chunks past the sequence end were never written
-// and are not read.
+// float32 decode on the vector ALUs (16 heads per workgroup, 4 waves,
+// 64-token tiles: one token per lane for the scores, one d column per lane
+// for the PV product).
+// ------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
+  constexpr int HPC = 16;
+  constexpr int NW = kWavesF32;
+  constexpr int DL = D / 64;  // d columns per lane in the PV product
+  __shared__ __attribute__((aligned(16))) float sq[HPC][D];
+  __shared__ float sp[NW][kTileF32][HPC];
+  __shared__ __attribute__((aligned(16))) float so[NW][HPC][D];
+  __shared__ float sm_ml[NW][HPC][2];
+
+  const int W = gridDim.x;
+  const int w = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int spb = a.n_kv * a.n_hchunk;
+  const int G = a.h_q / a.n_kv;
+  const long long T = tiles_before(a.seq_lens, a.B, a.S_max, kTileF32, spb, lane);
+  const long long lo = (long long)w * T / W;
+  const long long hi = (long long)(w + 1) * T / W;
+  const float* qg = static_cast<const float*>(a.q);
+  const float* kg = static_cast<const float*>(a.k);
+  const float* vg = static_cast<const float*>(a.v);
+
+  for (long long t = lo; t < hi;) {
+    int b, nt, L;
+    long long base;
+    locate_tile(a.seq_lens, a.B, a.S_max, kTileF32, spb, t, lane, b, base, nt, L);
+    const long long local = t - base;
+    const int slab_in_b = (int)(local / nt);
+    const int tile0 = (int)(local - (long long)slab_in_b * nt);
+    const int seg = (int)min(hi - t, (long long)(nt - tile0));
+    const int g = slab_in_b / a.n_hchunk;
+    const int hc = slab_in_b - g * a.n_hchunk;
+    const long long slot = w + (long long)b * spb + slab_in_b;
+    t += seg;
+
+    const int t_begin = tile0 * kTileF32;
+    const int t_end = min((tile0 + seg) * kTileF32, L);
+    const int hloc0 = hc * HPC;
+    const int nh = min(HPC, G - hloc0);
+    const int head0 = g * G + hloc0;
+
+    for (int e = threadIdx.x; e < HPC * D; e += NW * 64) {
+      const int hl = e / D, d = e - hl * D;
+      sq[hl][d] = hl < nh ? qg[((size_t)b * a.h_q + head0 + hl) * D + d] : 0.f;
+    }
+    __syncthreads();
+
+    const size_t slab = ((size_t)b * a.n_kv + g) * (size_t)a.S_max;
+    float m[HPC], l[HPC], o[HPC][DL];
+#pragma unroll
+    for (int h = 0; h < HPC; ++h) {
+      m[h] = kNegInf;
+      l[h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) o[h][c] = 0.f;
+    }
+
+    for (int tile = wave; tile < seg; tile += NW) {
+      const int tt0 = t_begin + tile * kTileF32;
+      const int tok = tt0 + lane;
+      const bool valid = tok < t_end;
+      float sc[HPC];
+#pragma unroll
+      for (int h = 0; h < HPC; ++h) sc[h] = 0.f;
+      if (valid) {
+        const float4* kr = reinterpret_cast<const float4*>(kg + (slab + tok) * D);
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+          const float4 kv = kr[d4];
+#pragma unroll
+          for (int h = 0; h < HPC; ++h) {
+            const float4 qv = *reinterpret_cast<const float4*>(&sq[h][4 * d4]);
+            sc[h] = fmaf(qv.x, kv.x, sc[h]);
+            sc[h] = fmaf(qv.y, kv.y, sc[h]);
+            sc[h] = fmaf(qv.z, kv.z, sc[h]);
+            sc[h] = fmaf(qv.w, kv.w, sc[h]);
+          }
+        }
+      }
+      float alpha[HPC];
+#pragma unroll
+      for (int h = 0; h < HPC; ++h) {
+        const float x = valid ? sc[h] * a.qk_scale_log2 : kNegInf;
+        float mt = x;
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) mt = wave_max_xor(mt, msk);
+        const float m_new = fmaxf(m[h], mt);
+        const float m_use = m_new == kNegInf ? 0.f : m_new;
+        alpha[h] = fast_exp2(m[h] - m_use);
+        m[h] = m_new;
+        const float p = fast_exp2(x - m_use);
+        l[h] = l[h] * alpha[h] + p;
+        sp[wave][lane][h] = p;
+      }
+      wave_lds_fence();
+      const int nvalid = min(kTileF32, t_end - tt0);
+#pragma unroll
+      for (int h = 0; h < HPC; ++h)
+#pragma unroll
+        for (int c = 0; c < DL; ++c) o[h][c] *= alpha[h];
+      for (int tt = 0; tt < nvalid; ++tt) {
+        const float* vr = vg + (slab + tt0 + tt) * D;
+        float vv[DL];
+#pragma unroll
+        for (int c = 0; c < DL; ++c) vv[c] = vr[lane + 64 * c];
+#pragma unroll
+        for (int h = 0; h < HPC; ++h) {
+          const float p = sp[wave][tt][h];
+#pragma unroll
+          for (int c = 0; c < DL; ++c) o[h][c] = fmaf(p, vv[c], o[h][c]);
+        }
+      }
+      wave_lds_fence();
+    }
+#pragma unroll
+    for (int h = 0; h < HPC; ++h) {
+      float lt = l[h];
+#pragma unroll
+      for (int msk = 32; msk >= 1; msk >>= 1) lt = wave_sum_xor(lt, msk);
+#pragma unroll
+      for (int c = 0; c < DL; ++c) so[wave][h][lane + 64 * c] = o[h][c];
+      if (lane == 0) {
+        sm_ml[wave][h][0] = m[h];
+        sm_ml[wave][h][1] = lt;
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nh * D; e += NW * 64) {
+      const int hl = e / D, d = e - hl * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, sm_ml[wv][hl][0]);
+      float acc = 0.f, lsum = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) {
+        const float mw = sm_ml[wv][hl][0];
+        const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+        acc += f * so[wv][hl][d];
+        lsum += f * sm_ml[wv][hl][1];
+      }
+      const size_t row = (size_t)slot * HPC + hl;
+      a.part_o[row * D + d] = acc;
+      if (d == 0) {
+        a.part_ml[row * 2 + 0] = M;
+        a.part_ml[row * 2 + 1] = lsum;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------
+// Combine: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
+// partials of one slab.  One workgroup per slab (sequence, kv-head, head
+// chunk); each thread owns 4 consecutive output columns of one head.
 // ------------------------------------------------------------------------
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gqa_decode_combine(const float* __restrict__ part_o,
-                                                          const float* __restrict__ part_ml,
-                                                          const int32_t* __restrict__ seq_lens, void* out, int B,
-                                                          int h_q, int S_max, int chunk, int n_split) {
-  constexpr int DL = D / 64;
-  const int row_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(256) void gqa_decode_combine(CombineArgs c) {
+  constexpr int D4 = D / 4;
+  const int sigma = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  if (row_id >= B * h_q) return;
-  const int b = row_id / h_q;
-  const int L = min(max(seq_lens[b], 0), S_max);
-  const int ns = (L + chunk - 1) / chunk;
-  const size_t base = (size_t)row_id * n_split;
-  float acc[DL];
-#pragma unroll
-  for (int c = 0; c < DL; ++c) acc[c] = 0.f;
-  float denom = 0.f;
-  if (ns > 0) {
-    float M = kNegInf;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(base + s) * 2]);
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) M = wave_max_xor(M, msk);
-    for (int s = 0; s < ns; ++s) {
-      const float ms = part_ml[(base + s) * 2];
-      const float ls = part_ml[(base + s) * 2 + 1];
-      const float w = ms == kNegInf ? 0.f : fast_exp2(ms - M);
-      denom += w * ls;
-#pragma unroll
-      for (int c = 0; c < DL; ++c) acc[c] += w * part_o[(base + s) * D + lane + 64 * c];
-    }
+  const int spb = c.n_kv * c.n_hchunk;
+  const int b = sigma / spb;
+  const int slab_in_b = sigma - b * spb;
+  const int g = slab_in_b / c.n_hchunk;
+  const int hc = slab_in_b - g * c.n_hchunk;
+  const int G = c.h_q / c.n_kv;
+  const int hpc = c.heads_per_chunk;
+  const int hloc0 = hc * hpc;
+  const int nh = min(hpc, G - hloc0);
+  const int head0 = g * G + hloc0;
+  const int nt = seq_tiles(c.seq_lens, b, c.S_max, c.tile);
+
+  // The slab's partials: one per workgroup whose range touches the slab.  When
+  // T >= W every range is non-empty, so these are exactly the workgroups from
+  // the owner of the slab's first tile to the owner of its last; when T < W a
+  // range holds at most one tile and the owners are enumerated tile by tile.
+  long long first = 0, wa = 0, T = 1;
+  int n_pieces = 0;
+  bool per_tile = false;
+  if (nt > 0) {
+    T = tiles_before(c.seq_lens, c.B, c.S_max, c.tile, spb, lane);
+    first = tiles_before(c.seq_lens, b, c.S_max, c.tile, spb, lane) + (long long)slab_in_b * nt;
+    const long long W = c.W;
+    wa = ((first + 1) * W - 1) / T;
+    per_tile = T < W;
+    n_pieces = per_tile ? nt : (int)(((first + nt) * W - 1) / T - wa + 1);
   }
-  const float inv = denom > 0.f ? 1.0f / denom : 0.f;
-#pragma unroll
-  for (int c = 0; c < DL; ++c) {
-    const float v = acc[c] * inv;
-    const size_t idx = (size_t)row_id * D + lane + 64 * c;
+  auto piece_slot = [&](int p) -> long long {
+    const long long w = per_tile ? ((first + p + 1) * (long long)c.W - 1) / T : wa + p;
+    return w + sigma;
+  };
+  for (int e = threadIdx.x; e < nh * D4; e += 256) {
+    const int hl = e / D4, d4 = e - hl * D4;
+    float M = kNegInf;
+    for (int p = 0; p < n_pieces; ++p) M = fmaxf(M, c.part_ml[(piece_slot(p) * hpc + hl) * 2]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float denom = 0.f;
+#pragma unroll 4
+    for (int p = 0; p < n_pieces; ++p) {
+      const size_t row = (size_t)piece_slot(p) * hpc + hl;
+      const float ms = c.part_ml[row * 2];
+      const float f = ms == kNegInf ? 0.f : fast_exp2(ms - M);
+      denom += f * c.part_ml[row * 2 + 1];
+      acc += f * *reinterpret_cast<const f32x4*>(c.part_o + row * D + 4 * d4);
+    }
+    const float inv = denom > 0.f ? 1.0f / denom : 0.f;
+    acc *= inv;
+    const size_t idx = ((size_t)b * c.h_q + head0 + hl) * D + 4 * d4;
     if constexpr (OUT_BF16) {
-      static_cast<__bf16*>(out)[idx] = (__bf16)v;
+      u32x2 wv;
+      wv[0] = pack_bf16x2(acc[0], acc[1]);
+      wv[1] = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c.out) + idx) = wv;
     } else {
-      static_cast<float*>(out)[idx] = v;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(c.out) + idx) = acc;
     }
   }
 }
 
 // ------------------------------------------------------------------------
-// Host-side launchers (called from api.cpp).
+// Host-side launchers (called from api.hip).
 // ------------------------------------------------------------------------
-hipError_t launch_decode_split(const DecodeArgs& a, int B, int D, int hb, int kind, hipStream_t stream) {
-  const dim3 grid(a.n_split, a.n_kv * a.n_hchunk, B);
-  const dim3 block(256);
-  // kind: 0 = f32, 1 = bf16 K/V, 2 = fp8 K/V
+constexpr int kWavesMfma = 8;
+
+hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream) {
+  const dim3 grid(W);
   if (kind == 0) {
+    const dim3 block(kWavesF32 * 64);
     if (D == 64) hipLaunchKernelGGL(gqa_decode_split_f32<64>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(gqa_decode_split_f32<128>, grid, block, 0, stream, a);
-  } else if (kind == 1) {
-    if (D == 64 && hb == 1) hipLaunchKernelGGL((gqa_decode_split_mfma<64, 1, false>), grid, block, 0, stream, a);
-    else if (D == 64) hipLaunchKernelGGL((gqa_decode_split_mfma<64, 2, false>), grid, block, 0, stream, a);
-    else if (hb == 1) hipLaunchKernelGGL((gqa_decode_split_mfma<128, 1, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gqa_decode_split_mfma<128, 2, false>), grid, block, 0, stream, a);
-  } else {
-    if (D == 64 && hb == 1) hipLaunchKernelGGL((gqa_decode_split_mfma<64, 1, true>), grid, block, 0, stream, a);
-    else if (D == 64) hipLaunchKernelGGL((gqa_decode_split_mfma<64, 2, true>), grid, block, 0, stream, a);
-    else if (hb == 1) hipLaunchKernelGGL((gqa_decode_split_mfma<128, 1, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gqa_decode_split_mfma<128, 2, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
   }
+  const dim3 block(kWavesMfma * 64);
+#define GQA_LAUNCH_DECODE(DD, HH, F8) \
+  hipLaunchKernelGGL((gqa_decode_split_mfma<DD, HH, F8, kWavesMfma>), grid, block, 0, stream, a)
+  const bool fp8 = kind == 2;
+  if (D == 64) {
+    if (hb == 1) { if (fp8) GQA_LAUNCH_DECODE(64, 1, true); else GQA_LAUNCH_DECODE(64, 1, false); }
+    else { if (fp8) GQA_LAUNCH_DECODE(64, 2, true); else GQA_LAUNCH_DECODE(64, 2, false); }
+  } else {
+    if (hb == 1) { if (fp8) GQA_LAUNCH_DECODE(128, 1, true); else GQA_LAUNCH_DECODE(128, 1, false); }
+    else { if (fp8) GQA_LAUNCH_DECODE(128, 2, true); else GQA_LAUNCH_DECODE(128, 2, false); }
+  }
+#undef GQA_LAUNCH_DECODE
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const float* part_o, const float* part_ml, const int32_t* seq_lens, void* out,
-                                 bool out_bf16, int B, int h_q, int S_max, int D, int chunk, int n_split,
-                                 hipStream_t stream) {
-  const dim3 grid((B * h_q + 3) / 4);
+hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream) {
+  const dim3 grid(c.B * c.n_kv * c.n_hchunk);
   const dim3 block(256);
   if (D == 64) {
-    if (out_bf16) hipLaunchKernelGGL((gqa_decode_combine<64, true>), grid, block, 0, stream, part_o, part_ml, seq_lens, out, B, h_q, S_max, chunk, n_split);
-    else hipLaunchKernelGGL((gqa_decode_combine<64, false>), grid, block, 0, stream, part_o, part_ml, seq_lens, out, B, h_q, S_max, chunk, n_split);
+    if (out_bf16) hipLaunchKernelGGL((gqa_decode_combine<64, true>), grid, block, 0, stream, c);
+    else hipLaunchKernelGGL((gqa_decode_combine<64, false>), grid, block, 0, stream, c);
   } else {
-    if (out_bf16) hipLaunchKernelGGL((gqa_decode_combine<128, true>), grid, block, 0, stream, part_o, part_ml, seq_lens, out, B, h_q, S_max, chunk, n_split);
-    else hipLaunchKernelGGL((gqa_decode_combine<128, false>), grid, block, 0, stream, part_o, part_ml, seq_lens, out, B, h_q, S_max, chunk, n_split);
+    if (out_bf16) hipLaunchKernelGGL((gqa_decode_combine<128, true>), grid, block, 0, stream, c);
+    else hipLaunchKernelGGL((gqa_decode_combine<128, false>), grid, block, 0, stream, c);
   }
   return hipGetLastError();
 }

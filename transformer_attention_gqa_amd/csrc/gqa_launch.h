@@ -6,6 +6,18 @@
 
 namespace gqa {
 
+// Decode work schedule.  The keys of one (sequence b, kv-head g, head chunk hc)
+// form a "slab" of ceil(L_b / tile) tiles; slabs are ordered (b, g, hc) and
+// their tiles concatenated into one global tile range [0, T).  Workgroup w of
+// the W launched takes the balanced range [w*T/W, (w+1)*T/W), which may cross
+// slab boundaries; for each slab sigma it touches it leaves one partial
+// (O, m, l) per head in slot (w + sigma).  Distinct (w, sigma) pairs of
+// non-empty ranges never share a slot, so there are at most W + n_slabs slots
+// and no atomics.  The combine for a slab recomputes which workgroups covered
+// it: tile t belongs to workgroup ((t+1)*W - 1) / T; for T >= W every range
+// is non-empty and the slab's partials come from all workgroups between the
+// owners of its first and last tile; for T < W each range holds at most one
+// tile and the owners are taken tile by tile.
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -13,18 +25,25 @@ struct DecodeArgs {
   const float* k_scale;
   const float* v_scale;
   const int32_t* seq_lens;
-  float* part_o;   // [B][h_q][n_split][D]
-  float* part_ml;  // [B][h_q][n_split][2]: running max (log2 domain), running sum
+  float* part_o;   // [W + n_slabs][heads_per_chunk][D]
+  float* part_ml;  // [W + n_slabs][heads_per_chunk][2]: running max (log2 domain), running sum
   float qk_scale_log2;
-  int h_q, n_kv, S_max, chunk, n_split, n_hchunk, heads_per_chunk;
+  int B, h_q, n_kv, S_max, n_hchunk, heads_per_chunk;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* seq_lens;
+  void* out;
+  int B, h_q, n_kv, S_max, n_hchunk, heads_per_chunk, tile, W;
 };
 
 // kind: 0 = float32 Q/K/V, 1 = bf16 Q/K/V, 2 = bf16 Q with e4m3 K/V.
 // hb: 16-head blocks per workgroup on the matrix-core paths (1 or 2).
-hipError_t launch_decode_split(const DecodeArgs& a, int B, int D, int hb, int kind, hipStream_t stream);
-hipError_t launch_decode_combine(const float* part_o, const float* part_ml, const int32_t* seq_lens, void* out,
-                                 bool out_bf16, int B, int h_q, int S_max, int D, int chunk, int n_split,
-                                 hipStream_t stream);
+// W: number of workgroups (balanced key ranges).
+hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream);
+hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream);
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S, int h_q, int n_kv, int D, hipStream_t stream);
 
