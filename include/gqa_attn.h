@@ -32,6 +32,8 @@
  *    long as each decode call has its own workspace.
  *  - `out` must not overlap any input or the workspace.
  *  - Supported head dimensions: d_h = 64 or 128.
+ *  - `scale` multiplies q . k before the softmax (the modules use
+ *    head_dim ** -0.5); it must be finite and > 0 (GQA_ERR_VALUE otherwise).
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -62,7 +64,8 @@ typedef enum gqa_status {
   GQA_ERR_DTYPE = 3,     /* unsupported element-type combination              */
   GQA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
   GQA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
-  GQA_ERR_HIP = 6        /* a HIP launch or query failed                      */
+  GQA_ERR_HIP = 6,       /* a HIP launch or query failed                      */
+  GQA_ERR_VALUE = 7      /* scale is not a finite number > 0                  */
 } gqa_status;
 
 /* ---------------------------------------------------------------- decode --

@@ -121,6 +121,18 @@ def test_prefill_errors(lib):
     assert call(pd(), out=MISALIGNED) == 4
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_scale_must_be_finite_positive(lib, scale):
+    desc = dd()
+    need = lib.attn_decode_workspace_bytes(ctypes.byref(desc))
+    assert lib.attn_decode(ctypes.byref(desc), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, scale, ALIGNED,
+                           ALIGNED, need, None) == 7
+    assert lib.attn_decode_partials(ctypes.byref(desc), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, scale,
+                                    ALIGNED, need, None) == 7
+    pdesc = binding.gqa_prefill_desc(1, 16, 4, 2, 128, 1)
+    assert lib.attn_prefill_causal(ctypes.byref(pdesc), ALIGNED, ALIGNED, ALIGNED, scale, ALIGNED, None) == 7
+
+
 def test_status_strings(lib):
     for code, name in binding.STATUS.items():
         assert lib.gqa_status_string(code).decode().startswith(name)

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE", 4: "GQA_ERR_ALIGN",
-          5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP"}
+          5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE"}
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
             "attn_decode_combine", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
 

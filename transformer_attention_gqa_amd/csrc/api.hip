@@ -31,6 +31,9 @@ void record_hip_error(hipError_t e) {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// The kernels take the running max on unscaled scores, which needs scale > 0.
+bool bad_scale(float s) { return !(s > 0.0f) || !(s < __builtin_huge_valf()); }
+
 struct DecodePlan {
   int kind;             // 0 f32, 1 bf16 K/V, 2 fp8 K/V
   int tile;             // tokens per wave tile
@@ -178,6 +181,7 @@ gqa_status attn_decode_partials(const gqa_decode_desc* d, const void* q, const v
   if (st != GQA_OK) return st;
   st = check_decode_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, seq_lens);
   if (st != GQA_OK) return st;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
   const DecodePlan p = plan_decode(d);
   if (!workspace || workspace_bytes < workspace_layout(d, p, nullptr)) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
@@ -206,6 +210,7 @@ gqa_status attn_decode(const gqa_decode_desc* d, const void* q, const void* k_ca
   if (st != GQA_OK) return st;
   if (!out) return GQA_ERR_NULL;
   if (misaligned(out)) return GQA_ERR_ALIGN;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
   const DecodePlan p = plan_decode(d);
   if (!workspace || workspace_bytes < workspace_layout(d, p, nullptr)) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
@@ -224,6 +229,7 @@ gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const v
   if (d->dtype != GQA_BF16) return GQA_ERR_DTYPE;
   if (!q || !k || !v || !out) return GQA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return GQA_ERR_ALIGN;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
   hipError_t e = launch_prefill_causal(q, k, v, out, (float)((double)scale * kLog2e), d->B, d->S, d->h_q, d->n_kv,
                                        d->d_h, stream);
   if (e != hipSuccess) {
@@ -242,6 +248,7 @@ const char* gqa_status_string(gqa_status s) {
     case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer not 16-byte aligned";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch failed";
+    case GQA_ERR_VALUE: return "GQA_ERR_VALUE: scale must be finite and > 0";
   }
   return "unknown gqa_status";
 }

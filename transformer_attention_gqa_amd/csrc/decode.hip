@@ -205,6 +205,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   constexpr int NT = D / 16;  // 16-wide d tiles of the PV product
   constexpr int TILE_BYTES = kTile * D * 2;
   constexpr int HPC = 16 * HB;
+  // 32 heads of a bf16 cache: one 32x32 score tile per 32 tokens on
+  // v_mfma_f32_32x32x16_bf16 (the same shape as the prefill kernel with heads
+  // in place of query rows); otherwise HB blocks of 16 heads on 16x16x32.
+  constexpr bool M32 = HB == 2 && !FP8;
+  constexpr int KS = D / 16;  // k-steps of the 32x32 score product
+  constexpr int NT32 = D / 32;
   static_assert(HPC * D * 4 <= 2 * TILE_BYTES, "partial O does not fit the wave slab");
   constexpr int QCH = (HPC * CH + NW * 64 - 1) / (NW * 64);  // 16-byte query chunks per thread
   __shared__ __attribute__((aligned(16))) char smem[NW][2][TILE_BYTES];
@@ -336,15 +342,25 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     }
     const int t_begin = cur.t_begin, t_end = cur.t_end;
 
-    // ---- running state (per lane: head r16 of every head block)
-    f32x4 o[HB][NT];
+    // ---- running state (per lane: head r16 of every head block; head l32 in the 32x32 shape)
+    f32x4 o[M32 ? 1 : HB][M32 ? 1 : NT];
+    f32x16 o32[M32 ? NT32 : 1];
     float m[HB], l[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       m[hb] = kNegInf;
       l[hb] = 0.f;
+    }
+    if constexpr (M32) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) o[hb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NT32; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o32[n][r] = 0.f;
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) o[hb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     for (int tile = wave; tile < cur.ntile;) {
@@ -399,101 +415,155 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       if (next_tile < cur.ntile) issue_loads(cur, next_tile);
       else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
 
-      // ---- scores S^T[token][head]: two 16-token halves
-      f32x4 sc[2][HB];
+      if constexpr (M32) {
+        const int l32 = lane & 31, h2 = lane >> 5;
+        // ---- S^T[32 tokens][32 heads] = K Q^T: lane holds tokens 8(r/4)+4h2+r%4 of head l32
+        f32x16 sacc;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 16 * h + r16;
-        u32x4 kf[KK];
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ (row % CH)) << 4));
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          // B operand of S^T = K Q^T: lane holds Q[head 16hb + r16][32kk + 8q4 .. +7]
-          const int qrow = 16 * hb + r16;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ (qrow % CH)) << 4)), acc);
-          sc[h][hb] = acc;
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 kf = lds_load<u32x4>(kt + l32 * (2 * D) + (((2 * ks + h2) ^ (l32 % CH)) << 4));
+          const u32x4 qf = lds_load<u32x4>(sq + l32 * (2 * D) + (((2 * ks + h2) ^ (l32 % CH)) << 4));
+          sacc = mfma32(kf, qf, sacc);
         }
-      }
-      // ---- online softmax per head block -> bf16 probabilities (B operand of PV).
-      // The reference max moves only when a tile's max exceeds it by more than
-      // kRescaleSlack (log2 units): O and l always share the same reference, so
-      // the result is unchanged, p stays <= 2^kRescaleSlack, and the rescale of
-      // O is skipped on almost every tile.
-      const bool tail = tt0 + kTile > t_end;
-      u32x4 pf[HB];
-      bool any_grow = false;
-      float alpha[HB];
+        if (tt0 + kTile > t_end) {
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        float sv[2][4];
+          for (int r = 0; r < 16; ++r)
+            sacc[r] = tt0 + 8 * (r >> 2) + 4 * h2 + (r & 3) < t_end ? sacc[r] : kNegInf;
+        }
         float mt = kNegInf;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sc[h][hb][i] * a.qk_scale_log2;
-            if constexpr (FP8) x *= kscur[h][i];
-            sv[h][i] = x;
-          }
-        if (tail) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sv[h][i] = tt0 + 16 * h + 4 * q4 + i < t_end ? sv[h][i] : kNegInf;
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sv[h][i]);
-        mt = wave_max_xor(mt, 16);
-        mt = wave_max_xor(mt, 32);
-        const bool grow = mt > m[hb] + kRescaleSlack;
-        const float m_new = grow ? mt : m[hb];
-        alpha[hb] = grow ? fast_exp2(m[hb] - m_new) : 1.0f;
-        any_grow = any_grow || grow;
-        m[hb] = m_new;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+        mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
+        const bool grow = mt > m[0] + kRescaleSlack;
+        const float m_new = grow ? mt : m[0];
+        const float alpha = grow ? fast_exp2(m[0] - m_new) : 1.0f;
+        m[0] = m_new;
         float psum = 0.f;
-        float p[2][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[h][i] = fast_exp2(sv[h][i] - m_new);
-            psum += p[h][i];
-          }
-        l[hb] = l[hb] * alpha[hb] + psum;
-        if constexpr (FP8) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[h][i] *= vscur[h][i];
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = fast_exp2(__builtin_fmaf(sacc[r], a.qk_scale_log2, -m_new));
+          psum += sacc[r];
         }
-        pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
-                       pack_bf16x2(p[1][2], p[1][3])};
-      }
-      if (__builtin_amdgcn_ballot_w64(any_grow)) {
+        l[0] = l[0] * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+          for (int n = 0; n < NT32; ++n) o32[n] *= alpha;
+        }
+        // ---- O^T += V^T P^T, two k-steps of 16 tokens (token order permuted as in S)
+        const int gi = lane >> 4, s16 = lane & 15;
 #pragma unroll
-          for (int n = 0; n < NT; ++n) o[hb][n] *= alpha[hb];
-      }
-      // ---- O^T += V^T P^T: one 16-wide d tile of V at a time, shared by all head blocks
+        for (int p = 0; p < 2; ++p) {
+          const u32x4 pf = {pack_bf16x2(sacc[8 * p + 0], sacc[8 * p + 1]), pack_bf16x2(sacc[8 * p + 2], sacc[8 * p + 3]),
+                            pack_bf16x2(sacc[8 * p + 4], sacc[8 * p + 5]), pack_bf16x2(sacc[8 * p + 6], sacc[8 * p + 7])};
+          const int ra = 16 * p + 4 * h2 + (s16 >> 2), rb = ra + 8;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int col = 16 * n + 4 * (r16 & 3);  // bf16 column
-        const int c = col >> 3, wsub = col & 7;
-        const int row_lo = 4 * q4 + (r16 >> 2);
-        const int row_hi = 16 + row_lo;
-        const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ (row_lo % CH)) << 4) + 2 * wsub);
-        const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ (row_hi % CH)) << 4) + 2 * wsub);
-        const u32x4 vf = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
+          for (int n = 0; n < NT32; ++n) {
+            const int col = 32 * n + 16 * (gi & 1) + 4 * (s16 & 3);
+            const int c = col >> 3, wsub = col & 7;
+            const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ (ra % CH)) << 4) + 2 * wsub);
+            const u32x2 vb = lds_read_tr16(vt + rb * (2 * D) + ((c ^ (rb % CH)) << 4) + 2 * wsub);
+            o32[n] = mfma32(u32x4{va[0], va[1], vb[0], vb[1]}, pf, o32[n]);
+          }
+        }
+      } else {
+        // ---- scores S^T[token][head]: two 16-token halves
+        f32x4 sc[2][HB];
+  #pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * h + r16;
+          u32x4 kf[KK];
+  #pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ (row % CH)) << 4));
+  #pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            // B operand of S^T = K Q^T: lane holds Q[head 16hb + r16][32kk + 8q4 .. +7]
+            const int qrow = 16 * hb + r16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+              acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ (qrow % CH)) << 4)), acc);
+            sc[h][hb] = acc;
+          }
+        }
+        // ---- online softmax per head block -> bf16 probabilities (B operand of PV).
+        // The reference max moves only when a tile's max exceeds it by more than
+        // kRescaleSlack (log2 units): O and l always share the same reference, so
+        // the result is unchanged, p stays <= 2^kRescaleSlack, and the rescale of
+        // O is skipped on almost every tile.
+        const bool tail = tt0 + kTile > t_end;
+        u32x4 pf[HB];
+        bool any_grow = false;
+        float alpha[HB];
+  #pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          float sv[2][4];
+          float mt = kNegInf;
+  #pragma unroll
+          for (int h = 0; h < 2; ++h)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = sc[h][hb][i];
+              if constexpr (FP8) x *= kscur[h][i];  // the per-token K scale (> 0)
+              sv[h][i] = x;
+            }
+          if (tail) {
+  #pragma unroll
+            for (int h = 0; h < 2; ++h)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) sv[h][i] = tt0 + 16 * h + 4 * q4 + i < t_end ? sv[h][i] : kNegInf;
+          }
+  #pragma unroll
+          for (int h = 0; h < 2; ++h)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sv[h][i]);
+          mt = wave_max_xor(mt, 16);
+          mt = wave_max_xor(mt, 32) * a.qk_scale_log2;  // scale > 0 keeps the order
+          const bool grow = mt > m[hb] + kRescaleSlack;
+          const float m_new = grow ? mt : m[hb];
+          alpha[hb] = grow ? fast_exp2(m[hb] - m_new) : 1.0f;
+          any_grow = any_grow || grow;
+          m[hb] = m_new;
+          float psum = 0.f;
+          float p[2][4];
+  #pragma unroll
+          for (int h = 0; h < 2; ++h)
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              p[h][i] = fast_exp2(__builtin_fmaf(sv[h][i], a.qk_scale_log2, -m_new));
+              psum += p[h][i];
+            }
+          l[hb] = l[hb] * alpha[hb] + psum;
+          if constexpr (FP8) {
+  #pragma unroll
+            for (int h = 0; h < 2; ++h)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) p[h][i] *= vscur[h][i];
+          }
+          pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                         pack_bf16x2(p[1][2], p[1][3])};
+        }
+        if (__builtin_amdgcn_ballot_w64(any_grow)) {
+  #pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+  #pragma unroll
+            for (int n = 0; n < NT; ++n) o[hb][n] *= alpha[hb];
+        }
+        // ---- O^T += V^T P^T: one 16-wide d tile of V at a time, shared by all head blocks
+  #pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const int col = 16 * n + 4 * (r16 & 3);  // bf16 column
+          const int c = col >> 3, wsub = col & 7;
+          const int row_lo = 4 * q4 + (r16 >> 2);
+          const int row_hi = 16 + row_lo;
+          const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ (row_lo % CH)) << 4) + 2 * wsub);
+          const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ (row_hi % CH)) << 4) + 2 * wsub);
+          const u32x4 vf = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+  #pragma unroll
+          for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
+        }
       }
       tile = next_tile;
     }
@@ -501,21 +571,37 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     if (wave >= cur.ntile && has_next && wave < nxt.ntile) issue_loads(nxt, wave);
 
     // ---- merge the waves of the workgroup, write one partial per head
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      float lt = wave_sum_xor(l[hb], 16);
-      lt = wave_sum_xor(lt, 32);
-      l[hb] = lt;
-    }
     wave_lds_fence();
-    // O^T[d = 16n + 4q4 + i][head r16] -> ow[head][d] (float32), reusing the wave slab
+    if constexpr (M32) {
+      // O^T[d = 32n + 8(r/4) + 4h2 + r%4][head l32] -> ow[head][d]
+      const int l32 = lane & 31, h2 = lane >> 5;
+      l[0] = wave_sum_xor(l[0], 32);
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
+      for (int n = 0; n < NT32; ++n)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) lds_store(ow + (hb * 16 + r16) * D + 16 * n + 4 * q4, o[hb][n]);
-      if (q4 == 0) {
-        sm_ml[wave][hb * 16 + r16][0] = m[hb];
-        sm_ml[wave][hb * 16 + r16][1] = l[hb];
+        for (int rq = 0; rq < 4; ++rq)
+          lds_store(ow + l32 * D + 32 * n + 8 * rq + 4 * h2,
+                    f32x4{o32[n][4 * rq], o32[n][4 * rq + 1], o32[n][4 * rq + 2], o32[n][4 * rq + 3]});
+      if (h2 == 0) {
+        sm_ml[wave][l32][0] = m[0];
+        sm_ml[wave][l32][1] = l[0];
+      }
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float lt = wave_sum_xor(l[hb], 16);
+        lt = wave_sum_xor(lt, 32);
+        l[hb] = lt;
+      }
+      // O^T[d = 16n + 4q4 + i][head r16] -> ow[head][d] (float32), reusing the wave slab
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) lds_store(ow + (hb * 16 + r16) * D + 16 * n + 4 * q4, o[hb][n]);
+        if (q4 == 0) {
+          sm_ml[wave][hb * 16 + r16][0] = m[hb];
+          sm_ml[wave][hb * 16 + r16][1] = l[hb];
+        }
       }
     }
     __syncthreads();

@@ -43,6 +43,7 @@ struct PrefillArgs {
 };
 
 constexpr int kBN = 64;  // keys per tile
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr int kNumXcd = 8;
 
 template <int D, int HC>
@@ -160,38 +161,47 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
           sacc[kh] = mfma32(kf, qf[ks], sacc[kh]);
         }
       }
-      // ---- online softmax (row = this lane's query; keys split with lane^32)
+      // ---- online softmax (row = this lane's query; keys split with lane^32).
+      // The max is taken on the raw scores (scale > 0 keeps the order) and the
+      // scale folds into one FMA feeding exp2.  The reference max m (log2
+      // units) moves only when the tile max exceeds it by more than
+      // kRescaleSlack: O and l share the reference, so the result is the same,
+      // p stays <= 2^kRescaleSlack, and rescaling O is skipped on almost
+      // every tile.
       const bool diag = key0 + kBN - 1 > row0;
+      if (diag) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            sacc[kh][r] = key > qrow ? kNegInf : sacc[kh][r];
+          }
+      }
       float mt = kNegInf;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kh][r] * a.qk_scale_log2;
-          if (diag) {
-            const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            x = key > qrow ? kNegInf : x;
-          }
-          sacc[kh][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = wave_max_xor(mt, 32);
-      const float m_new = fmaxf(m, mt);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kh][r]);
+      mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
+      const bool grow = mt > m + kRescaleSlack;
+      const float m_new = grow ? mt : m;
+      const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
       m = m_new;
       float psum = 0.f;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[kh][r] - m_use);
+          const float p = fast_exp2(__builtin_fmaf(sacc[kh][r], a.qk_scale_log2, -m_new));
           sacc[kh][r] = p;
           psum += p;
         }
       l = l * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+        for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+      }
       // ---- O^T += V^T P^T, 4 k-steps of 16 keys
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
