@@ -54,8 +54,6 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
   constexpr int KS = D / 16;     // k-steps of the score product
   constexpr int NT = D / 32;     // 32-wide d tiles of the PV product
   constexpr int TILE_BYTES = kBN * D * 2;
-  constexpr int NLD = TILE_BYTES / (256 * 16);  // 16-byte loads per thread per tensor
-  constexpr int LROWS = 256 / CH;               // rows covered by one load instruction
   __shared__ __attribute__((aligned(16))) char sk[2][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv[2][TILE_BYTES];
 
@@ -101,33 +99,30 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
 
   const uint16_t* kbase = a.k + (size_t)b * S * kv_row_stride + (size_t)g * D;
   const uint16_t* vbase = a.v + (size_t)b * S * kv_row_stride + (size_t)g * D;
-  const int ld_row = tid / CH;
-  const int ld_chunk = tid % CH;
-
-  u32x4 kreg[NLD], vreg[NLD];
-  auto load_tile = [&](int j) {
+  // ---- K/V tiles go straight from global memory into LDS (no VGPR staging).
+  // One wave instruction fills 1 KiB of LDS at (wave-uniform base + lane*16),
+  // i.e. 64/CH consecutive tile rows; each lane picks the global 16-byte chunk
+  // that belongs at its LDS slot under the XOR chunk swizzle, so the 16 (or 8)
+  // lanes of a row still read one contiguous cache row.  Rows past the
+  // sequence end re-read its last row (in bounds); their keys are always
+  // masked for valid query rows, so they contribute nothing.
+  constexpr int RPI = 64 / CH;                  // tile rows per wave instruction
+  constexpr int NINS = kBN / (RPI * 4);         // instructions per wave per tensor
+  const int dma_r = lane / CH;                  // row within an instruction's rows
+  const int dma_c = (lane % CH);                // physical chunk of this lane's LDS slot
+  auto dma_tile = [&](int j, int buf) {
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int key = j * kBN + u * LROWS + ld_row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < S) {
-        const size_t off = (size_t)key * kv_row_stride + ld_chunk * 8;
-        kv = *reinterpret_cast<const u32x4*>(kbase + off);
-        vv = *reinterpret_cast<const u32x4*>(vbase + off);
-      }
-      kreg[u] = kv;
-      vreg[u] = vv;
+    for (int u = 0; u < NINS; ++u) {
+      const int r0 = (u * 4 + wave) * RPI;      // first tile row of this instruction
+      const int r = r0 + dma_r;
+      const int key = min(j * kBN + r, S - 1);
+      const int c = dma_c ^ (r % CH);           // logical chunk stored at this slot
+      const size_t off = (size_t)key * kv_row_stride + c * 8;
+      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sk[buf] + r0 * (2 * D)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sv[buf] + r0 * (2 * D)), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int r = u * LROWS + ld_row;
-      const int pc = ld_chunk ^ (r % CH);
-      lds_store(sk[buf] + r * (2 * D) + (pc << 4), kreg[u]);
-      lds_store(sv[buf] + r * (2 * D) + (pc << 4), vreg[u]);
-    }
-  };
+  auto dma_wait = [&]() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   f32x16 o[NT];
 #pragma unroll
@@ -136,13 +131,14 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
     for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  dma_tile(0, 0);
+  dma_wait();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    // the other buffer was last read in iteration j-1, before its closing barrier
+    if (j + 1 < n_tiles) dma_tile(j + 1, buf ^ 1);
     const int key0 = j * kBN;
     // this wave's rows all precede the tile: nothing to do but keep in step
     if (key0 <= wave_last_row) {
@@ -223,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
         }
       }
     }
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    dma_wait();
     __syncthreads();
   }
 
