@@ -1,18 +1,20 @@
 """Benchmark of the GQA attention library on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only-main]
-                    [--no-cpu-baseline] [--no-graph]
+                    [--no-cpu-baseline] [--graph]
 
 A step is one attn_decode call (split kernel + combine kernel) over the whole
 gqa_decode_ragged_bf16 workload (B=16, h_q=64, n_kv=8, d_h=128, ragged
-L_b in [1024, 4096]); with inputs resident in HBM the timed region replays a
-HIP graph of K such steps, bracketed by device synchronisations.  The KV cache
-is held in several copies that the steps rotate through, so the 256 MB
-Infinity Cache cannot serve one step's reads from the previous step.
+L_b in [1024, 4096]).  With inputs resident in HBM, K steps are
+launched back to back and timed by the host clock between two device
+synchronisations; HIP events recorded on the launch stream at the two ends of
+the same region give the device-side time.  The KV cache is held in several
+copies that the steps rotate through, so the 256 MB Infinity Cache cannot
+serve one step's reads from the previous step.
 
 value    = KV bytes per step / step time  (KV bytes = 2 * b * n_kv * d_h * sum L_b)
-roofline = the split kernel alone: KV bytes / its mean launch duration, timed
-           with HIP events recorded on the stream the kernel runs on, against
+roofline = the split kernel, which reads the cache: KV bytes / its mean launch
+           duration (event time of a region of K split launches / K), against
            the 8 TB/s HBM peak.
 Also reported (same JSON line, "workloads"): the other decode workloads and
 the causal prefill (TFLOP/s against the 2.5 PFLOP/s bf16 matrix peak), each
@@ -62,47 +64,43 @@ def measured_traffic(kernel_key):
     return ent.get("hbm_bytes_per_launch")
 
 
-def front_load():
-    # keep the GPU busy while the host enqueues the event-timed launches, so
-    # no host gap lands between an event and the kernel it brackets
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(20_000_000)
+def time_steps(step_fn, steps, warmup, use_graph=False):
+    """Run `warmup` untimed steps, then time exactly `steps` steps.
 
-
-def time_graph(step_fn, steps, warmup):
-    """Warm up eagerly, capture `steps` steps into one graph, replay it timed."""
+    Returns (ms per step by the host clock between two device
+    synchronisations, ms per step by HIP events recorded on the launch stream
+    at the two ends of the same region).  With use_graph the steps are
+    captured once into a HIP graph and the timed region is one replay."""
     for i in range(warmup):
         step_fn(i)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(steps):
-                step_fn(i)
-    torch.cuda.synchronize()
-    g.replay()  # untimed replay
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    step_fn(i)
+        torch.cuda.synchronize()
+        g.replay()  # untimed replay
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g.replay()
+    e0.record()
+    if use_graph:
+        g.replay()
+    else:
+        for i in range(steps):
+            step_fn(i)
+    e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
-def time_eager(step_fn, steps, warmup):
-    for i in range(warmup):
-        step_fn(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step_fn(i)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
-
-
-def bench_decode(wl, steps, warmup, use_graph=True, n_split=0):
+def bench_decode(wl, steps, warmup, use_graph=False, n_split=0):
     dev = torch.device("cuda")
     x = inputs.make_decode_inputs(wl, device=dev)
     lens = x.seq_lens.cpu().tolist()
@@ -122,37 +120,24 @@ def bench_decode(wl, steps, warmup, use_graph=True, n_split=0):
     ws = torch.empty(binding.attn_decode_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     out = torch.empty_like(x.q)
 
-    def partials(i):
-        c = i % ncopies
-        binding.attn_decode_partials(x.q, ks[c], vs[c], x.seq_lens, wl.scale, ws, k_scale=kss[c], v_scale=vss[c],
-                                     n_split=n_split_req)
-
-    def combine(i):
-        binding.attn_decode_combine(x.q, x.k, x.seq_lens, ws, out, n_split=n_split_req)
+    # arguments checked and packed once per cache copy: a step is one ctypes call
+    calls = [binding.prepare_decode(x.q, ks[c], vs[c], x.seq_lens, wl.scale, out, ws, k_scale=kss[c],
+                                    v_scale=vss[c], n_split=n_split_req) for c in range(ncopies)]
+    part_calls = [binding.prepare_decode_partials(x.q, ks[c], vs[c], x.seq_lens, wl.scale, ws, k_scale=kss[c],
+                                                  v_scale=vss[c], n_split=n_split_req) for c in range(ncopies)]
 
     def step(i):
-        partials(i)
-        combine(i)
+        calls[i % ncopies]()
 
-    ms_step = time_graph(step, steps, warmup) if use_graph else time_eager(step, steps, warmup)
+    def partials(i):
+        part_calls[i % ncopies]()
 
-    # per-kernel durations: HIP events on the launch stream around each kernel
-    n_ev = min(steps, 100)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-    torch.cuda.synchronize()
-    front_load()
-    for i in range(n_ev):
-        ev[i][0].record()
-        partials(i)
-        ev[i][1].record()
-        combine(i)
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / n_ev
-    comb_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / n_ev
+    ms_step, ev_ms = time_steps(step, steps, warmup, use_graph)
+    # the split kernel (the one that reads the cache) over a region of its own
+    _, kernel_ms = time_steps(partials, steps, 2, use_graph)
 
     key = f"decode_split_{wl.kv_dtype}:{wl.name}"
-    achieved = kv_bytes / (split_ms * 1e-3) / 1e9
+    achieved = kv_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(key)
     return {
         "workload": wl.name,
@@ -165,10 +150,12 @@ def bench_decode(wl, steps, warmup, use_graph=True, n_split=0):
         "sum_L": int(sum(lens)),
         "n_split": n_split,
         "kv_copies_rotated": ncopies,
-        "split_kernel_ms": split_ms,
-        "combine_kernel_ms": comb_ms,
+        "event_ms_per_step": ev_ms,
+        "split_kernel_ms": kernel_ms,
+        "combine_ms_approx": ev_ms - kernel_ms,
         "roofline": {"bound": "hbm", "kernel": "gqa_decode_split_mfma" if wl.kv_dtype != "f32"
-                     else "gqa_decode_split_f32", "achieved": achieved, "peak": roofline.HBM_PEAK_GBPS,
+                     else "gqa_decode_split_f32",
+                     "achieved": achieved, "peak": roofline.HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / roofline.HBM_PEAK_GBPS, "traffic": traffic},
         "dtype": wl.kv_dtype,
         "config": {"workload": wl.name, "B": wl.B, "h_q": wl.h_q, "n_kv": wl.n_kv, "d_h": wl.d_h,
@@ -176,26 +163,18 @@ def bench_decode(wl, steps, warmup, use_graph=True, n_split=0):
     }
 
 
-def bench_prefill(wl, steps, warmup, use_graph=True):
+def bench_prefill(wl, steps, warmup, use_graph=False):
     dev = torch.device("cuda")
     x = inputs.make_prefill_inputs(wl, device=dev)
     out = torch.empty_like(x.q)
     flops = roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h)
 
-    def step(i):
-        binding.attn_prefill_causal(x.q, x.k, x.v, wl.scale, out=out)
+    call = binding.prepare_prefill_causal(x.q, x.k, x.v, wl.scale, out)
 
-    ms_step = time_graph(step, steps, warmup) if use_graph else time_eager(step, steps, warmup)
-    n_ev = min(steps, 50)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
-    torch.cuda.synchronize()
-    front_load()
-    for i in range(n_ev):
-        ev[i][0].record()
-        step(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    k_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / n_ev
+    def step(i):
+        call()
+
+    ms_step, k_ms = time_steps(step, steps, warmup, use_graph)  # one launch per step
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = roofline.MFMA_PEAK_TFLOPS["bf16"]
     return {
@@ -261,53 +240,69 @@ def cpu_baseline(wl, budget_s=12.0):
 # rocprofv3 output -> profiles/
 # ----------------------------------------------------------------------------
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -T -d <out>/prof_trace -o run --output-format csv -- "
+    "trace": "rocprofv3 --kernel-trace --stats -d <out>/prof_trace -o run --output-format csv -- "
              "python3 bench.py --steps 20 --warmup 2 --no-cpu-baseline",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace -T -d <out>/prof_fetch -o run --output-format csv -- "
-             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-graph --copy-calibration",
-    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace -T -d <out>/prof_write -o run --output-format csv -- "
-             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-graph --copy-calibration",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-trace -d <out>/prof_fetch -o run --output-format csv -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration",
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <out>/prof_write -o run --output-format csv -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration",
 }
 CALIB_GRID = (1 << 30) // 16  # threads of the calibration kernel (4 floats per thread)
 
 
+def kernel_identity(name):
+    """'void gqa::k<128, 1, false, 8>(gqa::Args)' -> ('k', ('128', '1', 'false', '8'))."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    name = name.split("(")[0]
+    base, _, targs = name.partition("<")
+    targs = tuple(t.strip() for t in targs.rstrip(">").split(",")) if targs else ()
+    return base.split("::")[-1].strip(), targs
+
+
 def _workload_launches():
-    """(kernel-name prefix, grid threads) -> (counter key, workload, algorithmic bytes or flops)."""
+    """(kernel, template args, grid threads) -> (counter key, workload, algorithmic bytes or flops, unit).
+
+    Mirrors the library's launch plan: the decode split kernel runs W
+    workgroups of 512 threads (matrix-core paths) or 256 (float32 path); the
+    combine kernel a grid of (slabs, ceil(heads_per_chunk * d / 4 / 256))
+    workgroups of 256."""
     out = {}
     for wl in inputs.DECODE_WORKLOADS.values():
         qd = torch.empty((wl.B, wl.h_q, wl.d_h), dtype={"f32": torch.float32, "bf16": torch.bfloat16}[wl.q_dtype],
                          device="meta")
         kd = torch.empty((wl.B, wl.n_kv, wl.S_max, wl.d_h), device="meta",
                          dtype={"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.kv_dtype])
-        desc = binding.decode_desc(qd, kd)
-        ns = binding.attn_decode_num_splits(desc)
+        ns = binding.attn_decode_num_splits(binding.decode_desc(qd, kd))
         G = wl.h_q // wl.n_kv
-        hpc = 16 if (wl.kv_dtype == "f32" or G <= 16) else 32
-        nh = -(-G // hpc)
-        grid = ns * wl.n_kv * nh * wl.B * 256
         lens = inputs.draw_lengths(wl.B, *wl.lens, wl.seed).tolist()
-        kernel = "gqa_decode_split_f32" if wl.kv_dtype == "f32" else "gqa_decode_split_mfma"
-        out[(kernel, grid)] = (f"decode_split_{wl.kv_dtype}:{wl.name}", wl.name,
-                               roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens), "bytes")
-        out[("gqa_decode_combine", ((wl.B * wl.h_q + 3) // 4) * 256)] = (f"decode_combine:{wl.name}", wl.name, None,
-                                                                        None)
+        kv = roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens)
+        key = f"decode_split_{wl.kv_dtype}:{wl.name}"
+        hpc = 16 if (wl.kv_dtype == "f32" or G <= 16) else 32
+        if wl.kv_dtype == "f32":
+            out[("gqa_decode_split_f32", (str(wl.d_h),), ns * 256)] = (key, wl.name, kv, "bytes")
+        else:
+            targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8")
+            out[("gqa_decode_split_mfma", targs, ns * 512)] = (key, wl.name, kv, "bytes")
+        n_slabs = wl.B * wl.n_kv * -(-G // hpc)
+        grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
+        targs = (str(wl.d_h), "false" if wl.q_dtype == "f32" else "true")
+        out[("gqa_decode_combine", targs, grid)] = (f"decode_combine:{wl.name}", wl.name, None, None)
     for wl in inputs.PREFILL_WORKLOADS.values():
         G = wl.h_q // wl.n_kv
         hc = math.gcd(G, 4)
         bm = 32 * (4 // hc)
         n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S // bm))
         grid = -(-n_wg // 8) * 8 * 256
-        out[("gqa_prefill_causal_kernel", grid)] = (f"prefill_causal:{wl.name}", wl.name,
-                                                    roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h), "flops")
+        out[("gqa_prefill_causal_kernel", (str(wl.d_h), str(hc)), grid)] = (
+            f"prefill_causal:{wl.name}", wl.name, roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h), "flops")
     return out
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
     import csv
     import statistics
-
-    def base(name):
-        return name.split("(")[0].split("<")[0].replace("void ", "").split("::")[-1].strip()
 
     def rows(d, suffix):
         for f in os.listdir(d):
@@ -318,16 +313,16 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
     launches = _workload_launches()
     dur = {}
     for r in rows(trace_dir, "kernel_trace.csv"):
-        key = (base(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        key = (*kernel_identity(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
         if key in launches:
             dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     counters = {}
     for kind, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         calib = []
         for r in rows(d, "counter_collection.csv"):
-            key = (base(r["Kernel_Name"]), int(r["Grid_Size"]))
+            key = (*kernel_identity(r["Kernel_Name"]), int(r["Grid_Size"]))
             v = float(r["Counter_Value"])
-            if key[0] == "vectorized_elementwise_kernel" and key[1] == CALIB_GRID and v > 1024:
+            if key[0] == "vectorized_elementwise_kernel" and key[2] == CALIB_GRID and v > 1024:
                 calib.append(v)
             elif key in launches:
                 counters.setdefault((kind, key), []).append(v)
@@ -344,7 +339,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
         write = counters.get(("WRITE_SIZE", key))
         fb = statistics.median(fetch) * 1024 * summary["fetch_scale"] if fetch else None
         wb = statistics.median(write) * 1024 * summary["write_scale"] if write else None
-        ent = {"kernel": key[0], "workload": wname, "grid_threads": key[1], "launches": len(d),
+        ent = {"kernel": key[0], "template_args": list(key[1]), "workload": wname, "grid_threads": key[2],
+               "launches": len(d),
                "mean_us": statistics.mean(d), "median_us": statistics.median(d), "min_us": d[0], "max_us": d[-1],
                "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
                "hbm_bytes_per_launch": (fb + wb) if fb is not None and wb is not None else None,
@@ -360,7 +356,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
         summary["kernels"][ckey] = ent
         fname = os.path.join(dest, f"{key[0]}__{wname}.txt")
         with open(fname, "w") as f:
-            f.write(f"kernel: {key[0]}   workload: {wname}   grid threads: {key[1]}\n")
+            f.write(f"kernel: {key[0]}<{', '.join(key[1])}>   workload: {wname}   grid threads: {key[2]}\n")
             f.write("commands (run from the repository root on one MI355X; <out> = output directory):\n")
             for k in ("trace", "fetch", "write"):
                 f.write(f"  {PROFILE_COMMANDS[k]}\n")
@@ -397,7 +393,8 @@ def main(argv=None):
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--graph", action="store_true", help="time one HIP-graph replay of the K steps instead of "
+                    "K eager launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -418,7 +415,7 @@ def main(argv=None):
         return 2
     binding.load_library()
     props = torch.cuda.get_device_properties(0)
-    use_graph = not args.no_graph
+    use_graph = args.graph
     if args.copy_calibration:
         print(f"[bench] copy calibration {copy_calibration()}", file=sys.stderr, flush=True)
 
@@ -452,7 +449,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": main_res["config"],
         "roofline": main_res["roofline"],
-        "timing": "hip-graph replay of K steps" if use_graph else "eager launches",
+        "timing": "one hip-graph replay of K steps" if use_graph else "K eager launches",
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
         "main": {k: v for k, v in main_res.items() if k not in ("config", "roofline")},

@@ -119,8 +119,8 @@ size_t attn_decode_workspace_bytes(const gqa_decode_desc* d);
 
 /* Full decode step: split kernel then combine kernel, both on `stream`.
  * workspace: caller-owned device memory of at least
- * attn_decode_workspace_bytes(d) bytes; it must stay untouched until the
- * stream reaches the end of this call's work. */
+ * attn_decode_workspace_bytes(d) bytes (any contents); it must stay untouched
+ * until the stream reaches the end of this call's work. */
 gqa_status attn_decode(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
                        const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -135,6 +135,53 @@ def test_partials_then_combine_equals_decode():
     assert torch.equal(out, full)
 
 
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_workspace_reused_across_calls(kd):
+    """One workspace, filled with NaN bit patterns once, serves calls with
+    different lengths and split counts; every result matches the oracle."""
+    w = wl("reuse", B=6, h_q=32, n_kv=4, d=128, S=900, qd="bf16", kd=kd, seed=61)
+    base = inputs.make_decode_inputs(w, device=DEV)
+    cases = [([900, 1, 450, 0, 33, 899], 0), ([5, 5, 5, 5, 5, 5], 0), ([900] * 6, 3), ([1, 64, 2, 0, 700, 31], 10 ** 6),
+             ([0] * 6, 0), ([321, 654, 87, 900, 12, 1], 17)]
+    need = max(binding.attn_decode_workspace_bytes(binding.decode_desc(base.q, base.k, ns)) for _, ns in cases)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    for lens, ns in cases:
+        inp = inputs.make_decode_inputs(w, device=DEV, seq_lens=lens, poison_tail=True)
+        print(f"[decode-reuse] {kd} lens={lens} n_split={ns}", flush=True)
+        out = torch.full_like(inp.q, float("nan"))
+        pu.run_decode(inp, n_split=ns, out=out, workspace=ws)
+        pu.sync()
+        err = pu.max_err(out, pu.oracle_decode_full(inp))
+        assert err <= pu.TOL[kd], f"lens={lens} n_split={ns}: max abs err {err}"
+
+
+def test_all_sequences_empty_gives_zero_rows():
+    w = wl("allempty", B=3, h_q=16, n_kv=2, d=64, S=128, qd="bf16", kd="bf16", seed=67)
+    inp = inputs.make_decode_inputs(w, device=DEV, seq_lens=[0, 0, 0])
+    out = torch.full_like(inp.q, float("nan"))
+    pu.run_decode(inp, out=out)
+    pu.sync()
+    assert torch.count_nonzero(out) == 0
+
+
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+def test_prepared_call_matches_plain_call(kd):
+    qd = "f32" if kd == "f32" else "bf16"
+    w = wl("prep", B=3, h_q=16, n_kv=2, d=128, S=300, qd=qd, kd=kd, seed=71)
+    inp = inputs.make_decode_inputs(w, device=DEV, seq_lens=[300, 2, 150])
+    ref = pu.run_decode(inp)
+    desc = binding.decode_desc(inp.q, inp.k)
+    ws = torch.empty(binding.attn_decode_workspace_bytes(desc), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(inp.q)
+    call = binding.prepare_decode(inp.q, inp.k, inp.v, inp.seq_lens, w.scale, out, ws, k_scale=inp.k_scale,
+                                  v_scale=inp.v_scale)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        assert call() is out
+        pu.sync()
+        assert torch.equal(out, ref)
+
+
 def test_runs_on_a_side_stream():
     w = wl("stream", B=2, h_q=16, n_kv=2, d=128, S=512, qd="bf16", kd="bf16", seed=59)
     inp = inputs.make_decode_inputs(w, device=DEV)

@@ -79,6 +79,19 @@ def test_prefill_deterministic():
     assert torch.equal(a, b)
 
 
+def test_prefill_prepared_call_matches_plain_call():
+    w = pwl(1, 300, 8, 2, 128, seed=13)
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    ref = run(inp)
+    out = torch.empty_like(inp.q)
+    call = binding.prepare_prefill_causal(inp.q, inp.k, inp.v, w.scale, out)
+    for _ in range(2):
+        out.fill_(float("nan"))
+        call()
+        pu.sync()
+        assert torch.equal(out, ref)
+
+
 def test_prefill_decode_consistency():
     # decode over the first L tokens (cache layout) equals prefill row L-1
     S, h_q, n_kv, d = 300, 16, 4, 128

@@ -160,6 +160,58 @@ def attn_decode(q, k_cache, v_cache, seq_lens, scale, out=None, k_scale=None, v_
     return out
 
 
+class PreparedCall:
+    """A library call with its arguments checked and packed once.
+
+    Calling it passes the same pointers again (one ctypes call, no per-call
+    checks), so the tensors it was built from must stay alive and keep their
+    storage.  The stream is the one given at preparation, or else torch's
+    current stream at each call."""
+
+    def __init__(self, fn, args, stream, result=None):
+        self._fn = fn
+        self._args = args
+        self._stream = None if stream is None else _stream(stream)
+        self.result = result
+
+    def __call__(self):
+        st = self._stream if self._stream is not None else ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        _check(self._fn(*self._args, st))
+        return self.result
+
+
+def prepare_decode(q, k_cache, v_cache, seq_lens, scale, out, workspace, k_scale=None, v_scale=None, n_split=0,
+                   stream=None):
+    """PreparedCall of attn_decode (see attn_decode for the arguments)."""
+    _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
+    desc = decode_desc(q, k_cache, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < attn_decode_workspace_bytes(desc):
+        raise ValueError("workspace smaller than attn_decode_workspace_bytes")
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace), ctypes.c_size_t(ws_bytes))
+    call = PreparedCall(lib.attn_decode, args, stream, out)
+    call._keep = (desc,)
+    return call
+
+
+def prepare_decode_partials(q, k_cache, v_cache, seq_lens, scale, workspace, k_scale=None, v_scale=None, n_split=0,
+                            stream=None):
+    """PreparedCall of attn_decode_partials."""
+    _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
+    desc = decode_desc(q, k_cache, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
+            ctypes.c_float(scale), _ptr(workspace), ctypes.c_size_t(ws_bytes))
+    call = PreparedCall(lib.attn_decode_partials, args, stream)
+    call._keep = (desc,)
+    return call
+
+
 def attn_decode_partials(q, k_cache, v_cache, seq_lens, scale, workspace, k_scale=None, v_scale=None, n_split=0,
                          stream=None):
     """Split kernel only: per-chunk partials into `workspace`."""
@@ -180,16 +232,32 @@ def attn_decode_combine(q, k_cache, seq_lens, workspace, out, n_split=0, stream=
     return out
 
 
-def attn_prefill_causal(q, k, v, scale, out=None, stream=None):
-    """out[B, S, h_q, d] = causal GQA attention over q [B,S,h_q,d], k/v [B,S,n_kv,d] (bf16)."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
+def _prefill_desc(q, k, v, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _require(t, name, 4)
     B, S, h_q, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[1] != S or k.shape[3] != d:
         raise ValueError("k/v must be [B, S, n_kv, d] matching q [B, S, h_q, d]")
-    desc = gqa_prefill_desc(B, S, h_q, k.shape[2], d, _dtype_code(q))
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be shaped and typed like q")
+    return gqa_prefill_desc(B, S, h_q, k.shape[2], d, _dtype_code(q))
+
+
+def attn_prefill_causal(q, k, v, scale, out=None, stream=None):
+    """out[B, S, h_q, d] = causal GQA attention over q [B,S,h_q,d], k/v [B,S,n_kv,d] (bf16)."""
     if out is None:
         out = torch.empty_like(q)
+    desc = _prefill_desc(q, k, v, out)
     _check(load_library().attn_prefill_causal(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(scale),
                                               _ptr(out), _stream(stream)))
     return out
+
+
+def prepare_prefill_causal(q, k, v, scale, out, stream=None):
+    """PreparedCall of attn_prefill_causal."""
+    desc = _prefill_desc(q, k, v, out)
+    lib = load_library()
+    call = PreparedCall(lib.attn_prefill_causal, (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                                  ctypes.c_float(scale), _ptr(out)), stream, out)
+    call._keep = (desc,)
+    return call

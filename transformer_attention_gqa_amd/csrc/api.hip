@@ -85,12 +85,20 @@ DecodePlan plan_decode(const gqa_decode_desc* d) {
   return p;
 }
 
-size_t workspace_layout(const gqa_decode_desc* d, const DecodePlan& p, size_t* ml_offset) {
+// Workspace: [partial O][partial (m, l)], the second part starting on a
+// 256-byte boundary.
+struct WorkspaceLayout {
+  size_t o_off, ml_off, total;
+};
+
+WorkspaceLayout workspace_layout(const gqa_decode_desc* d, const DecodePlan& p) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)(p.W + p.n_slabs) * p.heads_per_chunk;
-  const size_t o_bytes = rows * d->d_h * sizeof(float);
-  const size_t ml_off = (o_bytes + 255) & ~(size_t)255;
-  if (ml_offset) *ml_offset = ml_off;
-  return ml_off + rows * 2 * sizeof(float);
+  WorkspaceLayout l;
+  l.o_off = 0;
+  l.ml_off = up(rows * d->d_h * sizeof(float));
+  l.total = l.ml_off + rows * 2 * sizeof(float);
+  return l;
 }
 
 gqa_status check_decode_ptrs(const gqa_decode_desc* d, const void* q, const void* k, const void* v,
@@ -106,8 +114,7 @@ gqa_status check_decode_ptrs(const gqa_decode_desc* d, const void* q, const void
 gqa_status do_partials(const gqa_decode_desc* d, const DecodePlan& p, const void* q, const void* k, const void* v,
                        const float* ks, const float* vs, const int32_t* seq_lens, float scale, void* ws,
                        hipStream_t stream) {
-  size_t ml_off = 0;
-  workspace_layout(d, p, &ml_off);
+  const WorkspaceLayout wl = workspace_layout(d, p);
   DecodeArgs a;
   a.q = q;
   a.k = k;
@@ -115,8 +122,8 @@ gqa_status do_partials(const gqa_decode_desc* d, const DecodePlan& p, const void
   a.k_scale = ks;
   a.v_scale = vs;
   a.seq_lens = seq_lens;
-  a.part_o = static_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
   a.qk_scale_log2 = (float)((double)scale * kLog2e);
   a.B = d->B;
   a.h_q = d->h_q;
@@ -134,11 +141,10 @@ gqa_status do_partials(const gqa_decode_desc* d, const DecodePlan& p, const void
 
 gqa_status do_combine(const gqa_decode_desc* d, const DecodePlan& p, const int32_t* seq_lens, const void* ws,
                       void* out, hipStream_t stream) {
-  size_t ml_off = 0;
-  workspace_layout(d, p, &ml_off);
+  const WorkspaceLayout wl = workspace_layout(d, p);
   CombineArgs c;
-  c.part_o = static_cast<const float*>(ws);
-  c.part_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ml_off);
+  c.part_o = reinterpret_cast<const float*>(static_cast<const char*>(ws) + wl.o_off);
+  c.part_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + wl.ml_off);
   c.seq_lens = seq_lens;
   c.out = out;
   c.B = d->B;
@@ -171,7 +177,7 @@ int32_t attn_decode_num_splits(const gqa_decode_desc* d) {
 
 size_t attn_decode_workspace_bytes(const gqa_decode_desc* d) {
   if (validate_decode_desc(d) != GQA_OK) return 0;
-  return workspace_layout(d, plan_decode(d), nullptr);
+  return workspace_layout(d, plan_decode(d)).total;
 }
 
 gqa_status attn_decode_partials(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
@@ -183,7 +189,7 @@ gqa_status attn_decode_partials(const gqa_decode_desc* d, const void* q, const v
   if (st != GQA_OK) return st;
   if (bad_scale(scale)) return GQA_ERR_VALUE;
   const DecodePlan p = plan_decode(d);
-  if (!workspace || workspace_bytes < workspace_layout(d, p, nullptr)) return GQA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < workspace_layout(d, p).total) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
   return do_partials(d, p, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, workspace, stream);
 }
@@ -196,7 +202,7 @@ gqa_status attn_decode_combine(const gqa_decode_desc* d, const int32_t* seq_lens
   if (misaligned(out)) return GQA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0) return GQA_ERR_ALIGN;
   const DecodePlan p = plan_decode(d);
-  if (!workspace || workspace_bytes < workspace_layout(d, p, nullptr)) return GQA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < workspace_layout(d, p).total) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
   return do_combine(d, p, seq_lens, workspace, out, stream);
 }
@@ -212,7 +218,7 @@ gqa_status attn_decode(const gqa_decode_desc* d, const void* q, const void* k_ca
   if (misaligned(out)) return GQA_ERR_ALIGN;
   if (bad_scale(scale)) return GQA_ERR_VALUE;
   const DecodePlan p = plan_decode(d);
-  if (!workspace || workspace_bytes < workspace_layout(d, p, nullptr)) return GQA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < workspace_layout(d, p).total) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
   st = do_partials(d, p, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, workspace, stream);
   if (st != GQA_OK) return st;

@@ -791,13 +791,72 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------
-// Combine: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the
-// partials of one slab.  One workgroup per slab (sequence, kv-head, head
-// chunk); each thread owns 4 consecutive output columns of one head.
+// Combine: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s, over the partials of one slab.
 // ------------------------------------------------------------------------
+// The partials of the slab whose tiles are [first, first + nt) of the global
+// range [0, T) cut into W workgroup ranges: one per workgroup whose range
+// touches the slab.  When T >= W every range is non-empty, so these are the
+// workgroups from the owner of the slab's first tile to the owner of its last;
+// when T < W a range holds at most one tile and the owners go tile by tile.
+struct SlabPieces {
+  long long first, T, W, wa, sigma;
+  int nt, n;
+  __device__ __forceinline__ SlabPieces(long long sigma_, long long first_, int nt_, long long T_, long long W_)
+      : first(first_), T(T_), W(W_), wa(((first_ + 1) * W_ - 1) / T_), sigma(sigma_), nt(nt_) {
+    n = T >= W ? (int)(((first + nt) * W - 1) / T - wa + 1) : nt;
+  }
+  __device__ __forceinline__ long long slot(int p) const {
+    return (T >= W ? wa + p : ((first + p + 1) * W - 1) / T) + sigma;
+  }
+};
+
+// Merges the partials of one slab into its nh output rows (heads head0 ..
+// head0 + nh - 1 of sequence b).  Thread tid of nthreads takes the elements
+// tid, tid + nthreads, ... of the nh x D/4 grid of 4-column groups; each
+// element folds the pieces in one pass with a running maximum.
+template <int D, bool OUT_BF16>
+__device__ __forceinline__ void merge_slab(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                           void* __restrict__ out, int hpc, int h_q, int b, int head0, int nh,
+                                           const SlabPieces& sp, int tid, int nthreads) {
+  constexpr int D4 = D / 4;
+  for (int e = tid; e < nh * D4; e += nthreads) {
+    const int hl = e / D4, d4 = e - hl * D4;
+    float M = kNegInf, denom = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int p = 0; p < sp.n; ++p) {
+      const size_t row = (size_t)sp.slot(p) * hpc + hl;
+      const float ms = part_ml[row * 2], ls = part_ml[row * 2 + 1];
+      const f32x4 os = *reinterpret_cast<const f32x4*>(part_o + row * D + 4 * d4);
+      if (ms == kNegInf) continue;  // a piece that saw no visible key
+      if (ms > M) {
+        const float r = M == kNegInf ? 0.f : fast_exp2(M - ms);
+        acc *= r;
+        denom *= r;
+        M = ms;
+      }
+      const float f = fast_exp2(ms - M);
+      acc += f * os;
+      denom += f * ls;
+    }
+    acc *= denom > 0.f ? 1.0f / denom : 0.f;
+    const size_t idx = ((size_t)b * h_q + head0 + hl) * D + 4 * d4;
+    if constexpr (OUT_BF16) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(acc[0], acc[1]);
+      wv[1] = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx) = wv;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = acc;
+    }
+  }
+}
+
+// One workgroup per (slab, chunk of 256 elements): each thread merges one
+// 4-column group of one head, so every partial row is read by a single load.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void gqa_decode_combine(CombineArgs c) {
-  constexpr int D4 = D / 4;
   const int sigma = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int spb = c.n_kv * c.n_hchunk;
@@ -806,57 +865,21 @@ __global__ __launch_bounds__(256) void gqa_decode_combine(CombineArgs c) {
   const int g = slab_in_b / c.n_hchunk;
   const int hc = slab_in_b - g * c.n_hchunk;
   const int G = c.h_q / c.n_kv;
-  const int hpc = c.heads_per_chunk;
-  const int hloc0 = hc * hpc;
-  const int nh = min(hpc, G - hloc0);
-  const int head0 = g * G + hloc0;
+  const int hloc0 = hc * c.heads_per_chunk;
+  const int nh = min(c.heads_per_chunk, G - hloc0);
   const int nt = seq_tiles(c.seq_lens, b, c.S_max, c.tile);
-
-  // The slab's partials: one per workgroup whose range touches the slab.  When
-  // T >= W every range is non-empty, so these are exactly the workgroups from
-  // the owner of the slab's first tile to the owner of its last; when T < W a
-  // range holds at most one tile and the owners are enumerated tile by tile.
-  long long first = 0, wa = 0, T = 1;
-  int n_pieces = 0;
-  bool per_tile = false;
-  if (nt > 0) {
-    T = tiles_before(c.seq_lens, c.B, c.S_max, c.tile, spb, lane);
-    first = tiles_before(c.seq_lens, b, c.S_max, c.tile, spb, lane) + (long long)slab_in_b * nt;
-    const long long W = c.W;
-    wa = ((first + 1) * W - 1) / T;
-    per_tile = T < W;
-    n_pieces = per_tile ? nt : (int)(((first + nt) * W - 1) / T - wa + 1);
+  const int tid = blockIdx.y * 256 + threadIdx.x;
+  if (nt == 0) {  // empty sequence: zero rows
+    const SlabPieces none(sigma, 0, 0, 1, 1);
+    merge_slab<D, OUT_BF16>(c.part_o, c.part_ml, c.out, c.heads_per_chunk, c.h_q, b, g * G + hloc0, nh,
+                                   none, tid, gridDim.y * 256);
+    return;
   }
-  auto piece_slot = [&](int p) -> long long {
-    const long long w = per_tile ? ((first + p + 1) * (long long)c.W - 1) / T : wa + p;
-    return w + sigma;
-  };
-  for (int e = threadIdx.x; e < nh * D4; e += 256) {
-    const int hl = e / D4, d4 = e - hl * D4;
-    float M = kNegInf;
-    for (int p = 0; p < n_pieces; ++p) M = fmaxf(M, c.part_ml[(piece_slot(p) * hpc + hl) * 2]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float denom = 0.f;
-#pragma unroll 4
-    for (int p = 0; p < n_pieces; ++p) {
-      const size_t row = (size_t)piece_slot(p) * hpc + hl;
-      const float ms = c.part_ml[row * 2];
-      const float f = ms == kNegInf ? 0.f : fast_exp2(ms - M);
-      denom += f * c.part_ml[row * 2 + 1];
-      acc += f * *reinterpret_cast<const f32x4*>(c.part_o + row * D + 4 * d4);
-    }
-    const float inv = denom > 0.f ? 1.0f / denom : 0.f;
-    acc *= inv;
-    const size_t idx = ((size_t)b * c.h_q + head0 + hl) * D + 4 * d4;
-    if constexpr (OUT_BF16) {
-      u32x2 wv;
-      wv[0] = pack_bf16x2(acc[0], acc[1]);
-      wv[1] = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c.out) + idx) = wv;
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(c.out) + idx) = acc;
-    }
-  }
+  const long long T = tiles_before(c.seq_lens, c.B, c.S_max, c.tile, spb, lane);
+  const long long first = tiles_before(c.seq_lens, b, c.S_max, c.tile, spb, lane) + (long long)slab_in_b * nt;
+  const SlabPieces sp(sigma, first, nt, T, c.W);
+  merge_slab<D, OUT_BF16>(c.part_o, c.part_ml, c.out, c.heads_per_chunk, c.h_q, b, g * G + hloc0, nh, sp,
+                                 tid, gridDim.y * 256);
 }
 
 // ------------------------------------------------------------------------
@@ -888,7 +911,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int
 }
 
 hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream) {
-  const dim3 grid(c.B * c.n_kv * c.n_hchunk);
+  const dim3 grid(c.B * c.n_kv * c.n_hchunk, (c.heads_per_chunk * D / 4 + 255) / 256);
   const dim3 block(256);
   if (D == 64) {
     if (out_bf16) hipLaunchKernelGGL((gqa_decode_combine<64, true>), grid, block, 0, stream, c);
