@@ -291,10 +291,10 @@ def _workload_launches():
         out[("gqa_decode_combine", targs, grid)] = (f"decode_combine:{wl.name}", wl.name, None, None)
     for wl in inputs.PREFILL_WORKLOADS.values():
         G = wl.h_q // wl.n_kv
-        hc = math.gcd(G, 4)
-        bm = 32 * (4 // hc)
+        hc = math.gcd(G, 8)
+        bm = 32 * (8 // hc)
         n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S // bm))
-        grid = -(-n_wg // 8) * 8 * 256
+        grid = -(-n_wg // 8) * 8 * 512
         out[("gqa_prefill_causal_kernel", (str(wl.d_h), str(hc)), grid)] = (
             f"prefill_causal:{wl.name}", wl.name, roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h), "flops")
     return out

@@ -706,6 +706,7 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
       for (int h = 0; h < HPC; ++h) sc[h] = 0.f;
       if (valid) {
         const float4* kr = reinterpret_cast<const float4*>(kg + (slab + tok) * D);
+#pragma unroll 8
         for (int d4 = 0; d4 < D / 4; ++d4) {
           const float4 kv = kr[d4];
 #pragma unroll
@@ -739,16 +740,26 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
       for (int h = 0; h < HPC; ++h)
 #pragma unroll
         for (int c = 0; c < DL; ++c) o[h][c] *= alpha[h];
-      for (int tt = 0; tt < nvalid; ++tt) {
-        const float* vr = vg + (slab + tt0 + tt) * D;
-        float vv[DL];
+      // V rows U at a time: all U loads are issued before the first use;
+      // rows past the last valid one are re-reads of it and are skipped
+      constexpr int U = 8;
+      for (int tt = 0; tt < nvalid; tt += U) {
+        float vv[U][DL];
 #pragma unroll
-        for (int c = 0; c < DL; ++c) vv[c] = vr[lane + 64 * c];
+        for (int u = 0; u < U; ++u) {
+          const float* vr = vg + (slab + tt0 + min(tt + u, nvalid - 1)) * D;
 #pragma unroll
-        for (int h = 0; h < HPC; ++h) {
-          const float p = sp[wave][tt][h];
+          for (int c = 0; c < DL; ++c) vv[u][c] = vr[lane + 64 * c];
+        }
 #pragma unroll
-          for (int c = 0; c < DL; ++c) o[h][c] = fmaf(p, vv[c], o[h][c]);
+        for (int u = 0; u < U; ++u) {
+          if (tt + u >= nvalid) break;
+#pragma unroll
+          for (int h = 0; h < HPC; ++h) {
+            const float p = sp[wave][tt + u][h];
+#pragma unroll
+            for (int c = 0; c < DL; ++c) o[h][c] = fmaf(p, vv[u][c], o[h][c]);
+          }
         }
       }
       wave_lds_fence();

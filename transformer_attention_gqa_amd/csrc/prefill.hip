@@ -10,9 +10,11 @@
 // tiled computation, softmax on chip, only the final O written back).
 //
 // Work decomposition (MI355X-specific, not the pages' GPU):
-//  * a workgroup of 4 wavefronts serves HC query heads of ONE K/V group over
-//    32*(4/HC) query rows, so every K/V tile it stages in LDS feeds 4 waves
-//    (GQA: the G heads of a group read the same K/V);
+//  * a workgroup of 8 wavefronts (one workgroup per compute unit) serves HC
+//    query heads of ONE K/V group over 32*(8/HC) query rows, so every K/V
+//    tile it stages in LDS feeds 8 waves (GQA: the G heads of a group read the
+//    same K/V), which halves the global->LDS traffic per flop against
+//    4-wave workgroups at the same register occupancy;
 //  * each wave owns 32 query rows of one head: S^T[key][query] = K Q^T and
 //    O^T[d][query] += V^T P^T on v_mfma_f32_32x32x16_bf16.  The key order in
 //    the PV product is permuted so the score accumulator registers are the B
@@ -45,17 +47,36 @@ struct PrefillArgs {
 constexpr int kBN = 64;  // keys per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr int kNumXcd = 8;
+constexpr int kWaves = 8;  // wavefronts per workgroup
+
+// LDS chunk swizzle of a K/V tile: 16-byte chunk c of tile row r is stored at
+// chunk position c ^ swz(r).  A row is 256 bytes (d = 128), exactly one pass
+// over the 64 four-byte banks, so rows only spread over banks through the
+// swizzle.  swz maps r % 16 one-to-one onto 0..15 (the 16 rows of a K
+// fragment read hit 16 different chunk positions) and puts r's low two bits
+// on the chunk's high two bits: a transposed V read covers 4 consecutive rows
+// x 4 consecutive chunks, which then land on 16 different positions.  With
+// d = 64 (8 chunks, two rows per bank pass) the plain r % 8 is used.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return r % CH;
+}
 
 template <int D, int HC>
-__global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs a) {
-  constexpr int RB = 4 / HC;     // 32-row blocks per head in one workgroup
+__global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_causal_kernel(PrefillArgs a) {
+  constexpr int RB = kWaves / HC;  // 32-row blocks per head in one workgroup
   constexpr int BM = 32 * RB;    // query rows per workgroup
   constexpr int CH = D / 8;      // 16-byte chunks per K/V row
   constexpr int KS = D / 16;     // k-steps of the score product
   constexpr int NT = D / 32;     // 32-wide d tiles of the PV product
   constexpr int TILE_BYTES = kBN * D * 2;
-  __shared__ __attribute__((aligned(16))) char sk[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char sv[2][TILE_BYTES];
+  // two K/V buffers as four distinct LDS objects, selected at compile time,
+  // so the compiler can tell the tile being read from the one being filled
+  __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sk1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sv0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sv1[TILE_BYTES];
 
   // ---- XCD-aware, heavy-first workgroup -> work mapping
   const int n = blockIdx.x;
@@ -107,19 +128,20 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
   // sequence end re-read its last row (in bounds); their keys are always
   // masked for valid query rows, so they contribute nothing.
   constexpr int RPI = 64 / CH;                  // tile rows per wave instruction
-  constexpr int NINS = kBN / (RPI * 4);         // instructions per wave per tensor
+  constexpr int NINS = kBN / (RPI * kWaves);    // instructions per wave per tensor
+  static_assert(NINS * RPI * kWaves == kBN, "tile rows must split evenly over the waves");
   const int dma_r = lane / CH;                  // row within an instruction's rows
   const int dma_c = (lane % CH);                // physical chunk of this lane's LDS slot
-  auto dma_tile = [&](int j, int buf) {
+  auto dma_tile = [&](int j, char* kdst, char* vdst) {
 #pragma unroll
     for (int u = 0; u < NINS; ++u) {
-      const int r0 = (u * 4 + wave) * RPI;      // first tile row of this instruction
+      const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
       const int r = r0 + dma_r;
       const int key = min(j * kBN + r, S - 1);
-      const int c = dma_c ^ (r % CH);           // logical chunk stored at this slot
+      const int c = dma_c ^ swz<CH>(r);         // logical chunk stored at this slot
       const size_t off = (size_t)key * kv_row_stride + c * 8;
-      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(sk[buf] + r0 * (2 * D)), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(sv[buf] + r0 * (2 * D)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(kdst + r0 * (2 * D)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(vdst + r0 * (2 * D)), 16, 0, 0);
     }
   };
   auto dma_wait = [&]() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -131,31 +153,47 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
     for (int r = 0; r < 16; ++r) o[nt][r] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  dma_tile(0, 0);
+  dma_tile(0, sk0, sv0);
   dma_wait();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+  // one key tile: compute from (kt, vt) while the next tile fills (kn, vn)
+  auto tile_step = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
     // the other buffer was last read in iteration j-1, before its closing barrier
-    if (j + 1 < n_tiles) dma_tile(j + 1, buf ^ 1);
+    if (j + 1 < n_tiles) dma_tile(j + 1, kn, vn);
     const int key0 = j * kBN;
     // this wave's rows all precede the tile: nothing to do but keep in step
     if (key0 <= wave_last_row) {
-      const char* kt = sk[buf];
-      const char* vt = sv[buf];
-      // ---- S^T for the two 32-key halves
+      // ---- S^T for the two 32-key halves, k-steps interleaved: the K
+      // fragments of step ks+1 are read while the two products of step ks run
       f32x16 sacc[2];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+      for (int r = 0; r < 16; ++r) {
+        sacc[0][r] = 0.f;
+        sacc[1][r] = 0.f;
+      }
+      // swz(krow) is the same for both halves (32 is a multiple of 16)
+      const char* kp0 = kt + l32 * (2 * D);
+      auto kfrag = [&](int kh, int ks) {
+        return lds_load<u32x4>(kp0 + kh * 32 * (2 * D) + (((2 * ks + h2) ^ swz<CH>(l32)) << 4));
+      };
+      // fragments run two k-steps ahead of the products that use them
+      u32x4 kf[KS][2];
+      kf[0][0] = kfrag(0, 0);
+      kf[0][1] = kfrag(1, 0);
+      kf[1][0] = kfrag(0, 1);
+      kf[1][1] = kfrag(1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
-        const int krow = 32 * kh + l32;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kf = lds_load<u32x4>(kt + krow * (2 * D) + (((2 * ks + h2) ^ (krow % CH)) << 4));
-          sacc[kh] = mfma32(kf, qf[ks], sacc[kh]);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) {
+          kf[ks + 2][0] = kfrag(0, ks + 2);
+          kf[ks + 2][1] = kfrag(1, ks + 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads for step ks+2,
         }
+        sacc[0] = mfma32(kf[ks][0], qf[ks], sacc[0]);
+        sacc[1] = mfma32(kf[ks][1], qf[ks], sacc[1]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the products of step ks
       }
       // ---- online softmax (row = this lane's query; keys split with lane^32).
       // The max is taken on the raw scores (scale > 0 keeps the order) and the
@@ -212,8 +250,8 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
           const int c = col >> 3, w = col & 7;
           const int ra = 16 * p + 4 * h2 + (s16 >> 2);
           const int rbw = ra + 8;
-          const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ (ra % CH)) << 4) + 2 * w);
-          const u32x2 vb = lds_read_tr16(vt + rbw * (2 * D) + ((c ^ (rbw % CH)) << 4) + 2 * w);
+          const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ swz<CH>(ra)) << 4) + 2 * w);
+          const u32x2 vb = lds_read_tr16(vt + rbw * (2 * D) + ((c ^ swz<CH>(rbw)) << 4) + 2 * w);
           const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
           o[nt] = mfma32(vf, pf, o[nt]);
         }
@@ -221,6 +259,10 @@ __global__ __launch_bounds__(256, 2) void gqa_prefill_causal_kernel(PrefillArgs 
     }
     dma_wait();
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile_step(j, sk0, sv0, sk1, sv1);
+    if (j + 1 < n_tiles) tile_step(j + 1, sk1, sv1, sk0, sv0);
   }
 
   // ---- epilogue: O / l -> bf16, rows < S only
@@ -253,8 +295,8 @@ static int gcd_int(int x, int y) {
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S, int h_q, int n_kv, int D, hipStream_t stream) {
   const int G = h_q / n_kv;
-  const int HC = gcd_int(G, 4);
-  const int BM = 32 * (4 / HC);
+  const int HC = gcd_int(G, kWaves);
+  const int BM = 32 * (kWaves / HC);
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -269,14 +311,16 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   a.n_hc = G / HC;
   a.n_wg = B * n_kv * a.n_hc * a.n_qb;
   a.n_wg_pad = (a.n_wg + kNumXcd - 1) / kNumXcd * kNumXcd;
-  const dim3 grid(a.n_wg_pad), block(256);
+  const dim3 grid(a.n_wg_pad), block(kWaves * 64);
 #define GQA_LAUNCH_PREFILL(DD, HH) hipLaunchKernelGGL((gqa_prefill_causal_kernel<DD, HH>), grid, block, 0, stream, a)
   if (D == 128) {
-    if (HC == 4) GQA_LAUNCH_PREFILL(128, 4);
+    if (HC == 8) GQA_LAUNCH_PREFILL(128, 8);
+    else if (HC == 4) GQA_LAUNCH_PREFILL(128, 4);
     else if (HC == 2) GQA_LAUNCH_PREFILL(128, 2);
     else GQA_LAUNCH_PREFILL(128, 1);
   } else {
-    if (HC == 4) GQA_LAUNCH_PREFILL(64, 4);
+    if (HC == 8) GQA_LAUNCH_PREFILL(64, 8);
+    else if (HC == 4) GQA_LAUNCH_PREFILL(64, 4);
     else if (HC == 2) GQA_LAUNCH_PREFILL(64, 2);
     else GQA_LAUNCH_PREFILL(64, 1);
   }
