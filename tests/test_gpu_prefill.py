@@ -47,6 +47,24 @@ def test_prefill_head_dim_64(S):
     assert pu.max_err(out, ref) <= TOL
 
 
+@pytest.mark.parametrize("slope", [4.0, -4.0, 0.25])
+def test_prefill_steep_score_trends(slope):
+    """Scores with a linear trend along the keys: with slope 4 each 64-key tile
+    rises by about 33 log2 units, so the running reference max has to move on
+    almost every tile; with slope -4 the first tile holds the max and later
+    weights underflow; 0.25 is a mild rise."""
+    S = 400
+    w = pwl(1, S, 8, 2, 128, seed=17)
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    t = torch.arange(S, device=DEV, dtype=torch.float32)
+    inp.k[..., 0] = (slope * t)[None, :, None].to(torch.bfloat16)  # multiples of 1/4 below 1024: exact
+    inp.q[..., 0] = 1.0
+    out = run(inp)
+    pu.sync()
+    ref = oracle.prefill_causal(*pu.prefill_f64(inp), w.scale)
+    assert pu.max_err(out, ref) <= TOL
+
+
 def test_prefill_first_row_is_first_value_row():
     w = pwl(2, 70, 8, 2, 128, seed=3)
     inp = inputs.make_prefill_inputs(w, device=DEV)

@@ -45,7 +45,6 @@ struct PrefillArgs {
 };
 
 constexpr int kBN = 64;  // keys per tile
-constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag the true max
 constexpr int kNumXcd = 8;
 constexpr int kWaves = 8;  // wavefronts per workgroup
 
@@ -165,77 +164,93 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_causal_kernel(Pref
     // this wave's rows all precede the tile: nothing to do but keep in step
     if (key0 <= wave_last_row) {
       // ---- S^T for the two 32-key halves, k-steps interleaved: the K
-      // fragments of step ks+1 are read while the two products of step ks run
-      f32x16 sacc[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[0][r] = 0.f;
-        sacc[1][r] = 0.f;
-      }
-      // swz(krow) is the same for both halves (32 is a multiple of 16)
-      const char* kp0 = kt + l32 * (2 * D);
-      auto kfrag = [&](int kh, int ks) {
-        return lds_load<u32x4>(kp0 + kh * 32 * (2 * D) + (((2 * ks + h2) ^ swz<CH>(l32)) << 4));
-      };
-      // fragments run two k-steps ahead of the products that use them
-      u32x4 kf[KS][2];
-      kf[0][0] = kfrag(0, 0);
-      kf[0][1] = kfrag(1, 0);
-      kf[1][0] = kfrag(0, 1);
-      kf[1][1] = kfrag(1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 2 < KS) {
-          kf[ks + 2][0] = kfrag(0, ks + 2);
-          kf[ks + 2][1] = kfrag(1, ks + 2);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads for step ks+2,
-        }
-        sacc[0] = mfma32(kf[ks][0], qf[ks], sacc[0]);
-        sacc[1] = mfma32(kf[ks][1], qf[ks], sacc[1]);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the products of step ks
-      }
-      // ---- online softmax (row = this lane's query; keys split with lane^32).
-      // The max is taken on the raw scores (scale > 0 keeps the order) and the
-      // scale folds into one FMA feeding exp2.  The reference max m (log2
-      // units) moves only when the tile max exceeds it by more than
-      // kRescaleSlack: O and l share the reference, so the result is the same,
-      // p stays <= 2^kRescaleSlack, and rescaling O is skipped on almost
-      // every tile.
+      // fragments of step ks+2 are read while the two products of step ks run.
+      // Keys above the diagonal get -inf.
       const bool diag = key0 + kBN - 1 > row0;
-      if (diag) {
+      auto scores = [&](f32x16(&sacc)[2]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[0][r] = 0.f;
+          sacc[1][r] = 0.f;
+        }
+        // swz(krow) is the same for both halves (32 is a multiple of 16)
+        const char* kp0 = kt + l32 * (2 * D);
+        auto kfrag = [&](int kh, int ks) {
+          return lds_load<u32x4>(kp0 + kh * 32 * (2 * D) + (((2 * ks + h2) ^ swz<CH>(l32)) << 4));
+        };
+        u32x4 kf[KS][2];
+        kf[0][0] = kfrag(0, 0);
+        kf[0][1] = kfrag(1, 0);
+        kf[1][0] = kfrag(0, 1);
+        kf[1][1] = kfrag(1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 2 < KS) {
+            kf[ks + 2][0] = kfrag(0, ks + 2);
+            kf[ks + 2][1] = kfrag(1, ks + 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads for step ks+2,
+          }
+          sacc[0] = mfma32(kf[ks][0], qf[ks], sacc[0]);
+          sacc[1] = mfma32(kf[ks][1], qf[ks], sacc[1]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the products of step ks
+        }
+        if (diag) {
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * h2 + (r & 3);
+              sacc[kh][r] = key > qrow ? kNegInf : sacc[kh][r];
+            }
+        }
+      };
+      // p = 2^(scale*log2(e)*s - m) in place, returning this lane's sum
+      auto probs = [&](f32x16(&sacc)[2], float mref) {
+        float psum = 0.f;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kh + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            sacc[kh][r] = key > qrow ? kNegInf : sacc[kh][r];
+            const float p = fast_exp2(__builtin_fmaf(sacc[kh][r], a.qk_scale_log2, -mref));
+            sacc[kh][r] = p;
+            psum += p;
           }
-      }
-      float mt = kNegInf;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kh][r]);
-      mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
-      const bool grow = mt > m + kRescaleSlack;
-      const float m_new = grow ? mt : m;
-      const float alpha = grow ? fast_exp2(m - m_new) : 1.0f;
-      m = m_new;
+        return psum;
+      };
+      f32x16 sacc[2];
+      scores(sacc);
+      // ---- online softmax (row = this lane's query; its keys are split with
+      // lane ^ 32).  The reference max m (log2 units) is shared by O and l,
+      // so any reference gives the same result as long as nothing overflows.
+      // Fast path, every tile after the first: keep m and check that the
+      // tile's p stay bounded (psum <= 2^30 in every lane).  Otherwise (the
+      // first tile, or scores that rose far above m) the wave recomputes the
+      // scores, moves m to the running max (one exchange with lane ^ 32),
+      // rescales O and l, and takes p again.
       float psum = 0.f;
+      bool slow = j == 0;
+      if (!slow) {
+        psum = probs(sacc, m);
+        slow = __builtin_amdgcn_ballot_w64(!(psum <= 0x1p30f)) != 0;  // also catches inf / NaN
+        if (slow) scores(sacc);
+      }
+      if (slow) {
+        float mt = kNegInf;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[kh][r], a.qk_scale_log2, -m_new));
-          sacc[kh][r] = p;
-          psum += p;
-        }
-      l = l * alpha + psum;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kh][r]);
+        mt = wave_max_xor(mt, 32) * a.qk_scale_log2;  // scale > 0 keeps the order
+        const float m_new = fmaxf(m, mt);             // finite: key 0 is visible to every row
+        const float alpha = fast_exp2(m - m_new);     // 0 on the first tile
+        m = m_new;
+        l *= alpha;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[nt] *= alpha;
+        psum = probs(sacc, m);
       }
+      l += psum;
       // ---- O^T += V^T P^T, 4 k-steps of 16 keys
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
