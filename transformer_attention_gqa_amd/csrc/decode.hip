@@ -311,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     for (int i = 0; i < QCH; ++i) {
       const int e = threadIdx.x + i * NW * 64;
       const int hl = e / CH, c = e % CH;
-      if (e < HPC * CH) lds_store(sq + hl * (2 * D) + ((c ^ (hl % CH)) << 4), r.v[i]);
+      if (e < HPC * CH) lds_store(sq + hl * (2 * D) + ((c ^ swz<CH>(hl)) << 4), r.v[i]);
     }
   };
 
@@ -397,13 +397,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           t3 = e4m3x4_to_bf16x4(vreg[u][3]);
           const u32x4 vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
           const u32x4 vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-          const int sw = r % CH;
+          const int sw = swz<CH>(r);
           lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), klo);
           lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
           lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
           lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
         } else {
-          const int pc = ld_chunk ^ (r % CH);
+          const int pc = ld_chunk ^ swz<CH>(r);
           lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
           lds_store(vt + r * (2 * D) + (pc << 4), vreg[u]);
         }
@@ -423,8 +423,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 kf = lds_load<u32x4>(kt + l32 * (2 * D) + (((2 * ks + h2) ^ (l32 % CH)) << 4));
-          const u32x4 qf = lds_load<u32x4>(sq + l32 * (2 * D) + (((2 * ks + h2) ^ (l32 % CH)) << 4));
+          const u32x4 kf = lds_load<u32x4>(kt + l32 * (2 * D) + (((2 * ks + h2) ^ swz<CH>(l32)) << 4));
+          const u32x4 qf = lds_load<u32x4>(sq + l32 * (2 * D) + (((2 * ks + h2) ^ swz<CH>(l32)) << 4));
           sacc = mfma32(kf, qf, sacc);
         }
         if (tt0 + kTile > t_end) {
@@ -462,8 +462,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           for (int n = 0; n < NT32; ++n) {
             const int col = 32 * n + 16 * (gi & 1) + 4 * (s16 & 3);
             const int c = col >> 3, wsub = col & 7;
-            const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ (ra % CH)) << 4) + 2 * wsub);
-            const u32x2 vb = lds_read_tr16(vt + rb * (2 * D) + ((c ^ (rb % CH)) << 4) + 2 * wsub);
+            const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ swz<CH>(ra)) << 4) + 2 * wsub);
+            const u32x2 vb = lds_read_tr16(vt + rb * (2 * D) + ((c ^ swz<CH>(rb)) << 4) + 2 * wsub);
             o32[n] = mfma32(u32x4{va[0], va[1], vb[0], vb[1]}, pf, o32[n]);
           }
         }
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           u32x4 kf[KK];
   #pragma unroll
           for (int kk = 0; kk < KK; ++kk)
-            kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ (row % CH)) << 4));
+            kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ swz<CH>(row)) << 4));
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
             // B operand of S^T = K Q^T: lane holds Q[head 16hb + r16][32kk + 8q4 .. +7]
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-              acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ (qrow % CH)) << 4)), acc);
+              acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ swz<CH>(qrow)) << 4)), acc);
             sc[h][hb] = acc;
           }
         }
@@ -558,8 +558,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           const int c = col >> 3, wsub = col & 7;
           const int row_lo = 4 * q4 + (r16 >> 2);
           const int row_hi = 16 + row_lo;
-          const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ (row_lo % CH)) << 4) + 2 * wsub);
-          const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ (row_hi % CH)) << 4) + 2 * wsub);
+          const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ swz<CH>(row_lo)) << 4) + 2 * wsub);
+          const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ swz<CH>(row_hi)) << 4) + 2 * wsub);
           const u32x4 vf = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);

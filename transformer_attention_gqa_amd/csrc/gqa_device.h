@@ -44,6 +44,22 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                   0, 0);
 }
 
+// LDS chunk swizzle of a K/V (or Q) tile: 16-byte chunk c of tile row r is stored at
+// chunk position c ^ swz(r).  A row is 256 bytes (d = 128), exactly one pass
+// over the 64 four-byte banks, so rows only spread over banks through the
+// swizzle.  swz maps r % 16 one-to-one onto 0..15 (the 16 rows of a K
+// fragment read hit 16 different chunk positions) and puts r's low two bits
+// on the chunk's high two bits: the transposed V reads (4 consecutive rows x
+// 4 consecutive chunks for the 32x32 products, 16 rows x 2 chunks for the
+// 16x16 ones) then spread evenly over all 16 positions, so every fragment
+// read takes the minimum number of bank passes.  With d = 64 (8 chunks, two
+// rows per bank pass) the plain r % 8 is used.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return r % CH;
+}
+
 // Two float32 -> packed bf16x2 (round to nearest even; lo in bits 0..15).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;

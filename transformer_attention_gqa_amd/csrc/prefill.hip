@@ -48,20 +48,6 @@ constexpr int kBN = 64;  // keys per tile
 constexpr int kNumXcd = 8;
 constexpr int kWaves = 8;  // wavefronts per workgroup
 
-// LDS chunk swizzle of a K/V tile: 16-byte chunk c of tile row r is stored at
-// chunk position c ^ swz(r).  A row is 256 bytes (d = 128), exactly one pass
-// over the 64 four-byte banks, so rows only spread over banks through the
-// swizzle.  swz maps r % 16 one-to-one onto 0..15 (the 16 rows of a K
-// fragment read hit 16 different chunk positions) and puts r's low two bits
-// on the chunk's high two bits: a transposed V read covers 4 consecutive rows
-// x 4 consecutive chunks, which then land on 16 different positions.  With
-// d = 64 (8 chunks, two rows per bank pass) the plain r % 8 is used.
-template <int CH>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return r % CH;
-}
-
 template <int D, int HC>
 __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_causal_kernel(PrefillArgs a) {
   constexpr int RB = kWaves / HC;  // 32-row blocks per head in one workgroup
