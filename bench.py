@@ -10,7 +10,9 @@ launched back to back and timed by the host clock between two device
 synchronisations; HIP events recorded on the launch stream at the two ends of
 the same region give the device-side time.  The KV cache is held in several
 copies that the steps rotate through, so the 256 MB Infinity Cache cannot
-serve one step's reads from the previous step.
+serve one step's reads from the previous step.  Before the W warmup steps of
+each workload the GPU runs dense matrix products for 0.3 s, so the timed
+steps do not start from the idle clock state.
 
 value    = KV bytes per step / step time  (KV bytes = 2 * b * n_kv * d_h * sum L_b)
 roofline = the split kernel, which reads the cache: KV bytes / its mean launch
@@ -62,6 +64,19 @@ def measured_traffic(kernel_key):
     if not ent or ent.get("source_digest") != source_digest():
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def precondition_gpu(seconds=0.3):
+    """Run dense bf16 matrix products for about `seconds` so the GPU has left
+    its idle clock state before the first warmup step (a few warmup steps of
+    a 40 us decode would not get it there)."""
+    a = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            torch.mm(a, a)
+        torch.cuda.synchronize()
+    del a
 
 
 def time_steps(step_fn, steps, warmup, use_graph=False):
@@ -262,13 +277,15 @@ def kernel_identity(name):
 
 
 def _workload_launches():
-    """(kernel, template args, grid threads) -> (counter key, workload, algorithmic bytes or flops, unit).
+    """[((kernel, template args, grid threads), (counter key, workload, algorithmic bytes or flops, unit))].
 
     Mirrors the library's launch plan: the decode split kernel runs W
     workgroups of 512 threads (matrix-core paths) or 256 (float32 path); the
     combine kernel a grid of (slabs, ceil(heads_per_chunk * d / 4 / 256))
-    workgroups of 256."""
-    out = {}
+    workgroups of 256.  Two workloads can launch the same kernel with the same
+    grid (the combine kernel of the ragged GQA and the long MQA decode); such
+    launches are told apart by the workload whose unambiguous kernel ran last."""
+    out = []
     for wl in inputs.DECODE_WORKLOADS.values():
         qd = torch.empty((wl.B, wl.h_q, wl.d_h), dtype={"f32": torch.float32, "bf16": torch.bfloat16}[wl.q_dtype],
                          device="meta")
@@ -281,22 +298,23 @@ def _workload_launches():
         key = f"decode_split_{wl.kv_dtype}:{wl.name}"
         hpc = 16 if (wl.kv_dtype == "f32" or G <= 16) else 32
         if wl.kv_dtype == "f32":
-            out[("gqa_decode_split_f32", (str(wl.d_h),), ns * 256)] = (key, wl.name, kv, "bytes")
+            out.append((("gqa_decode_split_f32", (str(wl.d_h),), ns * 256), (key, wl.name, kv, "bytes")))
         else:
             targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8")
-            out[("gqa_decode_split_mfma", targs, ns * 512)] = (key, wl.name, kv, "bytes")
+            out.append((("gqa_decode_split_mfma", targs, ns * 512), (key, wl.name, kv, "bytes")))
         n_slabs = wl.B * wl.n_kv * -(-G // hpc)
         grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
         targs = (str(wl.d_h), "false" if wl.q_dtype == "f32" else "true")
-        out[("gqa_decode_combine", targs, grid)] = (f"decode_combine:{wl.name}", wl.name, None, None)
+        out.append((("gqa_decode_combine", targs, grid), (f"decode_combine:{wl.name}", wl.name, None, None)))
     for wl in inputs.PREFILL_WORKLOADS.values():
         G = wl.h_q // wl.n_kv
         hc = math.gcd(G, 8)
         bm = 32 * (8 // hc)
         n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S // bm))
         grid = -(-n_wg // 8) * 8 * 512
-        out[("gqa_prefill_causal_kernel", (str(wl.d_h), str(hc)), grid)] = (
-            f"prefill_causal:{wl.name}", wl.name, roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h), "flops")
+        out.append((("gqa_prefill_causal_kernel", (str(wl.d_h), str(hc)), grid),
+                    (f"prefill_causal:{wl.name}", wl.name, roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h),
+                     "flops")))
     return out
 
 
@@ -311,32 +329,56 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
         raise FileNotFoundError(f"no *{suffix} in {d}")
 
     launches = _workload_launches()
+    by_key = {}
+    for key, ent in launches:
+        by_key.setdefault(key, []).append(ent)
+    info = {ent[0]: (key, ent) for key, ent in launches}  # counter key -> (launch key, entry)
+
+    def resolve(stream):
+        """(launch key, row) in dispatch order -> (counter key, row) for our kernels."""
+        cur = None
+        for key, r in stream:
+            ents = by_key.get(key)
+            if not ents:
+                continue
+            if len(ents) == 1:
+                cur = ents[0][1]
+                yield ents[0][0], r
+            else:
+                match = [e for e in ents if e[1] == cur]
+                if match:
+                    yield match[0][0], r
+
+    def ordered(rs):
+        return sorted(rs, key=lambda r: int(r["Dispatch_Id"]))
+
     dur = {}
-    for r in rows(trace_dir, "kernel_trace.csv"):
-        key = (*kernel_identity(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
-        if key in launches:
-            dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    trace = ordered(rows(trace_dir, "kernel_trace.csv"))
+    for ckey, r in resolve(((*kernel_identity(r["Kernel_Name"]),
+                             int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])), r) for r in trace):
+        dur.setdefault(ckey, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     counters = {}
     for kind, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         calib = []
-        for r in rows(d, "counter_collection.csv"):
+        crow = ordered(rows(d, "counter_collection.csv"))
+        for r in crow:
             key = (*kernel_identity(r["Kernel_Name"]), int(r["Grid_Size"]))
-            v = float(r["Counter_Value"])
-            if key[0] == "vectorized_elementwise_kernel" and key[2] == CALIB_GRID and v > 1024:
-                calib.append(v)
-            elif key in launches:
-                counters.setdefault((kind, key), []).append(v)
+            if key[0] == "vectorized_elementwise_kernel" and key[2] == CALIB_GRID and float(r["Counter_Value"]) > 1024:
+                calib.append(float(r["Counter_Value"]))
+        for ckey, r in resolve(((*kernel_identity(r["Kernel_Name"]), int(r["Grid_Size"])), r) for r in crow):
+            counters.setdefault((kind, ckey), []).append(float(r["Counter_Value"]))
         counters[(kind, "scale")] = (1 << 20) / statistics.median(calib)  # KiB expected / KiB counted
     digest = source_digest()
     summary = {"source_digest": digest, "fetch_scale": counters[("FETCH_SIZE", "scale")],
                "write_scale": counters[("WRITE_SIZE", "scale")], "kernels": {}}
     os.makedirs(dest, exist_ok=True)
-    for key, (ckey, wname, algo, algo_unit) in sorted(launches.items(), key=lambda kv: kv[1][0]):
-        if key not in dur:
+    for ckey in sorted(info):
+        key, (_, wname, algo, algo_unit) = info[ckey]
+        if ckey not in dur:
             continue
-        d = sorted(dur[key])
-        fetch = counters.get(("FETCH_SIZE", key))
-        write = counters.get(("WRITE_SIZE", key))
+        d = sorted(dur[ckey])
+        fetch = counters.get(("FETCH_SIZE", ckey))
+        write = counters.get(("WRITE_SIZE", ckey))
         fb = statistics.median(fetch) * 1024 * summary["fetch_scale"] if fetch else None
         wb = statistics.median(write) * 1024 * summary["write_scale"] if write else None
         ent = {"kernel": key[0], "template_args": list(key[1]), "workload": wname, "grid_threads": key[2],
@@ -380,6 +422,17 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
                 f.write(f"causal flops: {algo:.4e} -> {ent['achieved_TFLOPs_at_mean']:.0f} TFLOP/s at the mean "
                         f"duration ({ent['achieved_TFLOPs_at_mean'] / 2500 * 100:.1f}% of 2.5 PFLOP/s bf16)\n")
     json.dump(summary, open(os.path.join(dest, "counters.json"), "w"), indent=1)
+    with open(os.path.join(dest, "all_kernels__bench_default_run.txt"), "w") as f:
+        f.write(f"rocprofv3 --stats kernel summary of: {PROFILE_COMMANDS['trace']}\n")
+        f.write("(all workloads of the default bench run, plus the dense matrix products that warm the GPU up "
+                "before each workload; per-workload figures are in the <kernel>__<workload>.txt files)\n")
+        f.write(f"kernel source digest: {digest}\n")
+        f.write(f"{'calls':>6} {'total_ms':>10} {'mean_us':>10} {'min_us':>9} {'max_us':>9} {'pct':>6}  kernel\n")
+        for r in rows(trace_dir, "kernel_stats.csv"):
+            name = r["Name"] if len(r["Name"]) <= 110 else r["Name"][:107] + "..."
+            f.write(f"{int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+                    f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:9.2f} "
+                    f"{float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):6.2f}  {name}\n")
     return summary
 
 
@@ -421,6 +474,7 @@ def main(argv=None):
 
     def run(name, steps, warmup):
         print(f"[bench] {name} steps={steps} warmup={warmup}", file=sys.stderr, flush=True)
+        precondition_gpu()
         if name in inputs.PREFILL_WORKLOADS:
             return bench_prefill(inputs.PREFILL_WORKLOADS[name], steps, warmup, use_graph)
         return bench_decode(inputs.DECODE_WORKLOADS[name], steps, warmup, use_graph, args.n_split)
