@@ -235,6 +235,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   char* kt = smem[wave][0];
   char* vt = smem[wave][1];
   float* ow = reinterpret_cast<float*>(smem[wave][0]);
+  // O exchange layout in a wave slab: head h's D floats are one row, and its
+  // 16-byte chunk q sits at q ^ (h % (D/4)).  A row is 512 bytes (d = 128),
+  // so without the swizzle the heads of one store instruction would all hit
+  // the same banks; with it both the fragment stores and the row reads of
+  // the merge spread over all banks.
+  auto ow_idx = [](int h, int d) { return h * D + ((((d >> 2) ^ (h % (D / 4))) << 2) | (d & 3)); };
 
   // per-lane load assignment.  bf16: a load instruction covers 64/CH rows,
   // each row by CH consecutive lanes.  fp8: rows of D bytes, D/16 lanes per row.
@@ -580,7 +586,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       for (int n = 0; n < NT32; ++n)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq)
-          lds_store(ow + l32 * D + 32 * n + 8 * rq + 4 * h2,
+          lds_store(ow + ow_idx(l32, 32 * n + 8 * rq + 4 * h2),
                     f32x4{o32[n][4 * rq], o32[n][4 * rq + 1], o32[n][4 * rq + 2], o32[n][4 * rq + 3]});
       if (h2 == 0) {
         sm_ml[wave][l32][0] = m[0];
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) lds_store(ow + (hb * 16 + r16) * D + 16 * n + 4 * q4, o[hb][n]);
+        for (int n = 0; n < NT; ++n) lds_store(ow + ow_idx(hb * 16 + r16, 16 * n + 4 * q4), o[hb][n]);
         if (q4 == 0) {
           sm_ml[wave][hb * 16 + r16][0] = m[hb];
           sm_ml[wave][hb * 16 + r16][1] = l[hb];
@@ -605,24 +611,33 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < cur.nh * D; e += NW * 64) {
-      const int hl = e / D, d = e - hl * D;
-      float M = kNegInf;
+    // each thread merges whole 16-byte chunks (4 consecutive d of one head);
+    // the trip count is a compile-time constant so the loads of all its
+    // chunks are in flight together
+    constexpr int D4 = D / 4;
 #pragma unroll
-      for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, sm_ml[wv][hl][0]);
-      float acc = 0.f, lsum = 0.f;
+    for (int i = 0; i < (HPC * D4 + NW * 64 - 1) / (NW * 64); ++i) {
+      const int e4 = threadIdx.x + i * NW * 64;
+      const int hl = e4 / D4, q = e4 - hl * D4;
+      if (e4 < HPC * D4 && hl < cur.nh) {
+        float M = kNegInf;
 #pragma unroll
-      for (int wv = 0; wv < NW; ++wv) {
-        const float mw = sm_ml[wv][hl][0];
-        const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-        acc += f * reinterpret_cast<const float*>(smem[wv][0])[hl * D + d];
-        lsum += f * sm_ml[wv][hl][1];
-      }
-      const size_t row = (size_t)cur.slot * HPC + hl;
-      a.part_o[row * D + d] = acc;
-      if (d == 0) {
-        a.part_ml[row * 2 + 0] = M;
-        a.part_ml[row * 2 + 1] = lsum;
+        for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, sm_ml[wv][hl][0]);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+          const float mw = sm_ml[wv][hl][0];
+          const float f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+          acc += f * lds_load<f32x4>(reinterpret_cast<const float*>(smem[wv][0]) + ow_idx(hl, 4 * q));
+          lsum += f * sm_ml[wv][hl][1];
+        }
+        const size_t row = (size_t)cur.slot * HPC + hl;
+        *reinterpret_cast<f32x4*>(a.part_o + row * D + 4 * q) = acc;
+        if (q == 0) {
+          a.part_ml[row * 2 + 0] = M;
+          a.part_ml[row * 2 + 1] = lsum;
+        }
       }
     }
     if (!has_next) break;
