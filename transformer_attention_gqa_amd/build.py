@@ -66,8 +66,23 @@ def build(verbose=False):
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _check_self_contained(tmp)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def _check_self_contained(lib):
+    """Fail the build if the library leaves any of its own symbols undefined
+    (e.g. a kernel whose host-side launch stub was not emitted), which would
+    otherwise only show when the library is loaded."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                         text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{res.stdout}")
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "_ZN3gqa" in ln]
+    if missing:
+        raise RuntimeError(f"{os.path.basename(lib)} leaves its own symbols undefined: {missing}")
 
 
 def main(argv=None):

@@ -117,16 +117,40 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_causal_kernel(Pref
   static_assert(NINS * RPI * kWaves == kBN, "tile rows must split evenly over the waves");
   const int dma_r = lane / CH;                  // row within an instruction's rows
   const int dma_c = (lane % CH);                // physical chunk of this lane's LDS slot
-  auto dma_tile = [&](int j, char* kdst, char* vdst) {
+  // Per-lane element offsets inside a tile, computed once; a full tile then
+  // costs one wave-uniform base and one instruction per 1 KiB.  Only a tile
+  // that runs past the sequence end clamps its rows.
+  // (a vector, not an array: a local array captured by the lambdas below
+  // makes hipcc's host pass drop this kernel's launch stub)
+  static_assert(NINS <= 4, "per-lane DMA offsets are kept in a u32x4");
+  u32x4 dma_off = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < NINS; ++u) {
-      const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
-      const int r = r0 + dma_r;
-      const int key = min(j * kBN + r, S - 1);
-      const int c = dma_c ^ swz<CH>(r);         // logical chunk stored at this slot
-      const size_t off = (size_t)key * kv_row_stride + c * 8;
-      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(kdst + r0 * (2 * D)), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(vdst + r0 * (2 * D)), 16, 0, 0);
+  for (int u = 0; u < NINS; ++u) {
+    const int r = (u * kWaves + wave) * RPI + dma_r;
+    dma_off[u] = (uint32_t)(r * kv_row_stride + (dma_c ^ swz<CH>(r)) * 8);
+  }
+  auto dma_tile = [&](int j, char* kdst, char* vdst) {
+    const int key0 = j * kBN;
+    if (key0 + kBN <= S) {
+      const uint16_t* kt = kbase + (size_t)key0 * kv_row_stride;
+      const uint16_t* vt = vbase + (size_t)key0 * kv_row_stride;
+#pragma unroll
+      for (int u = 0; u < NINS; ++u) {
+        const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
+        __builtin_amdgcn_global_load_lds(kt + dma_off[u], (lds_void*)(kdst + r0 * (2 * D)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + dma_off[u], (lds_void*)(vdst + r0 * (2 * D)), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NINS; ++u) {
+        const int r0 = (u * kWaves + wave) * RPI;
+        const int r = r0 + dma_r;
+        const int key = min(key0 + r, S - 1);
+        const int c = dma_c ^ swz<CH>(r);         // logical chunk stored at this slot
+        const size_t off = (size_t)key * kv_row_stride + c * 8;
+        __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(kdst + r0 * (2 * D)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(vdst + r0 * (2 * D)), 16, 0, 0);
+      }
     }
   };
   auto dma_wait = [&]() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); };
