@@ -79,6 +79,37 @@ def precondition_gpu(seconds=0.3):
     del a
 
 
+def measure_ceilings():
+    """Reference rates measured on this GPU in the same run (context for the
+    roofline fractions, which are taken against the vendor peaks): a 2 GiB
+    device-to-device copy (bytes read + written per second) and an
+    8192^3 bf16 matrix product through the vendor BLAS."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+    n = 1 << 30  # bf16 elements: 2 GiB
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    bm = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
+    t_mm = timed(lambda: torch.mm(a, bm), 20)
+    del a, bm
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * 2 * n / t_copy / 1e9,
+            "bf16_gemm_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
+            "note": "2 GiB device copy (read + write bytes) and an 8192^3 bf16 torch.mm, same run"}
+
+
 def time_steps(step_fn, steps, warmup, use_graph=False):
     """Run `warmup` untimed steps, then time exactly `steps` steps.
 
@@ -446,6 +477,7 @@ def main(argv=None):
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / GEMM reference rates")
     ap.add_argument("--graph", action="store_true", help="time one HIP-graph replay of the K steps instead of "
                     "K eager launches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -509,6 +541,9 @@ def main(argv=None):
         "main": {k: v for k, v in main_res.items() if k not in ("config", "roofline")},
         "workloads": others,
     }
+    if not args.no_ceilings:
+        print("[bench] measured ceilings", file=sys.stderr, flush=True)
+        line["measured_ceilings"] = measure_ceilings()
     if not args.no_cpu_baseline and args.workload in inputs.DECODE_WORKLOADS:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inputs.DECODE_WORKLOADS[args.workload])

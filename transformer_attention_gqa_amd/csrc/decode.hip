@@ -721,7 +721,7 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
       for (int h = 0; h < HPC; ++h) sc[h] = 0.f;
       if (valid) {
         const float4* kr = reinterpret_cast<const float4*>(kg + (slab + tok) * D);
-#pragma unroll 8
+#pragma unroll
         for (int d4 = 0; d4 < D / 4; ++d4) {
           const float4 kv = kr[d4];
 #pragma unroll
@@ -757,7 +757,7 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
         for (int c = 0; c < DL; ++c) o[h][c] *= alpha[h];
       // V rows U at a time: all U loads are issued before the first use;
       // rows past the last valid one are re-reads of it and are skipped
-      constexpr int U = 8;
+      constexpr int U = 64 / DL;
       for (int tt = 0; tt < nvalid; tt += U) {
         float vv[U][DL];
 #pragma unroll
