@@ -25,6 +25,8 @@ Sources (page title, then section):
 Modules:
   codecs     -- stored-value decoders (bf16 bit patterns, OCP e4m3fn codes).
   attention  -- the decode and causal-prefill definitions.
+  paged      -- decode over a paged cache ("Multi-Query Attention (MQA)"
+                glossary, "PagedAttention").
 
 Pinning: every function here is checked by `-m "not gpu"` tests against
 closed forms, invariants the pages fix, a library routine that computes the
@@ -32,7 +34,7 @@ same definition, and brute force on tiny inputs.  No function is parity
 unpinned.
 """
 
-from . import attention, codecs  # noqa: F401
+from . import attention, codecs, paged  # noqa: F401
 from .attention import (  # noqa: F401
     attend_one_row,
     decode,
@@ -41,3 +43,4 @@ from .attention import (  # noqa: F401
     prefill_rows,
 )
 from .codecs import bf16_bits_to_f64, dequantize_fp8_cache, e4m3fn_to_f64  # noqa: F401
+from .paged import decode_paged, gather_logical_cache  # noqa: F401

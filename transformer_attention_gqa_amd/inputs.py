@@ -184,6 +184,65 @@ def poison_cache_tails(inp):
 
 
 @dataclass
+class PagedDecodeInputs:
+    """A decode workload's cache cut into pages and scattered over a pool."""
+    base: DecodeInputs                 # q, seq_lens and the contiguous cache the pages were cut from
+    page_size: int
+    k_pages: torch.Tensor              # [num_pages, n_kv, page_size, d]
+    v_pages: torch.Tensor
+    k_scale_pages: Optional[torch.Tensor]  # [num_pages, n_kv, page_size] float32 (fp8 only)
+    v_scale_pages: Optional[torch.Tensor]
+    block_table: torch.Tensor          # [B, max_pages] int32
+
+    @property
+    def num_pages(self):
+        return self.k_pages.shape[0]
+
+
+def make_paged_decode_inputs(wl, page_size, device="cpu", seq_lens=None, poison_tail=False, seed=None,
+                             spare_pages=3, junk_unused_entries=False, keep_base=True):
+    """Draw a decode workload (as make_decode_inputs) and scatter its cache into
+    a pool of B * S_max / page_size + spare_pages pages in a seeded random
+    order.  Spare pages hold NaN (fp8: code 0x7F, NaN scales).  With
+    junk_unused_entries, block-table entries past a sequence's last page are
+    set to -1 (they must never be read)."""
+    if wl.S_max % page_size:
+        raise ValueError("S_max must be a multiple of page_size")
+    seed = wl.seed if seed is None else seed
+    base = make_decode_inputs(wl, device=device, seq_lens=seq_lens, poison_tail=poison_tail, seed=seed)
+    B, n_kv, d, S = wl.B, wl.n_kv, wl.d_h, wl.S_max
+    max_pages = S // page_size
+    num_pages = B * max_pages + spare_pages
+    g = torch.Generator(device="cpu").manual_seed(seed * 104729 + page_size)
+    perm = torch.randperm(num_pages, generator=g)[:B * max_pages].to(torch.int32)
+    table = perm.reshape(B, max_pages).clone()
+    fp8 = wl.kv_dtype == "fp8"
+    kp = torch.empty((num_pages, n_kv, page_size, d), dtype=base.k.dtype, device=device)
+    vp = torch.empty_like(kp)
+    kp.fill_(0x7F) if fp8 else kp.fill_(float("nan"))
+    vp.fill_(0x7F) if fp8 else vp.fill_(float("nan"))
+    ksp = vsp = None
+    if fp8:
+        ksp = torch.full((num_pages, n_kv, page_size), float("nan"), dtype=torch.float32, device=device)
+        vsp = torch.full_like(ksp, float("nan"))
+    idx = table.to(device=device, dtype=torch.long)
+    for b in range(B):
+        kp[idx[b]] = base.k[b].reshape(n_kv, max_pages, page_size, d).transpose(0, 1)
+        vp[idx[b]] = base.v[b].reshape(n_kv, max_pages, page_size, d).transpose(0, 1)
+        if fp8:
+            ksp[idx[b]] = base.k_scale[b].reshape(n_kv, max_pages, page_size).transpose(0, 1)
+            vsp[idx[b]] = base.v_scale[b].reshape(n_kv, max_pages, page_size).transpose(0, 1)
+    if junk_unused_entries:
+        lens = base.seq_lens.cpu().tolist()
+        for b in range(B):
+            used = (min(max(int(lens[b]), 0), S) + page_size - 1) // page_size
+            table[b, used:] = -1
+    if not keep_base:  # drop the contiguous cache (q and seq_lens stay)
+        base = DecodeInputs(wl, base.q, base.k[:0], base.v[:0], base.seq_lens)
+    return PagedDecodeInputs(base, page_size, kp, vp, ksp, vsp, table.to(device))
+
+
+@dataclass
 class PrefillInputs:
     wl: PrefillWorkload
     q: torch.Tensor  # [B, S, h_q, d] bf16
