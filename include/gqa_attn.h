@@ -60,7 +60,8 @@ enum {
 typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = 1,      /* a required pointer is NULL                        */
-  GQA_ERR_SHAPE = 2,     /* a dimension <= 0, h_q % n_kv != 0, bad d_h, ...   */
+  GQA_ERR_SHAPE = 2,     /* a dimension <= 0, h_q % n_kv != 0, bad d_h or
+                            page_size, ...                                    */
   GQA_ERR_DTYPE = 3,     /* unsupported element-type combination              */
   GQA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
   GQA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
@@ -98,6 +99,11 @@ typedef enum gqa_status {
  * leaves an unnormalised partial (O_s, m_s, l_s) per head for every
  * (sequence, kv-head) it touches, and a combine kernel merges them:
  *   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+ * On the matrix-core paths the waves of a workgroup take the tiles of its
+ * range as they become free, so the float32 summation order and the point at
+ * which each wave rounds its softmax weights to bf16 can change between two
+ * identical calls: results agree to about 1e-3, not bit for bit.  The float32
+ * path has a fixed order and is bitwise reproducible.
  */
 typedef struct gqa_decode_desc {
   int32_t B, h_q, n_kv, S_max, d_h;
@@ -135,6 +141,50 @@ gqa_status attn_decode_partials(const gqa_decode_desc* d, const void* q, const v
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 gqa_status attn_decode_combine(const gqa_decode_desc* d, const int32_t* seq_lens, const void* workspace,
                                size_t workspace_bytes, void* out, hipStream_t stream);
+
+/* ------------------------------------------------------ paged decode --
+ * The decode step of attn_decode over a paged cache ("Multi-Query Attention
+ * (MQA)" glossary, "PagedAttention": each sequence's cache is cut into
+ * fixed-size pages that may lie anywhere in memory).
+ *
+ * Shapes (row-major, innermost last):
+ *   q             [B, h_q, d_h]                     q_dtype
+ *   k_pages       [num_pages, n_kv, page_size, d_h] kv_dtype -- a pool of
+ *   v_pages       [num_pages, n_kv, page_size, d_h] pages; page p holds
+ *                                                   page_size consecutive
+ *                                                   tokens of all K/V heads
+ *                                                   of one sequence
+ *   k_scale_pages [num_pages, n_kv, page_size] float32   FP8 only, else NULL
+ *   v_scale_pages [num_pages, n_kv, page_size] float32
+ *   block_table   [B, max_pages_per_seq] int32 (device): entry (b, i) is the
+ *                 page holding tokens i*page_size .. (i+1)*page_size - 1 of
+ *                 sequence b.  Only the entries of the pages covering
+ *                 positions 0 .. L_b-1 are read; an entry outside
+ *                 [0, num_pages) is clamped into the pool (no fault; the
+ *                 output is then unspecified).
+ *   seq_lens      [B] int32 (device), clamped to [0, max_pages_per_seq *
+ *                 page_size]; L_b = 0 yields a zero row.
+ *   out           [B, h_q, d_h]                     q_dtype
+ * page_size must be a power of two >= 32.  Element types, workspace and
+ * results are those of attn_decode with S_max = max_pages_per_seq *
+ * page_size: the same kernels run with one block-table lookup per 32-token
+ * tile (the entries of a range are held in registers, 64 at a time).
+ */
+typedef struct gqa_paged_desc {
+  int32_t B, h_q, n_kv, d_h;
+  int32_t q_dtype, kv_dtype;
+  int32_t page_size;         /* tokens per page: a power of two >= 32      */
+  int32_t num_pages;         /* pages in the pool                          */
+  int32_t max_pages_per_seq; /* columns of block_table                     */
+  int32_t n_split;           /* as in gqa_decode_desc                      */
+} gqa_paged_desc;
+
+int32_t attn_decode_paged_num_splits(const gqa_paged_desc* d);
+size_t attn_decode_paged_workspace_bytes(const gqa_paged_desc* d);
+gqa_status attn_decode_paged(const gqa_paged_desc* d, const void* q, const void* k_pages, const void* v_pages,
+                             const float* k_scale_pages, const float* v_scale_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, float scale, void* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------- causal prefill --
  * Causal self-attention over whole prompts, the mode of the library call

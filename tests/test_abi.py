@@ -152,3 +152,50 @@ def _load_fresh(path):
         return binding.load_library(path)
     finally:
         binding._lib = saved
+
+
+def pgd(B=2, h_q=8, n_kv=2, d=128, qt=1, kt=1, ps=64, pages=10, maxp=4, ns=0):
+    return binding.gqa_paged_desc(B, h_q, n_kv, d, qt, kt, ps, pages, maxp, ns)
+
+
+def call_paged(lib, desc, q=ALIGNED, kp=ALIGNED, vp=ALIGNED, ks=None, vs=None, table=ALIGNED, lens=ALIGNED,
+               out=ALIGNED, ws=ALIGNED, ws_bytes=None, scale=1.0):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_paged_workspace_bytes(ctypes.byref(desc)) if desc is not None else 0
+    p = ctypes.byref(desc) if desc is not None else None
+    return lib.attn_decode_paged(p, q, kp, vp, ks, vs, table, lens, scale, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(ps=16), 2), (dict(ps=48), 2), (dict(ps=0), 2), (dict(pages=0), 2), (dict(maxp=0), 2),
+    (dict(ps=1 << 21), 2), (dict(B=0), 2), (dict(h_q=12, n_kv=8), 2), (dict(d=96), 2), (dict(ns=-1), 2),
+    (dict(qt=0, kt=1), 3), (dict(qt=1, kt=0), 3),
+])
+def test_paged_descriptor_errors(lib, bad, code):
+    desc = pgd(**bad)
+    assert call_paged(lib, desc) == code
+    assert lib.attn_decode_paged_workspace_bytes(ctypes.byref(desc)) == 0
+    assert lib.attn_decode_paged_num_splits(ctypes.byref(desc)) == -1
+
+
+def test_paged_plan_matches_the_contiguous_plan(lib):
+    """A paged call plans like a contiguous one with S_max = max_pages * page_size."""
+    for ps, maxp, ns in ((32, 4, 0), (64, 64, 0), (128, 32, 7), (256, 16, 10 ** 6)):
+        p = pgd(B=16, h_q=64, n_kv=8, ps=ps, pages=999, maxp=maxp, ns=ns)
+        c = dd(B=16, h_q=64, n_kv=8, S=ps * maxp, ns=ns)
+        assert lib.attn_decode_paged_num_splits(ctypes.byref(p)) == lib.attn_decode_num_splits(ctypes.byref(c))
+        assert lib.attn_decode_paged_workspace_bytes(ctypes.byref(p)) == \
+            lib.attn_decode_workspace_bytes(ctypes.byref(c))
+
+
+def test_paged_pointer_and_value_errors(lib):
+    desc = pgd()
+    assert call_paged(lib, None) == 1
+    assert call_paged(lib, desc, table=None) == 1
+    assert call_paged(lib, desc, kp=None) == 1
+    assert call_paged(lib, desc, out=None) == 1
+    assert call_paged(lib, pgd(kt=2), ks=None, vs=None) == 1
+    assert call_paged(lib, desc, table=ALIGNED + 2) == 4
+    assert call_paged(lib, desc, vp=MISALIGNED) == 4
+    assert call_paged(lib, desc, ws_bytes=16) == 5
+    assert call_paged(lib, desc, scale=0.0) == 7

@@ -113,6 +113,10 @@ def test_single_key_returns_value_row():
 
 @pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
 def test_deterministic_repeat(kd):
+    """Repeated calls agree bitwise where the summation order is fixed: always
+    on the float32 path, and on the matrix-core paths when each wave reduces at
+    most one tile of its workgroup's range (true at this size: at most 5 tiles
+    per range, 8 waves)."""
     qd = "f32" if kd == "f32" else "bf16"
     w = wl("det", B=4, h_q=32, n_kv=4, d=128, S=2048, qd=qd, kd=kd, lens=(100, 2048), seed=47)
     inp = inputs.make_decode_inputs(w, device=DEV)
@@ -120,6 +124,20 @@ def test_deterministic_repeat(kd):
     b = pu.run_decode(inp)
     pu.sync()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_repeat_at_full_size(kd):
+    """With several tiles per wave the waves take tiles as they free up, so two
+    identical calls may differ in float32 summation order and in where each
+    wave rounds its probabilities to bf16: the outputs stay within about 1e-3
+    of each other (4e-3 allowed), far inside the accuracy bar."""
+    w = inputs.GQA_RAGGED_BF16 if kd == "bf16" else inputs.GQA_FP8KV
+    inp = inputs.make_decode_inputs(w, device=DEV)
+    a = pu.run_decode(inp).clone()
+    b = pu.run_decode(inp)
+    pu.sync()
+    assert (a.float() - b.float()).abs().max().item() <= 4e-3
 
 
 def test_partials_then_combine_equals_decode():

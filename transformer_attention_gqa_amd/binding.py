@@ -21,7 +21,8 @@ GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE", 4: "GQA_ERR_ALIGN",
           5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE"}
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
-            "attn_decode_combine", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
+            "attn_decode_combine", "attn_decode_paged_num_splits", "attn_decode_paged_workspace_bytes",
+            "attn_decode_paged", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
 
 
 class GqaError(RuntimeError):
@@ -34,6 +35,12 @@ class gqa_decode_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
                 ("S_max", ctypes.c_int32), ("d_h", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+
+
+class gqa_paged_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("n_split", ctypes.c_int32)]
 
 
 class gqa_prefill_desc(ctypes.Structure):
@@ -63,6 +70,11 @@ def load_library(path=LIB_PATH):
     lib.attn_decode_partials.restype = ctypes.c_int
     lib.attn_decode_combine.argtypes = [dd, vp, vp, sz, vp, vp]
     lib.attn_decode_combine.restype = ctypes.c_int
+    gd = ctypes.POINTER(gqa_paged_desc)
+    lib.attn_decode_paged_num_splits.argtypes, lib.attn_decode_paged_num_splits.restype = [gd], i32
+    lib.attn_decode_paged_workspace_bytes.argtypes, lib.attn_decode_paged_workspace_bytes.restype = [gd], sz
+    lib.attn_decode_paged.argtypes = [gd, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]
+    lib.attn_decode_paged.restype = ctypes.c_int
     lib.attn_prefill_causal.argtypes = [pd, vp, vp, vp, f32, vp, vp]
     lib.attn_prefill_causal.restype = ctypes.c_int
     lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [ctypes.c_int], cp
@@ -230,6 +242,76 @@ def attn_decode_combine(q, k_cache, seq_lens, workspace, out, n_split=0, stream=
     _check(load_library().attn_decode_combine(ctypes.byref(desc), _ptr(seq_lens), _ptr(workspace), ws_bytes,
                                               _ptr(out), _stream(stream)))
     return out
+
+
+def paged_desc(q, k_pages, block_table, n_split=0):
+    """Descriptor for q [B, h_q, d], pages [num_pages, n_kv, page_size, d] and block_table [B, max_pages]."""
+    B, h_q, d = q.shape
+    num_pages, n_kv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    return gqa_paged_desc(B, h_q, n_kv, d, _dtype_code(q), _dtype_code(k_pages), page_size, num_pages,
+                          block_table.shape[1], n_split)
+
+
+def attn_decode_paged_num_splits(desc):
+    return load_library().attn_decode_paged_num_splits(ctypes.byref(desc))
+
+
+def attn_decode_paged_workspace_bytes(desc):
+    return load_library().attn_decode_paged_workspace_bytes(ctypes.byref(desc))
+
+
+def _paged_checks(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale):
+    _require(q, "q", 3)
+    _require(k_pages, "k_pages", 4)
+    _require(v_pages, "v_pages", 4)
+    if k_pages.shape != v_pages.shape or k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must have the same shape and dtype")
+    if k_pages.shape[3] != q.shape[2]:
+        raise ValueError("pages [num_pages, n_kv, page_size, d] do not match q [B, h_q, d]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != q.shape[0] \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 tensor of shape [B, max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
+    if _dtype_code(k_pages) == GQA_FP8_E4M3:
+        for name, s in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if s is None or s.dtype != torch.float32 or tuple(s.shape) != tuple(k_pages.shape[:3]) \
+                    or not s.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 tensor of shape [num_pages, n_kv, page_size]")
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out=None, k_scale=None, v_scale=None,
+                      workspace=None, n_split=0, stream=None):
+    """out[B, h_q, d] = GQA decode step over a paged cache (see attn_decode_paged in gqa_attn.h)."""
+    _paged_checks(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale)
+    desc = paged_desc(q, k_pages, block_table, n_split)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(max(attn_decode_paged_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().attn_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                            _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+                                            float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def prepare_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out, workspace, k_scale=None,
+                         v_scale=None, n_split=0, stream=None):
+    """PreparedCall of attn_decode_paged."""
+    _paged_checks(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale)
+    desc = paged_desc(q, k_pages, block_table, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < attn_decode_paged_workspace_bytes(desc):
+        raise ValueError("workspace smaller than attn_decode_paged_workspace_bytes")
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_table), _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+            ctypes.c_size_t(ws_bytes))
+    call = PreparedCall(lib.attn_decode_paged, args, stream, out)
+    call._keep = (desc,)
+    return call
 
 
 def _prefill_desc(q, k, v, out):

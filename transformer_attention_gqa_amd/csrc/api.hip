@@ -111,11 +111,21 @@ gqa_status check_decode_ptrs(const gqa_decode_desc* d, const void* q, const void
   return GQA_OK;
 }
 
+// Paging of the cache for do_partials (block_table null: contiguous cache).
+struct Paging {
+  const int32_t* block_table = nullptr;
+  int page_shift = 0, max_pages = 0, num_pages = 0;
+};
+
 gqa_status do_partials(const gqa_decode_desc* d, const DecodePlan& p, const void* q, const void* k, const void* v,
                        const float* ks, const float* vs, const int32_t* seq_lens, float scale, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const Paging& pg = Paging()) {
   const WorkspaceLayout wl = workspace_layout(d, p);
   DecodeArgs a;
+  a.block_table = pg.block_table;
+  a.page_shift = pg.page_shift;
+  a.max_pages = pg.max_pages;
+  a.num_pages = pg.num_pages;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -161,6 +171,24 @@ gqa_status do_combine(const gqa_decode_desc* d, const DecodePlan& p, const int32
     return GQA_ERR_HIP;
   }
   return GQA_OK;
+}
+
+// Paged decode: checks the paged descriptor and maps it onto the contiguous
+// one (S_max = max_pages * page_size), which fixes the plan and workspace.
+gqa_status paged_to_decode_desc(const gqa_paged_desc* pd, gqa_decode_desc* d, int* page_shift) {
+  if (!pd) return GQA_ERR_NULL;
+  const int ps = pd->page_size;
+  if (ps < 32 || ps > (1 << 20) || (ps & (ps - 1)) != 0) return GQA_ERR_SHAPE;
+  if (pd->num_pages <= 0 || pd->max_pages_per_seq <= 0) return GQA_ERR_SHAPE;
+  if ((int64_t)pd->max_pages_per_seq * ps > (int64_t)1 << 30) return GQA_ERR_SHAPE;
+  if ((int64_t)pd->B * pd->max_pages_per_seq > (int64_t)1 << 31) return GQA_ERR_SHAPE;
+  if ((int64_t)pd->num_pages * pd->n_kv * ps > (int64_t)1 << 40) return GQA_ERR_SHAPE;
+  *d = gqa_decode_desc{pd->B, pd->h_q, pd->n_kv, pd->max_pages_per_seq * ps, pd->d_h, pd->q_dtype, pd->kv_dtype,
+                       pd->n_split};
+  int sh = 0;
+  while ((1 << sh) < ps) ++sh;
+  *page_shift = sh;
+  return validate_decode_desc(d);
 }
 
 }  // namespace
@@ -221,6 +249,46 @@ gqa_status attn_decode(const gqa_decode_desc* d, const void* q, const void* k_ca
   if (!workspace || workspace_bytes < workspace_layout(d, p).total) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
   st = do_partials(d, p, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, workspace, stream);
+  if (st != GQA_OK) return st;
+  return do_combine(d, p, seq_lens, workspace, out, stream);
+}
+
+int32_t attn_decode_paged_num_splits(const gqa_paged_desc* pd) {
+  gqa_decode_desc d;
+  int sh;
+  if (paged_to_decode_desc(pd, &d, &sh) != GQA_OK) return -1;
+  return plan_decode(&d).W;
+}
+
+size_t attn_decode_paged_workspace_bytes(const gqa_paged_desc* pd) {
+  gqa_decode_desc d;
+  int sh;
+  if (paged_to_decode_desc(pd, &d, &sh) != GQA_OK) return 0;
+  return workspace_layout(&d, plan_decode(&d)).total;
+}
+
+gqa_status attn_decode_paged(const gqa_paged_desc* pd, const void* q, const void* k_pages, const void* v_pages,
+                             const float* k_scale_pages, const float* v_scale_pages, const int32_t* block_table,
+                             const int32_t* seq_lens, float scale, void* out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  gqa_decode_desc dd;
+  Paging pg;
+  gqa_status st = paged_to_decode_desc(pd, &dd, &pg.page_shift);
+  if (st != GQA_OK) return st;
+  const gqa_decode_desc* d = &dd;
+  st = check_decode_ptrs(d, q, k_pages, v_pages, k_scale_pages, v_scale_pages, seq_lens);
+  if (st != GQA_OK) return st;
+  if (!out || !block_table) return GQA_ERR_NULL;
+  if (misaligned(out)) return GQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0) return GQA_ERR_ALIGN;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
+  const DecodePlan p = plan_decode(d);
+  if (!workspace || workspace_bytes < workspace_layout(d, p).total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+  pg.block_table = block_table;
+  pg.max_pages = pd->max_pages_per_seq;
+  pg.num_pages = pd->num_pages;
+  st = do_partials(d, p, q, k_pages, v_pages, k_scale_pages, v_scale_pages, seq_lens, scale, workspace, stream, pg);
   if (st != GQA_OK) return st;
   return do_combine(d, p, seq_lens, workspace, out, stream);
 }

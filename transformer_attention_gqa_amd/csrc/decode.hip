@@ -166,11 +166,40 @@ struct Segment {
   int ntile;           // tiles of the segment
   int t_begin, t_end;  // token range [t_begin, t_end) inside the sequence
   int nh, head0;       // heads served and the global index of the first
-  size_t slab;         // cache row of token 0 of (b, g)
+  size_t slab;         // contiguous cache: cache row of token 0 of (b, g)
   long long slot;      // partial slot
+  int pwin;            // paged cache: first logical page of the block-table window ...
+  int pg;              // ... whose entry pwin + lane this lane holds (a VGPR)
 };
 
-template <int TILE>
+// Paged cache: lane i returns the physical page of logical page lp0 + i of
+// sequence b (0 past the table's width), clamped into the pool so that a bad
+// entry cannot address memory outside it.
+__device__ __forceinline__ int load_page_window(const DecodeArgs& a, int b, int lp0, int lane) {
+  const int lp = lp0 + lane;
+  const int p = lp < a.max_pages ? a.block_table[(size_t)b * a.max_pages + lp] : 0;
+  return min(max(p, 0), a.num_pages - 1);
+}
+
+// Cache row (in rows of d_h elements) of token t of segment s.  Paged: the
+// page comes from the segment's block-table window, refilled (one load) when
+// t lies past its 64 pages; rows never cross a page inside a 32-token tile.
+template <bool PAGED>
+__device__ __forceinline__ size_t cache_row(const DecodeArgs& a, Segment& s, int t, int lane) {
+  if constexpr (PAGED) {
+    const int lp = t >> a.page_shift;
+    if (lp - s.pwin >= 64) {  // wave-uniform
+      s.pwin = lp;
+      s.pg = load_page_window(a, s.b, lp, lane);
+    }
+    const int page = __builtin_amdgcn_readlane(s.pg, lp - s.pwin);
+    return ((((size_t)page * a.n_kv + s.g) << a.page_shift) | (size_t)(t & ((1 << a.page_shift) - 1)));
+  } else {
+    return s.slab + t;
+  }
+}
+
+template <int TILE, bool PAGED>
 __device__ __forceinline__ Segment make_segment(const DecodeArgs& a, const LaneLens& ll, long long t, long long hi,
                                                 int w, int spb, int hpc, int lane) {
   int b, nt, L;
@@ -195,10 +224,16 @@ __device__ __forceinline__ Segment make_segment(const DecodeArgs& a, const LaneL
   s.head0 = s.g * G + s.hc * hpc;
   s.slab = ((size_t)b * a.n_kv + s.g) * (size_t)a.S_max;
   s.slot = w + (long long)b * spb + slab_in_b;
+  s.pwin = 0;
+  s.pg = 0;
+  if constexpr (PAGED) {
+    s.pwin = s.t_begin >> a.page_shift;
+    s.pg = load_page_window(a, b, s.pwin, lane);
+  }
   return s;
 }
 
-template <int D, int HB, bool FP8, int NW>
+template <int D, int HB, bool FP8, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   constexpr int CH = D / 8;   // 16-byte bf16 chunks per row
   constexpr int KK = D / 32;  // k-steps of the score product
@@ -254,19 +289,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   float ksc[2][4], vsc[2][4];
 
   // loads of tile `tile` of segment s into kreg/vreg (and its fp8 scales).
-  // Branch-free: rows past the segment end re-read its last row (in bounds)
-  // and are zeroed at staging, so no NaN of a cache tail reaches the MFMA.
-  // loads of tile `tile` of segment s into kreg/vreg (and its fp8 scales).
   // A full tile is addressed as a wave-uniform base plus a per-lane constant;
   // the segment's last tile re-reads its last valid row for the rows past the
   // end (in bounds), which staging then zeroes, so no NaN of a cache tail can
   // reach the matrix cores.
   constexpr int ROWB = FP8 ? D : 2 * D;  // bytes per cache row
   const int lane_off = ld_row * ROWB + ld_chunk * 16;
-  auto issue_loads = [&](const Segment& s, int tile) {
+  auto issue_loads = [&](Segment& s, int tile) {
     const int tt0 = s.t_begin + tile * kTile;
-    const char* kb = static_cast<const char*>(a.k) + (s.slab + tt0) * ROWB;
-    const char* vb = static_cast<const char*>(a.v) + (s.slab + tt0) * ROWB;
+    const size_t row0 = cache_row<PAGED>(a, s, tt0, lane);
+    const char* kb = static_cast<const char*>(a.k) + row0 * ROWB;
+    const char* vb = static_cast<const char*>(a.v) + row0 * ROWB;
     if (tt0 + kTile <= s.t_end) {
 #pragma unroll
       for (int u = 0; u < NLD; ++u) {
@@ -283,8 +316,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       }
     }
     if constexpr (FP8) {
-      const float* ksb = a.k_scale + s.slab + tt0;
-      const float* vsb = a.v_scale + s.slab + tt0;
+      const float* ksb = a.k_scale + row0;
+      const float* vsb = a.v_scale + row0;
       const int nvalid = s.t_end - tt0;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -331,7 +364,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     return uniform(__shfl(v, 0, 64));
   };
 
-  Segment cur = make_segment<kTile>(a, ll, lo, hi, w, spb, HPC, lane);
+  Segment cur = make_segment<kTile, PAGED>(a, ll, lo, hi, w, spb, HPC, lane);
   if (wave < cur.ntile) issue_loads(cur, wave);
   wave_lds_fence();
   store_q(load_q(cur));
@@ -343,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     Segment nxt = cur;
     QRows q_next = {};
     if (has_next) {
-      nxt = make_segment<kTile>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
+      nxt = make_segment<kTile, PAGED>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
       q_next = load_q(nxt);  // used at the segment switch, long after it lands
     }
     const int t_begin = cur.t_begin, t_end = cur.t_end;
@@ -654,7 +687,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 // 64-token tiles: one token per lane for the scores, one d column per lane
 // for the PV product).
 // ------------------------------------------------------------------------
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
   constexpr int HPC = 16;
   constexpr int NW = kWavesF32;
@@ -716,11 +749,20 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
       const int tt0 = t_begin + tile * kTileF32;
       const int tok = tt0 + lane;
       const bool valid = tok < t_end;
+      // cache row of this lane's token (the segment's last one past the end);
+      // paged: one block-table lookup per lane
+      size_t row = slab + min(tok, t_end - 1);
+      if constexpr (PAGED) {
+        const int tc = min(tok, t_end - 1);
+        int page = a.block_table[(size_t)b * a.max_pages + (tc >> a.page_shift)];
+        page = min(max(page, 0), a.num_pages - 1);
+        row = (((size_t)page * a.n_kv + g) << a.page_shift) | (size_t)(tc & ((1 << a.page_shift) - 1));
+      }
       float sc[HPC];
 #pragma unroll
       for (int h = 0; h < HPC; ++h) sc[h] = 0.f;
       if (valid) {
-        const float4* kr = reinterpret_cast<const float4*>(kg + (slab + tok) * D);
+        const float4* kr = reinterpret_cast<const float4*>(kg + row * D);
 #pragma unroll
         for (int d4 = 0; d4 < D / 4; ++d4) {
           const float4 kv = kr[d4];
@@ -762,7 +804,10 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
         float vv[U][DL];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float* vr = vg + (slab + tt0 + min(tt + u, nvalid - 1)) * D;
+          const int src = min(tt + u, nvalid - 1);  // a lane of this tile (uniform)
+          const size_t vrow = ((size_t)(uint32_t)__builtin_amdgcn_readlane((int)(row >> 32), src) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)row, src);
+          const float* vr = vg + vrow * D;
 #pragma unroll
           for (int c = 0; c < DL; ++c) vv[u][c] = vr[lane + 64 * c];
         }
@@ -913,17 +958,18 @@ __global__ __launch_bounds__(256) void gqa_decode_combine(CombineArgs c) {
 // ------------------------------------------------------------------------
 constexpr int kWavesMfma = 8;
 
-hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream) {
+template <bool PAGED>
+static void launch_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream) {
   const dim3 grid(W);
   if (kind == 0) {
     const dim3 block(kWavesF32 * 64);
-    if (D == 64) hipLaunchKernelGGL(gqa_decode_split_f32<64>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(gqa_decode_split_f32<128>, grid, block, 0, stream, a);
-    return hipGetLastError();
+    if (D == 64) hipLaunchKernelGGL((gqa_decode_split_f32<64, PAGED>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gqa_decode_split_f32<128, PAGED>), grid, block, 0, stream, a);
+    return;
   }
   const dim3 block(kWavesMfma * 64);
 #define GQA_LAUNCH_DECODE(DD, HH, F8) \
-  hipLaunchKernelGGL((gqa_decode_split_mfma<DD, HH, F8, kWavesMfma>), grid, block, 0, stream, a)
+  hipLaunchKernelGGL((gqa_decode_split_mfma<DD, HH, F8, kWavesMfma, PAGED>), grid, block, 0, stream, a)
   const bool fp8 = kind == 2;
   if (D == 64) {
     if (hb == 1) { if (fp8) GQA_LAUNCH_DECODE(64, 1, true); else GQA_LAUNCH_DECODE(64, 1, false); }
@@ -933,6 +979,11 @@ hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int
     else { if (fp8) GQA_LAUNCH_DECODE(128, 2, true); else GQA_LAUNCH_DECODE(128, 2, false); }
   }
 #undef GQA_LAUNCH_DECODE
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream) {
+  if (a.block_table) launch_split<true>(a, D, hb, kind, W, stream);
+  else launch_split<false>(a, D, hb, kind, W, stream);
   return hipGetLastError();
 }
 

@@ -25,6 +25,12 @@ struct DecodeArgs {
   const float* k_scale;
   const float* v_scale;
   const int32_t* seq_lens;
+  // paged cache (block_table != null): k/v (and the fp8 scales) are a pool of
+  // pages [num_pages][n_kv][page_size][...], page_size = 1 << page_shift, and
+  // token t of sequence b lives in page block_table[b * max_pages + t / page_size];
+  // S_max is then max_pages * page_size
+  const int32_t* block_table;
+  int page_shift, max_pages, num_pages;
   float* part_o;   // [W + n_slabs][heads_per_chunk][D]
   float* part_ml;  // [W + n_slabs][heads_per_chunk][2]: running max (log2 domain), running sum
   float qk_scale_log2;
