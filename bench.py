@@ -209,6 +209,61 @@ def bench_decode(wl, steps, warmup, use_graph=False, n_split=0):
     }
 
 
+def bench_decode_paged(pwl, steps, warmup, use_graph=False):
+    """attn_decode_paged over a decode workload whose cache is scattered over a
+    page pool in a seeded random order.  Algorithmic bytes are those of the
+    contiguous workload (the visible K/V rows); the block-table reads (4 bytes
+    per page per (sequence, kv-head) range) are not counted."""
+    wl = pwl.base
+    dev = torch.device("cuda")
+    x = inputs.make_paged_decode_inputs(wl, pwl.page_size, device=dev, keep_base=False)
+    b = x.base
+    lens = b.seq_lens.cpu().tolist()
+    kv_bytes = roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens)
+    pool_bytes = x.k_pages.numel() * x.k_pages.element_size() * 2
+    ncopies = min(16, max(2, math.ceil(4 * MALL_BYTES / pool_bytes) + 1))
+    kps, vps = [x.k_pages], [x.v_pages]
+    for _ in range(ncopies - 1):
+        kps.append(x.k_pages.clone())
+        vps.append(x.v_pages.clone())
+    desc = binding.paged_desc(b.q, x.k_pages, x.block_table)
+    n_split = binding.attn_decode_paged_num_splits(desc)
+    ws = torch.empty(binding.attn_decode_paged_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(b.q)
+    calls = [binding.prepare_decode_paged(b.q, kps[c], vps[c], x.block_table, b.seq_lens, wl.scale, out, ws)
+             for c in range(ncopies)]
+
+    def step(i):
+        calls[i % ncopies]()
+
+    ms_step, ev_ms = time_steps(step, steps, warmup, use_graph)
+    key = f"decode_split_paged_{wl.kv_dtype}:{pwl.name}"
+    # a step is split + combine; the combine's share is taken from the
+    # contiguous workload's launches of the same grid in the kernel trace
+    achieved_step = kv_bytes / (ev_ms * 1e-3) / 1e9
+    return {
+        "workload": pwl.name,
+        "value": kv_bytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "ms_per_step": ms_step,
+        "pct_hbm_peak": 100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / roofline.HBM_PEAK_GBPS,
+        "kv_bytes": kv_bytes,
+        "sum_L": int(sum(lens)),
+        "page_size": pwl.page_size,
+        "num_pages": int(x.k_pages.shape[0]),
+        "n_split": n_split,
+        "kv_copies_rotated": ncopies,
+        "event_ms_per_step": ev_ms,
+        "roofline": {"bound": "hbm", "kernel": "gqa_decode_split_mfma (paged) + gqa_decode_combine",
+                     "achieved": achieved_step, "peak": roofline.HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved_step / roofline.HBM_PEAK_GBPS, "traffic": measured_traffic(key)},
+        "dtype": wl.kv_dtype,
+        "config": {"workload": pwl.name, "B": wl.B, "h_q": wl.h_q, "n_kv": wl.n_kv, "d_h": wl.d_h,
+                   "S_max": wl.S_max, "page_size": pwl.page_size, "q_dtype": wl.q_dtype,
+                   "kv_dtype": wl.kv_dtype, "seed": wl.seed},
+    }
+
+
 def bench_prefill(wl, steps, warmup, use_graph=False):
     dev = torch.device("cuda")
     x = inputs.make_prefill_inputs(wl, device=dev)
@@ -329,14 +384,30 @@ def _workload_launches():
         key = f"decode_split_{wl.kv_dtype}:{wl.name}"
         hpc = 16 if (wl.kv_dtype == "f32" or G <= 16) else 32
         if wl.kv_dtype == "f32":
-            out.append((("gqa_decode_split_f32", (str(wl.d_h),), ns * 256), (key, wl.name, kv, "bytes")))
+            out.append((("gqa_decode_split_f32", (str(wl.d_h), "false"), ns * 256), (key, wl.name, kv, "bytes")))
         else:
-            targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8")
+            targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8", "false")
             out.append((("gqa_decode_split_mfma", targs, ns * 512), (key, wl.name, kv, "bytes")))
         n_slabs = wl.B * wl.n_kv * -(-G // hpc)
         grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
         targs = (str(wl.d_h), "false" if wl.q_dtype == "f32" else "true")
         out.append((("gqa_decode_combine", targs, grid), (f"decode_combine:{wl.name}", wl.name, None, None)))
+    for pwl in inputs.PAGED_WORKLOADS.values():
+        wl = pwl.base
+        G = wl.h_q // wl.n_kv
+        hpc = 16 if G <= 16 else 32
+        qd = torch.empty((wl.B, wl.h_q, wl.d_h), dtype=torch.bfloat16, device="meta")
+        kd = torch.empty((wl.B, wl.n_kv, wl.S_max, wl.d_h), dtype=torch.bfloat16, device="meta")
+        ns = binding.attn_decode_num_splits(binding.decode_desc(qd, kd))
+        lens = inputs.draw_lengths(wl.B, *wl.lens, wl.seed).tolist()
+        kv = roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens)
+        targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8", "true")
+        out.append((("gqa_decode_split_mfma", targs, ns * 512),
+                    (f"decode_split_paged_{wl.kv_dtype}:{pwl.name}", pwl.name, kv, "bytes")))
+        n_slabs = wl.B * wl.n_kv * -(-G // hpc)
+        grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
+        out.append((("gqa_decode_combine", (str(wl.d_h), "true"), grid),
+                    (f"decode_combine:{pwl.name}", pwl.name, None, None)))
     for wl in inputs.PREFILL_WORKLOADS.values():
         G = wl.h_q // wl.n_kv
         hc = math.gcd(G, 8)
@@ -473,7 +544,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=MAIN, choices=sorted(inputs.DECODE_WORKLOADS) + sorted(
-        inputs.PREFILL_WORKLOADS))
+        inputs.PAGED_WORKLOADS) + sorted(inputs.PREFILL_WORKLOADS))
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -509,12 +580,14 @@ def main(argv=None):
         precondition_gpu()
         if name in inputs.PREFILL_WORKLOADS:
             return bench_prefill(inputs.PREFILL_WORKLOADS[name], steps, warmup, use_graph)
+        if name in inputs.PAGED_WORKLOADS:
+            return bench_decode_paged(inputs.PAGED_WORKLOADS[name], steps, warmup, use_graph)
         return bench_decode(inputs.DECODE_WORKLOADS[name], steps, warmup, use_graph, args.n_split)
 
     main_res = run(args.workload, args.steps, args.warmup)
     others = {}
     if not args.only_main:
-        for name in list(inputs.DECODE_WORKLOADS) + list(inputs.PREFILL_WORKLOADS):
+        for name in list(inputs.DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS) + list(inputs.PREFILL_WORKLOADS):
             if name == args.workload:
                 continue
             others[name] = run(name, max(5, min(args.steps, 20)), 2)

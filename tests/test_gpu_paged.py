@@ -68,6 +68,17 @@ def test_paged_group_sizes(G, d):
         check(pin)
 
 
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_paged_shared_prefix_pages(kd):
+    """Sequences 1 and 2 reuse sequence 0's first pages (a shared prompt
+    prefix): several table rows name the same physical pages."""
+    w = wl(B=4, h_q=32, n_kv=4, d=128, S=512, kd=kd, seed=233)
+    pin = inputs.make_paged_decode_inputs(w, 32, device=DEV, seq_lens=[512, 400, 97, 250], poison_tail=True)
+    pin.block_table[1, :5] = pin.block_table[0, :5]
+    pin.block_table[2, :3] = pin.block_table[0, :3]
+    check(pin)
+
+
 @pytest.mark.parametrize("n_split", [1, 7, 10 ** 6])
 def test_paged_forced_splits(n_split):
     w = wl(B=3, h_q=16, n_kv=2, d=128, S=384, kd="bf16", seed=211)

@@ -109,3 +109,20 @@ def test_paged_input_generator_scatters_the_contiguous_cache(kd):
                 assert torch.equal(pin.k_scale_pages[p], base.k_scale[b, :, 32 * i:32 * (i + 1)])
     used_pages = {int(x) for x in pin.block_table.flatten() if x >= 0}
     assert len(used_pages) == sum((n + 31) // 32 for n in lens)
+
+
+def test_sequences_sharing_a_prefix_page_read_it_each():
+    """Two sequences whose tables name the same first page (a shared prompt
+    prefix) each attend to it: equal to contiguous caches that both hold a copy."""
+    ps, n_kv, d = 4, 2, 3
+    shared_k, shared_v = _rand(n_kv, ps, d, seed=12), _rand(n_kv, ps, d, seed=13)
+    tail_k, tail_v = _rand(2, n_kv, ps, d, seed=14), _rand(2, n_kv, ps, d, seed=15)
+    kp = np.stack([shared_k, tail_k[0], tail_k[1]])
+    vp = np.stack([shared_v, tail_v[0], tail_v[1]])
+    table = np.array([[0, 1], [0, 2]])
+    q = _rand(2, 4, d, seed=16)
+    lens = [7, 6]
+    k = np.stack([np.concatenate([shared_k, tail_k[b]], axis=1) for b in range(2)])
+    v = np.stack([np.concatenate([shared_v, tail_v[b]], axis=1) for b in range(2)])
+    got = oracle.decode_paged(q, kp, vp, table, lens, 0.5, ps)
+    assert np.array_equal(got, oracle.decode(q, k, v, lens, 0.5))

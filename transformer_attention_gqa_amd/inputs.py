@@ -87,6 +87,19 @@ DECODE_WORKLOADS = {w.name: w for w in (MQA_TINY_F32, GQA_RAGGED_BF16, MQA_LONG_
 PREFILL_WORKLOADS = {GQA_PREFILL_BF16.name: GQA_PREFILL_BF16}
 
 
+@dataclass(frozen=True)
+class PagedDecodeWorkload:
+    """A decode workload whose cache lives in a pool of fixed-size pages."""
+    name: str
+    base: DecodeWorkload
+    page_size: int
+
+
+# The ragged GQA decode with its cache in 64-token pages scattered over the pool.
+GQA_RAGGED_BF16_PAGED64 = PagedDecodeWorkload("gqa_decode_ragged_bf16_paged64", GQA_RAGGED_BF16, 64)
+PAGED_WORKLOADS = {GQA_RAGGED_BF16_PAGED64.name: GQA_RAGGED_BF16_PAGED64}
+
+
 def _torch_dtype(tag):
     return {"f32": torch.float32, "bf16": torch.bfloat16}[tag]
 
