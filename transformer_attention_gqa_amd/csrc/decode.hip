@@ -289,43 +289,34 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   float ksc[2][4], vsc[2][4];
 
   // loads of tile `tile` of segment s into kreg/vreg (and its fp8 scales).
-  // A full tile is addressed as a wave-uniform base plus a per-lane constant;
-  // the segment's last tile re-reads its last valid row for the rows past the
-  // end (in bounds), which staging then zeroes, so no NaN of a cache tail can
-  // reach the matrix cores.
+  // The tile's first row is wave-uniform: it becomes the base of a buffer
+  // resource whose range ends at the segment's last valid row, so rows past
+  // the end read as zero without a memory access (a cache tail may hold NaN)
+  // and each load needs only a 32-bit lane offset.
   constexpr int ROWB = FP8 ? D : 2 * D;  // bytes per cache row
-  const int lane_off = ld_row * ROWB + ld_chunk * 16;
+  const unsigned lane_off = ld_row * ROWB + ld_chunk * 16;
   auto issue_loads = [&](Segment& s, int tile) {
     const int tt0 = s.t_begin + tile * kTile;
-    const size_t row0 = cache_row<PAGED>(a, s, tt0, lane);
-    const char* kb = static_cast<const char*>(a.k) + row0 * ROWB;
-    const char* vb = static_cast<const char*>(a.v) + row0 * ROWB;
-    if (tt0 + kTile <= s.t_end) {
+    const size_t row0 = (size_t)uniform((long long)cache_row<PAGED>(a, s, tt0, lane));
+    const int nvalid = uniform(min(kTile, s.t_end - tt0));
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + row0 * ROWB, nvalid * ROWB);
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + row0 * ROWB, nvalid * ROWB);
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        kreg[u] = load_nt(kb + lane_off + u * RPL * ROWB);
-        vreg[u] = load_nt(vb + lane_off + u * RPL * ROWB);
-      }
-    } else {
-      const int last = s.t_end - 1 - tt0;
-#pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int off = min(u * RPL + ld_row, last) * ROWB + ld_chunk * 16;
-        kreg[u] = load_nt(kb + off);
-        vreg[u] = load_nt(vb + off);
-      }
+    for (int u = 0; u < NLD; ++u) {
+      kreg[u] = buffer_load_x4_nt(rk, lane_off + u * RPL * ROWB);
+      vreg[u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
     }
     if constexpr (FP8) {
-      const float* ksb = a.k_scale + row0;
-      const float* vsb = a.v_scale + row0;
-      const int nvalid = s.t_end - tt0;
+      // lane (q4, .) needs the scales of rows 16h + 4q4 + i; rows past the end
+      // read zero, and their scores are masked anyway
+      const auto rks = make_rsrc(a.k_scale + row0, nvalid * 4);
+      const auto rvs = make_rsrc(a.v_scale + row0, nvalid * 4);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * h + 4 * q4 + i;
-          ksc[h][i] = r < nvalid ? ksb[r] : 0.f;
-          vsc[h][i] = r < nvalid ? vsb[r] : 0.f;
+          ksc[h][i] = buffer_load_f32(rks, 16 * q4 + 4 * (16 * h + i));
+          vsc[h][i] = buffer_load_f32(rvs, 16 * q4 + 4 * (16 * h + i));
         }
     }
   };
@@ -354,32 +345,88 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     }
   };
 
-  // Tiles of a segment are handed out dynamically: wave i starts with tile i,
-  // then claims the next unclaimed one from an LDS counter, so waves whose
-  // loads are served faster take more tiles and all reach the segment's merge
-  // at about the same time.
+  // Further tiles of a segment (after each wave's first two) are claimed
+  // from an LDS counter, so waves whose loads are served faster take more
+  // tiles and all reach the segment's merge at about the same time.
   auto claim_tile = [&]() {
     int v = 0;
     if (lane == 0) v = atomicAdd(&s_next_tile, 1);
     return uniform(__shfl(v, 0, 64));
   };
 
+  // Stage the tile whose loads were issued last into the wave's LDS slab and
+  // take over its fp8 scales.
+  float kscur[2][4], vscur[2][4];
+  auto stage = [&]() {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kscur[h][i] = ksc[h][i];
+          vscur[h][i] = vsc[h][i];
+        }
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int r = u * RPL + ld_row;
+      if constexpr (FP8) {
+        // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
+        const int c0 = 2 * ld_chunk;
+        u32x2 t0 = e4m3x4_to_bf16x4(kreg[u][0]), t1 = e4m3x4_to_bf16x4(kreg[u][1]);
+        u32x2 t2 = e4m3x4_to_bf16x4(kreg[u][2]), t3 = e4m3x4_to_bf16x4(kreg[u][3]);
+        const u32x4 klo = u32x4{t0[0], t0[1], t1[0], t1[1]};
+        const u32x4 khi = u32x4{t2[0], t2[1], t3[0], t3[1]};
+        t0 = e4m3x4_to_bf16x4(vreg[u][0]);
+        t1 = e4m3x4_to_bf16x4(vreg[u][1]);
+        t2 = e4m3x4_to_bf16x4(vreg[u][2]);
+        t3 = e4m3x4_to_bf16x4(vreg[u][3]);
+        const u32x4 vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
+        const u32x4 vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
+        const int sw = swz<CH>(r);
+        lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), klo);
+        lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
+        lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
+        lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
+      } else {
+        const int pc = ld_chunk ^ swz<CH>(r);
+        lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
+        lds_store(vt + r * (2 * D) + (pc << 4), vreg[u]);
+      }
+    }
+    wave_lds_fence();
+  };
+
   Segment cur = make_segment<kTile, PAGED>(a, ll, lo, hi, w, spb, HPC, lane);
+  QRows qc = load_q(cur);
+  wave_lds_fence();  // the first tile's loads go out after the query rows'
   if (wave < cur.ntile) issue_loads(cur, wave);
-  wave_lds_fence();
-  store_q(load_q(cur));
-  if (threadIdx.x == 0) s_next_tile = NW;
-  __syncthreads();
 
   for (;;) {
     const bool has_next = lo + cur.ntile < hi;
     Segment nxt = cur;
-    QRows q_next = {};
-    if (has_next) {
-      nxt = make_segment<kTile, PAGED>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
-      q_next = load_q(nxt);  // used at the segment switch, long after it lands
-    }
+    if (has_next) nxt = make_segment<kTile, PAGED>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
     const int t_begin = cur.t_begin, t_end = cur.t_end;
+
+    // ---- prologue: wave i takes tiles i and i + NW.  It stages the first and
+    // puts the second (or its first tile of the next segment) in flight before
+    // the workgroup waits for the segment's query rows, so that no wave's
+    // second load waits for the slowest wave's first: at kernel start every
+    // wave's first load is queued behind the whole chip's first burst.
+    int tile = wave, next_tile = wave + NW;
+    if (tile < cur.ntile) {
+      stage();
+      if (next_tile < cur.ntile) issue_loads(cur, next_tile);
+      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
+    } else if (has_next && wave < nxt.ntile) {
+      issue_loads(nxt, wave);
+    }
+    QRows q_next = {};
+    if (has_next) q_next = load_q(nxt);  // used at the segment switch, long after it lands
+    store_q(qc);
+    if (threadIdx.x == 0) s_next_tile = 2 * NW;
+    __syncthreads();  // sq and the tile counter ready
 
     // ---- running state (per lane: head r16 of every head block; head l32 in the 32x32 shape)
     f32x4 o[M32 ? 1 : HB][M32 ? 1 : NT];
@@ -402,58 +449,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         for (int n = 0; n < NT; ++n) o[hb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int tile = wave; tile < cur.ntile;) {
-      float kscur[2][4], vscur[2][4];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            kscur[h][i] = ksc[h][i];
-            vscur[h][i] = vsc[h][i];
-          }
-      }
+    // ---- compute the staged tile, then stage the one in flight and put the
+    // wave's next tile (of this segment, else its first of the next) in flight
+    while (tile < cur.ntile) {
       const int tt0 = t_begin + tile * kTile;
-      wave_lds_fence();
-      // ---- stage the landed tile into the wave's LDS slab
-#pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int r = u * RPL + ld_row;
-        if (tt0 + r >= t_end) {  // past the segment end: zero (a cache tail may hold NaN)
-          kreg[u] = u32x4{0u, 0u, 0u, 0u};
-          vreg[u] = u32x4{0u, 0u, 0u, 0u};
-        }
-        if constexpr (FP8) {
-          // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
-          const int c0 = 2 * ld_chunk;
-          u32x2 t0 = e4m3x4_to_bf16x4(kreg[u][0]), t1 = e4m3x4_to_bf16x4(kreg[u][1]);
-          u32x2 t2 = e4m3x4_to_bf16x4(kreg[u][2]), t3 = e4m3x4_to_bf16x4(kreg[u][3]);
-          const u32x4 klo = u32x4{t0[0], t0[1], t1[0], t1[1]};
-          const u32x4 khi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-          t0 = e4m3x4_to_bf16x4(vreg[u][0]);
-          t1 = e4m3x4_to_bf16x4(vreg[u][1]);
-          t2 = e4m3x4_to_bf16x4(vreg[u][2]);
-          t3 = e4m3x4_to_bf16x4(vreg[u][3]);
-          const u32x4 vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
-          const u32x4 vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-          const int sw = swz<CH>(r);
-          lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), klo);
-          lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
-          lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
-          lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
-        } else {
-          const int pc = ld_chunk ^ swz<CH>(r);
-          lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
-          lds_store(vt + r * (2 * D) + (pc << 4), vreg[u]);
-        }
-      }
-      wave_lds_fence();
-      // ---- keep one tile in flight: the next claimed tile of this segment, or
-      // this wave's first tile of the next segment
-      const int next_tile = claim_tile();
-      if (next_tile < cur.ntile) issue_loads(cur, next_tile);
-      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
-
       if constexpr (M32) {
         const int l32 = lane & 31, h2 = lane >> 5;
         // ---- S^T[32 tokens][32 heads] = K Q^T: lane holds tokens 8(r/4)+4h2+r%4 of head l32
@@ -605,9 +604,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         }
       }
       tile = next_tile;
+      if (tile >= cur.ntile) break;
+      stage();
+      next_tile = claim_tile();
+      if (next_tile < cur.ntile) issue_loads(cur, next_tile);
+      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
     }
-    // a wave with no tile in this segment starts its next-segment tile now
-    if (wave >= cur.ntile && has_next && wave < nxt.ntile) issue_loads(nxt, wave);
 
     // ---- merge the waves of the workgroup, write one partial per head
     wave_lds_fence();
@@ -674,9 +676,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       }
     }
     if (!has_next) break;
-    store_q(q_next);  // sq is not read by the merge
-    if (threadIdx.x == 0) s_next_tile = NW;  // every wave is past its last claim
-    __syncthreads();  // slabs, sq and the tile counter ready for the next segment
+    qc = q_next;
+    __syncthreads();  // the merge's reads of the slabs are done before the next prologue stages into them
     lo += cur.ntile;
     cur = nxt;
   }

@@ -111,4 +111,24 @@ __device__ __forceinline__ u32x4 load_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Raw buffer access (gfx9 buffer resource: base address, byte range, and the
+// third-dword format word for 32-bit untyped data).  The base is wave-uniform
+// and lives in scalar registers, so each load needs only a 32-bit lane offset;
+// a load whose offset (lane offset + immediate) is at or past `bytes` returns
+// zero without touching memory.
+constexpr int kBufferFormatWord = 0x00020000;
+constexpr int kCacheNonTemporal = 2;  // cache-policy operand: nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFormatWord);
+}
+
+__device__ __forceinline__ u32x4 buffer_load_x4_nt(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNonTemporal));
+}
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 }  // namespace gqa
