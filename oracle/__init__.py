@@ -20,10 +20,11 @@ Sources (page title, then section):
   * "Multi-query attention" (learn.pranaymahendrakar.com) -- "Formulation"
     (O_i = softmax(Q_i K^T / sqrt(d_h)) V with one shared K/V head).
   * "Multi-Query Attention (MQA)" glossary (inferensys.com) -- "KV cache
-    quantization" (FP8 cache with scaling factors).
+    quantization" (FP8 / INT8 / INT4 cache with scaling factors).
 
 Modules:
-  codecs     -- stored-value decoders (bf16 bit patterns, OCP e4m3fn codes).
+  codecs     -- stored-value decoders (bf16 bit patterns, OCP e4m3fn codes,
+                int8 and packed int4 codes).
   attention  -- the decode and causal-prefill definitions.
   paged      -- decode over a paged cache ("Multi-Query Attention (MQA)"
                 glossary, "PagedAttention").
@@ -42,5 +43,12 @@ from .attention import (  # noqa: F401
     prefill_causal,
     prefill_rows,
 )
-from .codecs import bf16_bits_to_f64, dequantize_fp8_cache, e4m3fn_to_f64  # noqa: F401
+from .codecs import (  # noqa: F401
+    bf16_bits_to_f64,
+    dequantize_fp8_cache,
+    dequantize_int_cache,
+    e4m3fn_to_f64,
+    int4_unpack,
+    int8_to_f64,
+)
 from .paged import decode_paged, gather_logical_cache  # noqa: F401

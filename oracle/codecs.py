@@ -16,6 +16,13 @@ rounded or quantised.
   the OCP 8-bit float E4M3 format: 1 sign bit, 4 exponent bits with bias 7,
   3 mantissa bits, subnormals at exponent field 0, no infinities, and NaN only
   for exponent 1111 with mantissa 111.  Largest finite magnitude 448.
+* int8 / int4: the glossary's "KV cache quantization" also names INT8 and INT4
+  caches with quantization-aware scaling factors.  Reading taken: symmetric
+  signed integer codes (int8 in [-127, 127], int4 in [-7, 7]) with the same
+  granularity as the FP8 cache, one float32 scale per (token, kv-head) row,
+  value = code * scale.  An int4 row of d elements is stored as d / 2 bytes,
+  element 2i in the low nibble of byte i and element 2i + 1 in the high
+  nibble, each nibble a two's-complement 4-bit integer.
 """
 
 import numpy as np
@@ -64,6 +71,50 @@ def dequantize_fp8_cache(codes, scales):
     if scales.dtype != np.float32:
         raise TypeError("fp8 scales must be float32")
     vals = e4m3fn_to_f64(codes)
+    if vals.shape[:-1] != scales.shape:
+        raise ValueError("scale shape must equal code shape without the last axis")
+    return vals * scales.astype(np.float64)[..., None]
+
+
+def int8_to_f64(codes):
+    """int8 codes -> float64 (exact)."""
+    codes = np.asarray(codes)
+    if codes.dtype != np.int8:
+        raise TypeError("int8 codes must be int8")
+    return codes.astype(np.float64)
+
+
+def int4_unpack(packed):
+    """uint8 [..., d/2] packed nibbles -> int64 codes [..., d].
+
+    Byte i holds element 2i in bits 0..3 and element 2i + 1 in bits 4..7; a
+    nibble n stands for n - 16 when its top bit is set (two's complement)."""
+    packed = np.asarray(packed)
+    if packed.dtype != np.uint8:
+        raise TypeError("int4 codes must be packed into uint8")
+    lo = (packed & 0x0F).astype(np.int64)
+    hi = (packed >> 4).astype(np.int64)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequantize_int_cache(codes, scales, bits):
+    """int8 codes [..., S, d] (bits = 8) or packed int4 codes [..., S, d/2]
+    (bits = 4), and float32 scales [..., S] -> float64 values code * scale
+    (exact: small integers times a float32, formed in float64)."""
+    scales = np.asarray(scales)
+    if scales.dtype != np.float32:
+        raise TypeError("int cache scales must be float32")
+    if bits == 8:
+        vals = int8_to_f64(codes)
+    elif bits == 4:
+        vals = int4_unpack(codes).astype(np.float64)
+    else:
+        raise ValueError("bits must be 8 or 4")
     if vals.shape[:-1] != scales.shape:
         raise ValueError("scale shape must equal code shape without the last axis")
     return vals * scales.astype(np.float64)[..., None]

@@ -8,7 +8,10 @@ import oracle
 from transformer_attention_gqa_amd import binding, inputs
 
 # max-abs-error bars, by the K/V element type the path reads
-TOL = {"f32": 1e-3, "bf16": 2e-2, "fp8": 5e-2}
+# (int8 / int4 caches take the quantized-cache bar: the oracle sees the exact
+# dequantized values, and the kernel's arithmetic is that of the fp8 path with
+# an exact code -> bf16 conversion)
+TOL = {"f32": 1e-3, "bf16": 2e-2, "fp8": 5e-2, "int8": 5e-2, "int4": 5e-2}
 
 
 def to_f64(t):
@@ -21,12 +24,19 @@ def to_f64(t):
     raise TypeError(arr.dtype)
 
 
+def dequantize(kind, codes, scales):
+    """Stored codes and scales of a quantized cache -> float64 values (oracle decoders)."""
+    c, sc = inputs.stored_numpy(codes), inputs.stored_numpy(scales)
+    if kind == "fp8":
+        return oracle.dequantize_fp8_cache(c, sc)
+    return oracle.dequantize_int_cache(c, sc, 8 if kind == "int8" else 4)
+
+
 def cache_f64(inp, b, g):
     """K/V slab (b, g) of a decode input as float64 values [S_max, d] each."""
-    if inp.wl.kv_dtype == "fp8":
-        k = oracle.dequantize_fp8_cache(inputs.stored_numpy(inp.k[b, g]), inputs.stored_numpy(inp.k_scale[b, g]))
-        v = oracle.dequantize_fp8_cache(inputs.stored_numpy(inp.v[b, g]), inputs.stored_numpy(inp.v_scale[b, g]))
-        return k, v
+    kind = inp.wl.kv_dtype
+    if kind in inputs.QUANTIZED:
+        return (dequantize(kind, inp.k[b, g], inp.k_scale[b, g]), dequantize(kind, inp.v[b, g], inp.v_scale[b, g]))
     return to_f64(inp.k[b, g]), to_f64(inp.v[b, g])
 
 

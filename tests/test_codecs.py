@@ -79,3 +79,63 @@ def test_dequantize_rejects_wrong_types():
         codecs.e4m3fn_to_f64(np.zeros(3, dtype=np.int32))
     with pytest.raises(TypeError):
         codecs.dequantize_fp8_cache(np.zeros((2, 3), dtype=np.uint8), np.zeros(2, dtype=np.float64))
+
+
+# ---- int8 / int4 caches ("KV cache quantization": INT8 / INT4 with scales)
+
+def test_int8_codes_are_their_own_values():
+    codes = np.arange(-128, 128, dtype=np.int8)
+    assert codecs.int8_to_f64(codes).tolist() == list(range(-128, 128))
+
+
+def test_int4_nibble_order_and_sign_hand_built():
+    # byte 0x9F: low nibble 0xF = -1 (element 0), high nibble 0x9 = -7 (element 1);
+    # byte 0x70: low 0x0 = 0 (element 2), high 0x7 = +7 (element 3)
+    packed = np.array([[0x9F, 0x70]], dtype=np.uint8)
+    assert codecs.int4_unpack(packed).tolist() == [[-1, -7, 0, 7]]
+
+
+def test_int4_unpack_exhaustive_against_shift_sign_extension():
+    # every byte, decoded by a different route: move each nibble to the top of
+    # a signed byte and shift it back arithmetically
+    b = np.arange(256, dtype=np.uint8)
+    lo_ref = ((b << 4).astype(np.uint8).view(np.int8) >> 4).astype(np.int64)
+    hi_ref = (b.view(np.int8) >> 4).astype(np.int64)
+    out = codecs.int4_unpack(b.reshape(256, 1))
+    assert np.array_equal(out[:, 0], lo_ref) and np.array_equal(out[:, 1], hi_ref)
+
+
+def test_int4_pack_unpack_round_trip():
+    codes = torch.randint(-8, 8, (5, 7, 64), dtype=torch.int8)
+    back = codecs.int4_unpack(inputs.pack_int4(codes).numpy())
+    assert np.array_equal(back, codes.numpy().astype(np.int64))
+
+
+@pytest.mark.parametrize("kind,qmax", [("int8", 127), ("int4", 7)])
+def test_int_quantizer_round_trip_bound(kind, qmax):
+    x = torch.randn(6, 33, 64, dtype=torch.float32)
+    x[0, 0] = 0.0  # an all-zero row keeps scale 1 and codes 0
+    codes, scales = inputs.quantize_rows(x, kind)
+    deq = codecs.dequantize_int_cache(codes.numpy(), scales.numpy(), 8 if kind == "int8" else 4)
+    xs = x.double().numpy()
+    sc = scales.double().numpy()[..., None]
+    ints = np.rint(deq / sc)
+    assert np.abs(ints).max() <= qmax
+    # the row maximum maps to +-qmax; every value is within half a step
+    nz = np.abs(xs).max(-1) > 0
+    top = np.take_along_axis(ints, np.abs(xs).argmax(-1)[..., None], -1)[..., 0]
+    assert np.all(np.abs(top[nz]) == qmax)
+    assert np.all(np.abs(deq - xs) <= 0.5 * sc * (1 + 1e-6))
+    assert scales[0, 0].item() == 1.0 and np.all(deq[0, 0] == 0.0)
+
+
+def test_int_dequantize_is_code_times_scale():
+    codes = np.array([[[-127, 0, 5, 127]]], dtype=np.int8)
+    scales = np.array([[0.25]], dtype=np.float32)
+    assert codecs.dequantize_int_cache(codes, scales, 8).tolist() == [[[-31.75, 0.0, 1.25, 31.75]]]
+    packed = np.array([[[0x9F, 0x70]]], dtype=np.uint8)
+    assert codecs.dequantize_int_cache(packed, scales, 4).tolist() == [[[-0.25, -1.75, 0.0, 1.75]]]
+    with pytest.raises(TypeError):
+        codecs.dequantize_int_cache(codes.astype(np.uint8), scales, 8)
+    with pytest.raises(ValueError):
+        codecs.dequantize_int_cache(codes, scales, 2)

@@ -1,6 +1,7 @@
 """Seeded input generator: determinism, shapes, ranges, poisoning."""
 
 import numpy as np
+import pytest
 import torch
 
 from transformer_attention_gqa_amd import inputs
@@ -43,3 +44,22 @@ def test_poisoned_tails():
     x = inputs.make_decode_inputs(w, seq_lens=[3, 16], poison_tail=True)
     assert torch.isnan(x.k[0, :, 3:].float()).all() and not torch.isnan(x.k[0, :, :3].float()).any()
     assert not torch.isnan(x.v[1].float()).any()
+
+
+@pytest.mark.parametrize("kind", ["int8", "int4"])
+def test_int_cache_generator_shapes_and_poison(kind):
+    wl = inputs.DecodeWorkload("q", B=2, h_q=8, n_kv=2, d_h=64, S_max=48, q_dtype="bf16", kv_dtype=kind,
+                               lens=(1, 48), seed=9)
+    inp = inputs.make_decode_inputs(wl, seq_lens=[48, 10], poison_tail=True)
+    dc = 64 if kind == "int8" else 32
+    want = torch.int8 if kind == "int8" else torch.uint8
+    assert inp.k.shape == (2, 2, 48, dc) and inp.k.dtype == want and inp.v.dtype == want
+    assert inp.k_scale.shape == (2, 2, 48) and inp.k_scale.dtype == torch.float32
+    assert torch.isnan(inp.k_scale[1, :, 10:]).all() and torch.isfinite(inp.k_scale[1, :, :10]).all()
+    assert torch.isfinite(inp.k_scale[0]).all()
+    pc = inputs.POISON_CODE[kind]
+    assert (inp.k[1, :, 10:].view(torch.uint8) == pc).all()
+    pin = inputs.make_paged_decode_inputs(wl, 16, seq_lens=[48, 10])
+    assert pin.k_pages.shape[-1] == dc and pin.k_pages.dtype == want
+    spare = sorted(set(range(pin.num_pages)) - {int(x) for x in pin.block_table.flatten()})
+    assert torch.isnan(pin.k_scale_pages[spare]).all()

@@ -14,6 +14,10 @@ Recipe (every workload is synthetic):
     via torch's round-to-nearest-even cast -- the "quantization-aware scaling
     factors" reading of the KV-cache quantisation passage of the
     "Multi-Query Attention (MQA)" glossary page;
+  * int8 / int4 KV caches (the same passage's INT8 / INT4 caches): the same
+    per-row granularity, scale = max|x| / 127 (int8) or / 7 (int4), code =
+    round-half-to-even(x / scale) clamped to the symmetric range; int4 codes
+    are packed two per byte, element 2i in the low nibble;
   * ragged lengths: integers drawn uniformly from [lo, hi] inclusive from a CPU
     generator, so a workload's lengths are the same whichever device holds the
     tensors;
@@ -26,8 +30,11 @@ from typing import Optional, Tuple
 
 import torch
 
-DTYPES = ("f32", "bf16", "fp8")
+DTYPES = ("f32", "bf16", "fp8", "int8", "int4")
 FP8_MAX = 448.0
+INT8_MAX = 127  # symmetric codes: -127 .. 127
+INT4_MAX = 7    # symmetric codes: -7 .. 7
+QUANTIZED = ("fp8", "int8", "int4")
 
 
 @dataclass(frozen=True)
@@ -39,7 +46,7 @@ class DecodeWorkload:
     d_h: int
     S_max: int
     q_dtype: str  # "f32" | "bf16"
-    kv_dtype: str  # "f32" | "bf16" | "fp8"
+    kv_dtype: str  # "f32" | "bf16" | "fp8" | "int8" | "int4"
     lens: Tuple[int, int]  # inclusive range of L_b; (S, S) for fixed length
     seed: int
 
@@ -128,20 +135,61 @@ def quantize_e4m3_rows(x):
     return codes, scale
 
 
+def quantize_int_rows(x, qmax):
+    """float32 [..., d] -> (int8 codes [..., d] in [-qmax, qmax], float32 scales
+    [...]): symmetric absmax per row, round half to even."""
+    x = x.float()
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / qmax, torch.ones_like(amax)).float()
+    codes = torch.round(x / scale[..., None]).clamp(-qmax, qmax).to(torch.int8)
+    return codes, scale
+
+
+def pack_int4(codes):
+    """int8 codes [..., d] in [-8, 7] -> uint8 [..., d/2]: element 2i in the low
+    nibble of byte i, element 2i + 1 in the high nibble (two's complement)."""
+    c = codes.to(torch.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).to(torch.uint8)
+
+
+def quantize_rows(x, kind):
+    """float32 [..., d] -> (stored codes, float32 scales) for a quantized cache kind."""
+    if kind == "fp8":
+        return quantize_e4m3_rows(x)
+    if kind == "int8":
+        return quantize_int_rows(x, INT8_MAX)
+    if kind == "int4":
+        codes, scale = quantize_int_rows(x, INT4_MAX)
+        return pack_int4(codes), scale
+    raise ValueError(kind)
+
+
+def code_shape(kind, shape):
+    """Shape and dtype of the stored codes of a quantized cache of `shape` [..., d]."""
+    if kind == "int4":
+        return tuple(shape[:-1]) + (shape[-1] // 2,), torch.uint8
+    return tuple(shape), (torch.int8 if kind == "int8" else torch.uint8)
+
+
+# Code patterns that fill cache rows which must never be read: NaN for fp8,
+# the largest codes for the integer kinds (their scales are set to NaN).
+POISON_CODE = {"fp8": 0x7F, "int8": 0x7F, "int4": 0x77}
+
+
 @dataclass
 class DecodeInputs:
     wl: DecodeWorkload
     q: torch.Tensor  # [B, h_q, d] f32/bf16
-    k: torch.Tensor  # [B, n_kv, S_max, d] f32/bf16 or uint8 codes
+    k: torch.Tensor  # [B, n_kv, S_max, d] f32/bf16, uint8 fp8 / int8 codes, or [.., d/2] packed int4
     v: torch.Tensor
     seq_lens: torch.Tensor  # [B] int32, same device
-    k_scale: Optional[torch.Tensor] = None  # [B, n_kv, S_max] f32 (fp8 only)
+    k_scale: Optional[torch.Tensor] = None  # [B, n_kv, S_max] f32 (quantized caches only)
     v_scale: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
 
 
 def make_decode_inputs(wl, device="cpu", seq_lens=None, poison_tail=False, seed=None):
-    """Draw q, K/V cache (and fp8 scales) for a decode workload.
+    """Draw q, K/V cache (and scales of a quantized cache) for a decode workload.
 
     seq_lens overrides the workload's length rule (list/tensor of B ints).
     """
@@ -153,17 +201,18 @@ def make_decode_inputs(wl, device="cpu", seq_lens=None, poison_tail=False, seed=
     else:
         lens = torch.as_tensor(seq_lens, dtype=torch.int32).reshape(B)
     q = torch.randn((B, h_q, d), generator=g, device=device, dtype=torch.float32).to(_torch_dtype(wl.q_dtype))
-    if wl.kv_dtype == "fp8":
-        k = torch.empty((B, n_kv, S, d), dtype=torch.uint8, device=device)
-        v = torch.empty((B, n_kv, S, d), dtype=torch.uint8, device=device)
+    if wl.kv_dtype in QUANTIZED:
+        shape, cdt = code_shape(wl.kv_dtype, (B, n_kv, S, d))
+        k = torch.empty(shape, dtype=cdt, device=device)
+        v = torch.empty(shape, dtype=cdt, device=device)
         ks = torch.empty((B, n_kv, S), dtype=torch.float32, device=device)
         vs = torch.empty((B, n_kv, S), dtype=torch.float32, device=device)
         for b in range(B):  # per batch entry to bound temporary memory
             xk = torch.randn((n_kv, S, d), generator=g, device=device, dtype=torch.float32)
-            k[b], ks[b] = quantize_e4m3_rows(xk)
+            k[b], ks[b] = quantize_rows(xk, wl.kv_dtype)
             del xk
             xv = torch.randn((n_kv, S, d), generator=g, device=device, dtype=torch.float32)
-            v[b], vs[b] = quantize_e4m3_rows(xv)
+            v[b], vs[b] = quantize_rows(xv, wl.kv_dtype)
             del xv
         inp = DecodeInputs(wl, q, k, v, lens.to(device), ks, vs)
     else:
@@ -180,20 +229,27 @@ def make_decode_inputs(wl, device="cpu", seq_lens=None, poison_tail=False, seed=
 
 
 def poison_cache_tails(inp):
-    """Fill cache rows at positions >= L_b with NaN (codes 0x7F for fp8)."""
+    """Fill cache rows at positions >= L_b with NaN (quantized caches: the
+    POISON_CODE pattern and NaN scales)."""
     S = inp.wl.S_max
     for b in range(inp.wl.B):
         n = int(min(max(int(inp.seq_lens[b]), 0), S))
         if n >= S:
             continue
-        if inp.wl.kv_dtype == "fp8":
-            inp.k[b, :, n:, :] = 0x7F
-            inp.v[b, :, n:, :] = 0x7F
+        if inp.wl.kv_dtype in QUANTIZED:
+            pc = POISON_CODE[inp.wl.kv_dtype]
+            inp.k[b, :, n:, :] = _as_code(pc, inp.k.dtype)
+            inp.v[b, :, n:, :] = _as_code(pc, inp.v.dtype)
             inp.k_scale[b, :, n:] = float("nan")
             inp.v_scale[b, :, n:] = float("nan")
         else:
             inp.k[b, :, n:, :] = float("nan")
             inp.v[b, :, n:, :] = float("nan")
+
+
+def _as_code(byte, dtype):
+    """A byte pattern as a fill value of a code tensor's dtype."""
+    return byte - 256 if dtype == torch.int8 and byte >= 128 else byte
 
 
 @dataclass
@@ -203,7 +259,7 @@ class PagedDecodeInputs:
     page_size: int
     k_pages: torch.Tensor              # [num_pages, n_kv, page_size, d]
     v_pages: torch.Tensor
-    k_scale_pages: Optional[torch.Tensor]  # [num_pages, n_kv, page_size] float32 (fp8 only)
+    k_scale_pages: Optional[torch.Tensor]  # [num_pages, n_kv, page_size] float32 (quantized caches only)
     v_scale_pages: Optional[torch.Tensor]
     block_table: torch.Tensor          # [B, max_pages] int32
 
@@ -216,7 +272,8 @@ def make_paged_decode_inputs(wl, page_size, device="cpu", seq_lens=None, poison_
                              spare_pages=3, junk_unused_entries=False, keep_base=True):
     """Draw a decode workload (as make_decode_inputs) and scatter its cache into
     a pool of B * S_max / page_size + spare_pages pages in a seeded random
-    order.  Spare pages hold NaN (fp8: code 0x7F, NaN scales).  With
+    order.  Spare pages hold NaN (quantized caches: POISON_CODE and NaN
+    scales).  With
     junk_unused_entries, block-table entries past a sequence's last page are
     set to -1 (they must never be read)."""
     if wl.S_max % page_size:
@@ -229,20 +286,22 @@ def make_paged_decode_inputs(wl, page_size, device="cpu", seq_lens=None, poison_
     g = torch.Generator(device="cpu").manual_seed(seed * 104729 + page_size)
     perm = torch.randperm(num_pages, generator=g)[:B * max_pages].to(torch.int32)
     table = perm.reshape(B, max_pages).clone()
-    fp8 = wl.kv_dtype == "fp8"
-    kp = torch.empty((num_pages, n_kv, page_size, d), dtype=base.k.dtype, device=device)
+    quant = wl.kv_dtype in QUANTIZED
+    dc = base.k.shape[-1]  # stored elements per row (d / 2 for packed int4)
+    kp = torch.empty((num_pages, n_kv, page_size, dc), dtype=base.k.dtype, device=device)
     vp = torch.empty_like(kp)
-    kp.fill_(0x7F) if fp8 else kp.fill_(float("nan"))
-    vp.fill_(0x7F) if fp8 else vp.fill_(float("nan"))
+    fill = _as_code(POISON_CODE[wl.kv_dtype], kp.dtype) if quant else float("nan")
+    kp.fill_(fill)
+    vp.fill_(fill)
     ksp = vsp = None
-    if fp8:
+    if quant:
         ksp = torch.full((num_pages, n_kv, page_size), float("nan"), dtype=torch.float32, device=device)
         vsp = torch.full_like(ksp, float("nan"))
     idx = table.to(device=device, dtype=torch.long)
     for b in range(B):
-        kp[idx[b]] = base.k[b].reshape(n_kv, max_pages, page_size, d).transpose(0, 1)
-        vp[idx[b]] = base.v[b].reshape(n_kv, max_pages, page_size, d).transpose(0, 1)
-        if fp8:
+        kp[idx[b]] = base.k[b].reshape(n_kv, max_pages, page_size, dc).transpose(0, 1)
+        vp[idx[b]] = base.v[b].reshape(n_kv, max_pages, page_size, dc).transpose(0, 1)
+        if quant:
             ksp[idx[b]] = base.k_scale[b].reshape(n_kv, max_pages, page_size).transpose(0, 1)
             vsp[idx[b]] = base.v_scale[b].reshape(n_kv, max_pages, page_size).transpose(0, 1)
     if junk_unused_entries:
@@ -275,7 +334,8 @@ def make_prefill_inputs(wl, device="cpu", seed=None):
 
 def stored_numpy(t):
     """A tensor's stored encoding as a numpy array: bf16 -> uint16 bit patterns,
-    fp8 codes stay uint8, float32/int32 as is.  (Bit views, no arithmetic.)"""
+    fp8 and packed int4 codes stay uint8, int8 codes int8, float32/int32 as is.
+    (Bit views, no arithmetic.)"""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
