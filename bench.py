@@ -372,11 +372,14 @@ def _workload_launches():
     grid (the combine kernel of the ragged GQA and the long MQA decode); such
     launches are told apart by the workload whose unambiguous kernel ran last."""
     out = []
-    for wl in inputs.DECODE_WORKLOADS.values():
+    kvf = {"bf16": "0", "fp8": "1", "int8": "2", "int4": "3"}  # template code of the cache format
+    for wl in list(inputs.DECODE_WORKLOADS.values()) + list(inputs.QUANT_DECODE_WORKLOADS.values()):
         qd = torch.empty((wl.B, wl.h_q, wl.d_h), dtype={"f32": torch.float32, "bf16": torch.bfloat16}[wl.q_dtype],
                          device="meta")
-        kd = torch.empty((wl.B, wl.n_kv, wl.S_max, wl.d_h), device="meta",
-                         dtype={"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.kv_dtype])
+        shape, cdt = inputs.code_shape(wl.kv_dtype, (wl.B, wl.n_kv, wl.S_max, wl.d_h)) \
+            if wl.kv_dtype in inputs.QUANTIZED else ((wl.B, wl.n_kv, wl.S_max, wl.d_h),
+                                                     {"f32": torch.float32, "bf16": torch.bfloat16}[wl.kv_dtype])
+        kd = torch.empty(shape, device="meta", dtype=cdt)
         ns = binding.attn_decode_num_splits(binding.decode_desc(qd, kd))
         G = wl.h_q // wl.n_kv
         lens = inputs.draw_lengths(wl.B, *wl.lens, wl.seed).tolist()
@@ -386,7 +389,7 @@ def _workload_launches():
         if wl.kv_dtype == "f32":
             out.append((("gqa_decode_split_f32", (str(wl.d_h), "false"), ns * 256), (key, wl.name, kv, "bytes")))
         else:
-            targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8", "false")
+            targs = (str(wl.d_h), str(hpc // 16), kvf[wl.kv_dtype], "8", "false")
             out.append((("gqa_decode_split_mfma", targs, ns * 512), (key, wl.name, kv, "bytes")))
         n_slabs = wl.B * wl.n_kv * -(-G // hpc)
         grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
@@ -401,7 +404,7 @@ def _workload_launches():
         ns = binding.attn_decode_num_splits(binding.decode_desc(qd, kd))
         lens = inputs.draw_lengths(wl.B, *wl.lens, wl.seed).tolist()
         kv = roofline.decode_kv_bytes(wl.kv_dtype, wl.n_kv, wl.d_h, lens)
-        targs = (str(wl.d_h), str(hpc // 16), "true" if wl.kv_dtype == "fp8" else "false", "8", "true")
+        targs = (str(wl.d_h), str(hpc // 16), kvf[wl.kv_dtype], "8", "true")
         out.append((("gqa_decode_split_mfma", targs, ns * 512),
                     (f"decode_split_paged_{wl.kv_dtype}:{pwl.name}", pwl.name, kv, "bytes")))
         n_slabs = wl.B * wl.n_kv * -(-G // hpc)
@@ -544,7 +547,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=MAIN, choices=sorted(inputs.DECODE_WORKLOADS) + sorted(
-        inputs.PAGED_WORKLOADS) + sorted(inputs.PREFILL_WORKLOADS))
+        inputs.QUANT_DECODE_WORKLOADS) + sorted(inputs.PAGED_WORKLOADS) + sorted(inputs.PREFILL_WORKLOADS))
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -582,12 +585,14 @@ def main(argv=None):
             return bench_prefill(inputs.PREFILL_WORKLOADS[name], steps, warmup, use_graph)
         if name in inputs.PAGED_WORKLOADS:
             return bench_decode_paged(inputs.PAGED_WORKLOADS[name], steps, warmup, use_graph)
-        return bench_decode(inputs.DECODE_WORKLOADS[name], steps, warmup, use_graph, args.n_split)
+        wl = {**inputs.DECODE_WORKLOADS, **inputs.QUANT_DECODE_WORKLOADS}[name]
+        return bench_decode(wl, steps, warmup, use_graph, args.n_split)
 
     main_res = run(args.workload, args.steps, args.warmup)
     others = {}
     if not args.only_main:
-        for name in list(inputs.DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS) + list(inputs.PREFILL_WORKLOADS):
+        for name in (list(inputs.DECODE_WORKLOADS) + list(inputs.QUANT_DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS)
+                     + list(inputs.PREFILL_WORKLOADS)):
             if name == args.workload:
                 continue
             others[name] = run(name, max(5, min(args.steps, 20)), 2)

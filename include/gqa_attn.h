@@ -51,10 +51,14 @@ typedef struct ihipStream_t* hipStream_t;
 
 /* Element types. */
 enum {
-  GQA_F32 = 0,      /* IEEE binary32                                        */
-  GQA_BF16 = 1,     /* bfloat16 (upper half of binary32)                    */
-  GQA_FP8_E4M3 = 2  /* OCP 8-bit float E4M3 ("e4m3fn": bias 7, max 448,     */
-                    /* no infinities, NaN = S.1111.111)                     */
+  GQA_F32 = 0,       /* IEEE binary32                                        */
+  GQA_BF16 = 1,      /* bfloat16 (upper half of binary32)                    */
+  GQA_FP8_E4M3 = 2,  /* OCP 8-bit float E4M3 ("e4m3fn": bias 7, max 448,     */
+                     /* no infinities, NaN = S.1111.111)                     */
+  GQA_INT8 = 3,      /* signed 8-bit integer code                            */
+  GQA_INT4 = 4       /* signed 4-bit integer code (two's complement), two    */
+                     /* per byte: element 2i in bits 0..3 of byte i,         */
+                     /* element 2i+1 in bits 4..7                            */
 };
 
 typedef enum gqa_status {
@@ -80,18 +84,21 @@ typedef enum gqa_status {
  *   q        [B, h_q, d_h]             q_dtype (F32 or BF16)
  *   k_cache  [B, n_kv, S_max, d_h]     kv_dtype -- the cache layout after the
  *   v_cache  [B, n_kv, S_max, d_h]     modules' view(B,S,n_kv,d).transpose(1,2)
- *   k_scale  [B, n_kv, S_max] float32  FP8 cache only: one dequantisation
- *   v_scale  [B, n_kv, S_max] float32  factor per (token, kv-head) row;
- *                                      value = e4m3(code) * scale ("KV cache
- *                                      quantization" in the MQA glossary).
- *                                      NULL for F32/BF16 caches.
+ *                                      (INT4: [B, n_kv, S_max, d_h/2] bytes)
+ *   k_scale  [B, n_kv, S_max] float32  FP8 / INT8 / INT4 caches only: one
+ *   v_scale  [B, n_kv, S_max] float32  dequantisation factor per (token,
+ *                                      kv-head) row; value = decode(code) *
+ *                                      scale ("KV cache quantization" in the
+ *                                      MQA glossary).  NULL for F32/BF16.
  *   seq_lens [B] int32 (device)        L_b = visible cache positions 0..L_b-1
  *                                      of sequence b.  Read on the device
  *                                      only: values are clamped to [0, S_max];
  *                                      L_b = 0 yields a zero output row.
  *   out      [B, h_q, d_h]             q_dtype
- * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
- * Accumulation is float32 throughout.
+ * Supported (q_dtype, kv_dtype): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3),
+ * (BF16, INT8), (BF16, INT4).  Codes become bf16 exactly; the K scale
+ * multiplies the score and the V scale the softmax weight.  Accumulation is
+ * float32 throughout.
  *
  * Sequence split: the 32-token tiles (64 on the F32 path) of every
  * (sequence, kv-head) are concatenated and cut into n_split equal ranges, one
@@ -149,12 +156,13 @@ gqa_status attn_decode_combine(const gqa_decode_desc* d, const int32_t* seq_lens
  *
  * Shapes (row-major, innermost last):
  *   q             [B, h_q, d_h]                     q_dtype
- *   k_pages       [num_pages, n_kv, page_size, d_h] kv_dtype -- a pool of
+ *   k_pages       [num_pages, n_kv, page_size, d_h] kv_dtype (INT4: d_h/2
+ *                                                   bytes per row) -- a pool of
  *   v_pages       [num_pages, n_kv, page_size, d_h] pages; page p holds
  *                                                   page_size consecutive
  *                                                   tokens of all K/V heads
  *                                                   of one sequence
- *   k_scale_pages [num_pages, n_kv, page_size] float32   FP8 only, else NULL
+ *   k_scale_pages [num_pages, n_kv, page_size] float32   FP8/INT8/INT4 only
  *   v_scale_pages [num_pages, n_kv, page_size] float32
  *   block_table   [B, max_pages_per_seq] int32 (device): entry (b, i) is the
  *                 page holding tokens i*page_size .. (i+1)*page_size - 1 of

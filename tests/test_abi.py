@@ -199,3 +199,16 @@ def test_paged_pointer_and_value_errors(lib):
     assert call_paged(lib, desc, vp=MISALIGNED) == 4
     assert call_paged(lib, desc, ws_bytes=16) == 5
     assert call_paged(lib, desc, scale=0.0) == 7
+
+
+@pytest.mark.parametrize("kt", [3, 4])
+def test_int_caches_are_accepted_with_scales(lib, kt):
+    """INT8 (3) and INT4 (4) caches take bf16 Q and per-row scales, like FP8."""
+    desc = dd(kt=kt)
+    assert lib.attn_decode_num_splits(ctypes.byref(desc)) > 0
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(desc)) == \
+        lib.attn_decode_workspace_bytes(ctypes.byref(dd(kt=2)))
+    assert call_decode(lib, desc, ks=None, vs=ALIGNED) == 1
+    assert call_decode(lib, desc, ks=ALIGNED, vs=MISALIGNED) == 4
+    assert call_decode(lib, dd(qt=0, kt=kt)) == 3
+    assert call_paged(lib, pgd(kt=kt), ks=None, vs=None) == 1

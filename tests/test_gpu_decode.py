@@ -41,9 +41,10 @@ def test_mqa_tiny_f32_full():
     check_full(inp)
 
 
-@pytest.mark.parametrize("name", ["gqa_decode_ragged_bf16", "mqa_decode_long_bf16", "gqa_decode_fp8kv"])
+@pytest.mark.parametrize("name", ["gqa_decode_ragged_bf16", "mqa_decode_long_bf16", "gqa_decode_fp8kv",
+                                  "gqa_decode_int8kv", "gqa_decode_int4kv"])
 def test_full_size_workload_sampled(name):
-    w = inputs.DECODE_WORKLOADS[name]
+    w = {**inputs.DECODE_WORKLOADS, **inputs.QUANT_DECODE_WORKLOADS}[name]
     inp = inputs.make_decode_inputs(w, device=DEV)
     print(f"[decode-full] {name} sumL={int(inp.seq_lens.sum())}", flush=True)
     out = pu.run_decode(inp)
@@ -58,7 +59,7 @@ def test_full_size_workload_sampled(name):
 
 # ------------------------------------------------------ reduced, all outputs
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "int8", "int4"])
 def test_gqa_ragged_poisoned_tails(kd):
     w = wl("ragged", B=5, h_q=64, n_kv=8, d=128, S=520, qd="bf16", kd=kd, seed=7)
     inp = inputs.make_decode_inputs(w, device=DEV, seq_lens=[1, 33, 300, 520, 97], poison_tail=True)
@@ -72,7 +73,7 @@ def test_mqa_long_ragged_tile_tail():
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16, 32, 64])
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_group_size_sweep(G, kd, d):
     n_kv = 2 if G <= 32 else 1
@@ -83,7 +84,7 @@ def test_group_size_sweep(G, kd, d):
 
 
 @pytest.mark.parametrize("n_split", [1, 2, 7, 10 ** 6])
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_forced_splits_agree(n_split, kd):
     qd = "f32" if kd == "f32" else "bf16"
     w = wl("splits", B=3, h_q=16, n_kv=2, d=128, S=700, qd=qd, kd=kd, seed=31)
@@ -93,7 +94,7 @@ def test_forced_splits_agree(n_split, kd):
     check_full(inp, n_split=n_split)
 
 
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_empty_and_overlong_lengths(kd):
     qd = "f32" if kd == "f32" else "bf16"
     w = wl("edge", B=4, h_q=8, n_kv=2, d=128, S=96, qd=qd, kd=kd, seed=41)
@@ -111,7 +112,7 @@ def test_single_key_returns_value_row():
         assert torch.equal(out[:, j], inp.v[:, j // 4, 0])  # p = 1 exactly; bf16 value passes through
 
 
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_deterministic_repeat(kd):
     """Repeated calls agree bitwise where the summation order is fixed: always
     on the float32 path, and on the matrix-core paths when each wave reduces at
@@ -126,13 +127,14 @@ def test_deterministic_repeat(kd):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "int8", "int4"])
 def test_repeat_at_full_size(kd):
     """With several tiles per wave the waves take tiles as they free up, so two
     identical calls may differ in float32 summation order and in where each
     wave rounds its probabilities to bf16: the outputs stay within about 1e-3
     of each other (4e-3 allowed), far inside the accuracy bar."""
-    w = inputs.GQA_RAGGED_BF16 if kd == "bf16" else inputs.GQA_FP8KV
+    w = {"bf16": inputs.GQA_RAGGED_BF16, "fp8": inputs.GQA_FP8KV, "int8": inputs.GQA_INT8KV,
+         "int4": inputs.GQA_INT4KV}[kd]
     inp = inputs.make_decode_inputs(w, device=DEV)
     a = pu.run_decode(inp).clone()
     b = pu.run_decode(inp)
@@ -153,7 +155,7 @@ def test_partials_then_combine_equals_decode():
     assert torch.equal(out, full)
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "int8", "int4"])
 def test_workspace_reused_across_calls(kd):
     """One workspace, filled with NaN bit patterns once, serves calls with
     different lengths and split counts; every result matches the oracle."""
@@ -182,7 +184,7 @@ def test_all_sequences_empty_gives_zero_rows():
     assert torch.count_nonzero(out) == 0
 
 
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_prepared_call_matches_plain_call(kd):
     qd = "f32" if kd == "f32" else "bf16"
     w = wl("prep", B=3, h_q=16, n_kv=2, d=128, S=300, qd=qd, kd=kd, seed=71)

@@ -22,10 +22,9 @@ def wl(B, h_q, n_kv, d, S, kd, lens=None, seed=200):
 
 def pages_f64(pin):
     """Pool contents as float64 values [num_pages, n_kv, page_size, d] (the oracle's input)."""
-    if pin.base.wl.kv_dtype == "fp8":
-        k = oracle.dequantize_fp8_cache(inputs.stored_numpy(pin.k_pages), inputs.stored_numpy(pin.k_scale_pages))
-        v = oracle.dequantize_fp8_cache(inputs.stored_numpy(pin.v_pages), inputs.stored_numpy(pin.v_scale_pages))
-        return k, v
+    kind = pin.base.wl.kv_dtype
+    if kind in inputs.QUANTIZED:
+        return (pu.dequantize(kind, pin.k_pages, pin.k_scale_pages), pu.dequantize(kind, pin.v_pages, pin.v_scale_pages))
     return pu.to_f64(pin.k_pages), pu.to_f64(pin.v_pages)
 
 
@@ -49,7 +48,7 @@ def check(pin, n_split=0):
     return out
 
 
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 @pytest.mark.parametrize("page_size", [32, 64, 128])
 def test_paged_matches_oracle(kd, page_size):
     w = wl(B=4, h_q=16, n_kv=2, d=128, S=512, kd=kd, seed=201 + page_size)
@@ -62,13 +61,13 @@ def test_paged_matches_oracle(kd, page_size):
 @pytest.mark.parametrize("G,d", [(1, 64), (8, 128), (32, 128), (64, 64)])
 def test_paged_group_sizes(G, d):
     n_kv = 2 if G <= 32 else 1
-    for kd in ("bf16", "fp8"):
+    for kd in ("bf16", "fp8", "int8", "int4"):
         w = wl(B=3, h_q=G * n_kv, n_kv=n_kv, d=d, S=256, kd=kd, seed=G * 7 + d)
         pin = inputs.make_paged_decode_inputs(w, 32, device=DEV, seq_lens=[256, 77, 33], poison_tail=True)
         check(pin)
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "int8", "int4"])
 def test_paged_shared_prefix_pages(kd):
     """Sequences 1 and 2 reuse sequence 0's first pages (a shared prompt
     prefix): several table rows name the same physical pages."""
@@ -86,7 +85,7 @@ def test_paged_forced_splits(n_split):
     check(pin, n_split=n_split)
 
 
-@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_paged_equals_contiguous_bitwise(kd):
     """Same values, same plan: the paged call must reproduce attn_decode exactly.
     At this size every workgroup's key range holds fewer tiles than it has

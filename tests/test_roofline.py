@@ -54,3 +54,12 @@ def test_workload_byte_and_flop_counts():
     w = inputs.GQA_RAGGED_BF16
     lens = inputs.draw_lengths(w.B, *w.lens, w.seed)
     assert roofline.decode_kv_bytes("bf16", w.n_kv, w.d_h, lens.tolist()) == 4096 * int(lens.sum())
+
+
+def test_int_cache_bytes():
+    # int8: one byte per element, int4: two elements per byte; both carry the
+    # same float32 scales as the fp8 cache
+    lens = [32768] * 32
+    assert roofline.decode_kv_bytes("int8", 8, 128, lens) == 2147483648
+    assert roofline.decode_kv_bytes("int4", 8, 128, lens) == 1073741824
+    assert roofline.decode_scale_bytes("int4", 8, lens) == roofline.decode_scale_bytes("fp8", 8, lens) == 67108864

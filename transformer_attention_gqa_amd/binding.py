@@ -17,7 +17,8 @@ import torch
 LIB_NAME = "libgqa_attn.so"
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
-GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
+GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_INT8, GQA_INT4 = 0, 1, 2, 3, 4
+QUANTIZED_KV = (GQA_FP8_E4M3, GQA_INT8, GQA_INT4)
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE", 4: "GQA_ERR_ALIGN",
           5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE"}
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
@@ -112,6 +113,26 @@ def _dtype_code(t):
     raise TypeError(f"unsupported tensor dtype {t.dtype}")
 
 
+def _kv_code(cache, d):
+    """Element type of a K/V cache (or page pool) read with head dim d: int8
+    codes are INT8; byte codes are FP8 E4M3 when a row holds d of them and
+    packed INT4 when it holds d / 2."""
+    if cache.dtype == torch.int8:
+        return GQA_INT8
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        if cache.shape[-1] == d:
+            return GQA_FP8_E4M3
+        if cache.dtype == torch.uint8 and 2 * cache.shape[-1] == d:
+            return GQA_INT4
+        raise ValueError(f"byte cache rows of {cache.shape[-1]} do not match head dim {d} (fp8) or {d}/2 (int4)")
+    return _dtype_code(cache)
+
+
+def _row_elems(cache, d):
+    """Stored elements per cache row for head dim d."""
+    return d // 2 if _kv_code(cache, d) == GQA_INT4 else d
+
+
 def _require(t, name, ndim):
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
@@ -123,7 +144,7 @@ def decode_desc(q, k_cache, n_split=0):
     """Descriptor for q [B, h_q, d] and cache [B, n_kv, S_max, d]."""
     B, h_q, d = q.shape
     n_kv, s_max = k_cache.shape[1], k_cache.shape[2]
-    return gqa_decode_desc(B, h_q, n_kv, s_max, d, _dtype_code(q), _dtype_code(k_cache), n_split)
+    return gqa_decode_desc(B, h_q, n_kv, s_max, d, _dtype_code(q), _kv_code(k_cache, d), n_split)
 
 
 def attn_decode_num_splits(desc):
@@ -140,11 +161,11 @@ def _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale):
     _require(v_cache, "v_cache", 4)
     if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache must have the same shape and dtype")
-    if k_cache.shape[0] != q.shape[0] or k_cache.shape[3] != q.shape[2]:
-        raise ValueError("cache [B, n_kv, S_max, d] does not match q [B, h_q, d]")
+    if k_cache.shape[0] != q.shape[0] or k_cache.shape[3] != _row_elems(k_cache, q.shape[2]):
+        raise ValueError("cache [B, n_kv, S_max, d] (packed int4: d/2 bytes) does not match q [B, h_q, d]")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
-    if _dtype_code(k_cache) == GQA_FP8_E4M3:
+    if _kv_code(k_cache, q.shape[2]) in QUANTIZED_KV:
         for name, s in (("k_scale", k_scale), ("v_scale", v_scale)):
             if s is None or s.dtype != torch.float32 or tuple(s.shape) != tuple(k_cache.shape[:3]) \
                     or not s.is_contiguous():
@@ -248,7 +269,7 @@ def paged_desc(q, k_pages, block_table, n_split=0):
     """Descriptor for q [B, h_q, d], pages [num_pages, n_kv, page_size, d] and block_table [B, max_pages]."""
     B, h_q, d = q.shape
     num_pages, n_kv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
-    return gqa_paged_desc(B, h_q, n_kv, d, _dtype_code(q), _dtype_code(k_pages), page_size, num_pages,
+    return gqa_paged_desc(B, h_q, n_kv, d, _dtype_code(q), _kv_code(k_pages, d), page_size, num_pages,
                           block_table.shape[1], n_split)
 
 
@@ -266,14 +287,14 @@ def _paged_checks(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale):
     _require(v_pages, "v_pages", 4)
     if k_pages.shape != v_pages.shape or k_pages.dtype != v_pages.dtype:
         raise ValueError("k_pages and v_pages must have the same shape and dtype")
-    if k_pages.shape[3] != q.shape[2]:
-        raise ValueError("pages [num_pages, n_kv, page_size, d] do not match q [B, h_q, d]")
+    if k_pages.shape[3] != _row_elems(k_pages, q.shape[2]):
+        raise ValueError("pages [num_pages, n_kv, page_size, d] (packed int4: d/2 bytes) do not match q [B, h_q, d]")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != q.shape[0] \
             or not block_table.is_contiguous():
         raise ValueError("block_table must be a contiguous int32 tensor of shape [B, max_pages]")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],) or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
-    if _dtype_code(k_pages) == GQA_FP8_E4M3:
+    if _kv_code(k_pages, q.shape[2]) in QUANTIZED_KV:
         for name, s in (("k_scale", k_scale), ("v_scale", v_scale)):
             if s is None or s.dtype != torch.float32 or tuple(s.shape) != tuple(k_pages.shape[:3]) \
                     or not s.is_contiguous():

@@ -31,11 +31,14 @@ void record_hip_error(hipError_t e) {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// K/V element types that come with per-row scales
+bool is_quantized(int32_t t) { return t == GQA_FP8_E4M3 || t == GQA_INT8 || t == GQA_INT4; }
+
 // The kernels take the running max on unscaled scores, which needs scale > 0.
 bool bad_scale(float s) { return !(s > 0.0f) || !(s < __builtin_huge_valf()); }
 
 struct DecodePlan {
-  int kind;             // 0 f32, 1 bf16 K/V, 2 fp8 K/V
+  int kind;             // 0 f32, 1 bf16 K/V, 2 fp8, 3 int8, 4 int4 K/V
   int tile;             // tokens per wave tile
   int hb;               // 16-head blocks per workgroup (matrix-core paths)
   int heads_per_chunk;  // query heads one workgroup serves at a time
@@ -51,8 +54,7 @@ gqa_status validate_decode_desc(const gqa_decode_desc* d) {
   if (d->h_q % d->n_kv != 0) return GQA_ERR_SHAPE;
   if (d->d_h != 64 && d->d_h != 128) return GQA_ERR_SHAPE;
   const bool ok = (d->q_dtype == GQA_F32 && d->kv_dtype == GQA_F32) ||
-                  (d->q_dtype == GQA_BF16 && d->kv_dtype == GQA_BF16) ||
-                  (d->q_dtype == GQA_BF16 && d->kv_dtype == GQA_FP8_E4M3);
+                  (d->q_dtype == GQA_BF16 && (d->kv_dtype == GQA_BF16 || is_quantized(d->kv_dtype)));
   if (!ok) return GQA_ERR_DTYPE;
   // index arithmetic inside the kernels: B*h_q rows, B*n_kv*S_max cache rows
   if ((int64_t)d->B * d->h_q > (int64_t)1 << 30) return GQA_ERR_SHAPE;
@@ -64,7 +66,13 @@ gqa_status validate_decode_desc(const gqa_decode_desc* d) {
 DecodePlan plan_decode(const gqa_decode_desc* d) {
   DecodePlan p{};
   const int G = d->h_q / d->n_kv;
-  p.kind = d->kv_dtype == GQA_F32 ? 0 : (d->kv_dtype == GQA_BF16 ? 1 : 2);
+  switch (d->kv_dtype) {
+    case GQA_F32: p.kind = 0; break;
+    case GQA_BF16: p.kind = 1; break;
+    case GQA_FP8_E4M3: p.kind = 2; break;
+    case GQA_INT8: p.kind = 3; break;
+    default: p.kind = 4; break;  // GQA_INT4
+  }
   if (p.kind == 0) {
     p.tile = kTileF32;
     p.hb = 1;
@@ -104,10 +112,10 @@ WorkspaceLayout workspace_layout(const gqa_decode_desc* d, const DecodePlan& p) 
 gqa_status check_decode_ptrs(const gqa_decode_desc* d, const void* q, const void* k, const void* v,
                              const float* ks, const float* vs, const int32_t* seq_lens) {
   if (!q || !k || !v || !seq_lens) return GQA_ERR_NULL;
-  if (d->kv_dtype == GQA_FP8_E4M3 && (!ks || !vs)) return GQA_ERR_NULL;
+  if (is_quantized(d->kv_dtype) && (!ks || !vs)) return GQA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v)) return GQA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0) return GQA_ERR_ALIGN;
-  if (d->kv_dtype == GQA_FP8_E4M3 && (misaligned(ks) || misaligned(vs))) return GQA_ERR_ALIGN;
+  if (is_quantized(d->kv_dtype) && (misaligned(ks) || misaligned(vs))) return GQA_ERR_ALIGN;
   return GQA_OK;
 }
 

@@ -233,8 +233,14 @@ __device__ __forceinline__ Segment make_segment(const DecodeArgs& a, const LaneL
   return s;
 }
 
-template <int D, int HB, bool FP8, int NW, bool PAGED>
+// Element format of a matrix-core decode's K/V cache.
+enum KvFormat : int { kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2, kKvInt4 = 3 };
+
+template <int D, int HB, int KVF, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
+  // quantized caches carry one float32 scale per (token, kv-head) row for K
+  // and for V: the K scale multiplies the score, the V scale the probability
+  constexpr bool QUANT = KVF != kKvBf16;
   constexpr int CH = D / 8;   // 16-byte bf16 chunks per row
   constexpr int KK = D / 32;  // k-steps of the score product
   constexpr int NT = D / 16;  // 16-wide d tiles of the PV product
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // 32 heads of a bf16 cache: one 32x32 score tile per 32 tokens on
   // v_mfma_f32_32x32x16_bf16 (the same shape as the prefill kernel with heads
   // in place of query rows); otherwise HB blocks of 16 heads on 16x16x32.
-  constexpr bool M32 = HB == 2 && !FP8;
+  constexpr bool M32 = HB == 2 && KVF == kKvBf16;
   constexpr int KS = D / 16;  // k-steps of the 32x32 score product
   constexpr int NT32 = D / 32;
   static_assert(HPC * D * 4 <= 2 * TILE_BYTES, "partial O does not fit the wave slab");
@@ -277,23 +283,24 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // the merge spread over all banks.
   auto ow_idx = [](int h, int d) { return h * D + ((((d >> 2) ^ (h % (D / 4))) << 2) | (d & 3)); };
 
-  // per-lane load assignment.  bf16: a load instruction covers 64/CH rows,
-  // each row by CH consecutive lanes.  fp8: rows of D bytes, D/16 lanes per row.
-  constexpr int NLD = FP8 ? (kTile * D) / (64 * 16) : (kTile * D * 2) / (64 * 16);
-  constexpr int LPR = FP8 ? D / 16 : CH;  // lanes per row
-  constexpr int RPL = 64 / LPR;            // rows per load instruction
+  // per-lane load assignment: each lane loads 16 bytes of a cache row, a row
+  // by ROWB/16 consecutive lanes (bf16: CH lanes of 8 elements; fp8 / int8:
+  // D/16 lanes of 16 codes; int4: D/32 lanes of 32 codes).
+  constexpr int ROWB = KVF == kKvBf16 ? 2 * D : (KVF == kKvInt4 ? D / 2 : D);  // bytes per cache row
+  constexpr int NLD = (kTile * ROWB) / (64 * 16);  // load instructions per tensor and tile
+  constexpr int LPR = ROWB / 16;                   // lanes per row
+  constexpr int RPL = 64 / LPR;                    // rows per load instruction
   const int ld_row = lane / LPR;
   const int ld_chunk = lane % LPR;
 
   u32x4 kreg[NLD], vreg[NLD];
   float ksc[2][4], vsc[2][4];
 
-  // loads of tile `tile` of segment s into kreg/vreg (and its fp8 scales).
+  // loads of tile `tile` of segment s into kreg/vreg (and its K/V scales).
   // The tile's first row is wave-uniform: it becomes the base of a buffer
   // resource whose range ends at the segment's last valid row, so rows past
   // the end read as zero without a memory access (a cache tail may hold NaN)
   // and each load needs only a 32-bit lane offset.
-  constexpr int ROWB = FP8 ? D : 2 * D;  // bytes per cache row
   const unsigned lane_off = ld_row * ROWB + ld_chunk * 16;
   auto issue_loads = [&](Segment& s, int tile) {
     const int tt0 = s.t_begin + tile * kTile;
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       kreg[u] = buffer_load_x4_nt(rk, lane_off + u * RPL * ROWB);
       vreg[u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
     }
-    if constexpr (FP8) {
+    if constexpr (QUANT) {
       // lane (q4, .) needs the scales of rows 16h + 4q4 + i; rows past the end
       // read zero, and their scores are masked anyway
       const auto rks = make_rsrc(a.k_scale + row0, nvalid * 4);
@@ -354,11 +361,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     return uniform(__shfl(v, 0, 64));
   };
 
-  // Stage the tile whose loads were issued last into the wave's LDS slab and
-  // take over its fp8 scales.
+  // Stage the tile whose loads were issued last into the wave's LDS slab as
+  // bf16 (quantized codes are converted exactly) and take over its scales.
   float kscur[2][4], vscur[2][4];
   auto stage = [&]() {
-    if constexpr (FP8) {
+    if constexpr (QUANT) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int r = u * RPL + ld_row;
-      if constexpr (FP8) {
+      if constexpr (KVF == kKvFp8) {
         // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
         const int c0 = 2 * ld_chunk;
         u32x2 t0 = e4m3x4_to_bf16x4(kreg[u][0]), t1 = e4m3x4_to_bf16x4(kreg[u][1]);
@@ -389,6 +396,26 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
         lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
         lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
+      } else if constexpr (KVF == kKvInt8) {
+        // 16 codes -> logical bf16 chunks 2c, 2c+1 of row r
+        const int c0 = 2 * ld_chunk;
+        const int sw = swz<CH>(r);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x2 k0 = i8x4_to_bf16x4(kreg[u][2 * h]), k1 = i8x4_to_bf16x4(kreg[u][2 * h + 1]);
+          const u32x2 v0 = i8x4_to_bf16x4(vreg[u][2 * h]), v1 = i8x4_to_bf16x4(vreg[u][2 * h + 1]);
+          lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{k0[0], k0[1], k1[0], k1[1]});
+          lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{v0[0], v0[1], v1[0], v1[1]});
+        }
+      } else if constexpr (KVF == kKvInt4) {
+        // 32 codes -> logical bf16 chunks 4c .. 4c+3 of row r (one per dword)
+        const int c0 = 4 * ld_chunk;
+        const int sw = swz<CH>(r);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[u][h]));
+          lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(vreg[u][h]));
+        }
       } else {
         const int pc = ld_chunk ^ swz<CH>(r);
         lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
@@ -544,7 +571,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
               float x = sc[h][hb][i];
-              if constexpr (FP8) x *= kscur[h][i];  // the per-token K scale (> 0)
+              if constexpr (QUANT) x *= kscur[h][i];  // the per-token K scale (> 0)
               sv[h][i] = x;
             }
           if (tail) {
@@ -574,7 +601,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
               psum += p[h][i];
             }
           l[hb] = l[hb] * alpha[hb] + psum;
-          if constexpr (FP8) {
+          if constexpr (QUANT) {
   #pragma unroll
             for (int h = 0; h < 2; ++h)
   #pragma unroll
@@ -969,16 +996,21 @@ static void launch_split(const DecodeArgs& a, int D, int hb, int kind, int W, hi
     return;
   }
   const dim3 block(kWavesMfma * 64);
-#define GQA_LAUNCH_DECODE(DD, HH, F8) \
-  hipLaunchKernelGGL((gqa_decode_split_mfma<DD, HH, F8, kWavesMfma, PAGED>), grid, block, 0, stream, a)
-  const bool fp8 = kind == 2;
-  if (D == 64) {
-    if (hb == 1) { if (fp8) GQA_LAUNCH_DECODE(64, 1, true); else GQA_LAUNCH_DECODE(64, 1, false); }
-    else { if (fp8) GQA_LAUNCH_DECODE(64, 2, true); else GQA_LAUNCH_DECODE(64, 2, false); }
-  } else {
-    if (hb == 1) { if (fp8) GQA_LAUNCH_DECODE(128, 1, true); else GQA_LAUNCH_DECODE(128, 1, false); }
-    else { if (fp8) GQA_LAUNCH_DECODE(128, 2, true); else GQA_LAUNCH_DECODE(128, 2, false); }
+#define GQA_LAUNCH_DECODE(DD, HH, F) \
+  hipLaunchKernelGGL((gqa_decode_split_mfma<DD, HH, F, kWavesMfma, PAGED>), grid, block, 0, stream, a)
+#define GQA_LAUNCH_DECODE_KVF(DD, HH)                     \
+  switch (kind) {                                         \
+    case 2: GQA_LAUNCH_DECODE(DD, HH, kKvFp8); break;     \
+    case 3: GQA_LAUNCH_DECODE(DD, HH, kKvInt8); break;    \
+    case 4: GQA_LAUNCH_DECODE(DD, HH, kKvInt4); break;    \
+    default: GQA_LAUNCH_DECODE(DD, HH, kKvBf16); break;   \
   }
+  if (D == 64) {
+    if (hb == 1) GQA_LAUNCH_DECODE_KVF(64, 1) else GQA_LAUNCH_DECODE_KVF(64, 2)
+  } else {
+    if (hb == 1) GQA_LAUNCH_DECODE_KVF(128, 1) else GQA_LAUNCH_DECODE_KVF(128, 2)
+  }
+#undef GQA_LAUNCH_DECODE_KVF
 #undef GQA_LAUNCH_DECODE
 }
 

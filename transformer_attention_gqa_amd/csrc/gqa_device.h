@@ -81,6 +81,26 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Four signed int8 codes (one dword, code i in byte i) -> four bf16 values;
+// exact (|code| <= 128 needs 8 significant bits).
+__device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
+  const float f0 = (float)((int)(w << 24) >> 24), f1 = (float)((int)(w << 16) >> 24);
+  const float f2 = (float)((int)(w << 8) >> 24), f3 = (float)((int)w >> 24);
+  u32x2 r;
+  r[0] = pack_bf16x2(f0, f1);
+  r[1] = pack_bf16x2(f2, f3);
+  return r;
+}
+
+// Eight signed int4 codes (one dword, code i in bits 4i .. 4i+3, two's
+// complement) -> eight bf16 values, exact.
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (float)((int)(w << (28 - 4 * i)) >> 28);
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }

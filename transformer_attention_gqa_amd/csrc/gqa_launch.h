@@ -45,7 +45,8 @@ struct CombineArgs {
   int B, h_q, n_kv, S_max, n_hchunk, heads_per_chunk, tile, W;
 };
 
-// kind: 0 = float32 Q/K/V, 1 = bf16 Q/K/V, 2 = bf16 Q with e4m3 K/V.
+// kind: 0 = float32 Q/K/V, 1 = bf16 Q/K/V; bf16 Q with 2 = e4m3, 3 = int8 or
+// 4 = packed int4 K/V (each with per-row scales).
 // hb: 16-head blocks per workgroup on the matrix-core paths (1 or 2).
 // W: number of workgroups (balanced key ranges).
 hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream);

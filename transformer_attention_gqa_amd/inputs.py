@@ -91,6 +91,13 @@ GQA_FP8KV = DecodeWorkload("gqa_decode_fp8kv", B=32, h_q=64, n_kv=8, d_h=128, S_
                            q_dtype="bf16", kv_dtype="fp8", lens=(32768, 32768), seed=5)
 
 DECODE_WORKLOADS = {w.name: w for w in (MQA_TINY_F32, GQA_RAGGED_BF16, MQA_LONG_BF16, GQA_FP8KV)}
+
+# The fp8-cache workload's shape with int8 and packed int4 caches.
+GQA_INT8KV = DecodeWorkload("gqa_decode_int8kv", B=32, h_q=64, n_kv=8, d_h=128, S_max=32768,
+                            q_dtype="bf16", kv_dtype="int8", lens=(32768, 32768), seed=6)
+GQA_INT4KV = DecodeWorkload("gqa_decode_int4kv", B=32, h_q=64, n_kv=8, d_h=128, S_max=32768,
+                            q_dtype="bf16", kv_dtype="int4", lens=(32768, 32768), seed=7)
+QUANT_DECODE_WORKLOADS = {w.name: w for w in (GQA_INT8KV, GQA_INT4KV)}
 PREFILL_WORKLOADS = {GQA_PREFILL_BF16.name: GQA_PREFILL_BF16}
 
 

@@ -20,7 +20,8 @@ Causal prefill FLOPs count only the key/query pairs the causal mask keeps:
 S (S + 1) / 2 pairs per (batch, query head), 4 * d_h flops each.
 """
 
-ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1, "int4": 0.5}
+QUANTIZED = ("fp8", "int8", "int4")  # caches with per-(token, kv-head) float32 scales
 
 # MI355X published peaks (dense).
 HBM_PEAK_GBPS = 8000.0
@@ -45,12 +46,12 @@ def kv_fraction_of_mha(n_kv, h):
 def decode_kv_bytes(kv_dtype, n_kv, d_h, seq_lens):
     """KV bytes one decode call must read (L = 1 layer, sum over ragged lengths)."""
     total = sum(int(x) for x in seq_lens)
-    return kv_cache_bytes(ELEMENT_BYTES[kv_dtype], 1, n_kv, d_h, total, 1)
+    return int(kv_cache_bytes(ELEMENT_BYTES[kv_dtype], 1, n_kv, d_h, total, 1))
 
 
 def decode_scale_bytes(kv_dtype, n_kv, seq_lens):
-    """fp8 cache only: the float32 per-(token, kv-head) scales of K and V."""
-    if kv_dtype != "fp8":
+    """Quantized caches only: the float32 per-(token, kv-head) scales of K and V."""
+    if kv_dtype not in QUANTIZED:
         return 0
     return 2 * 4 * n_kv * sum(int(x) for x in seq_lens)
 
