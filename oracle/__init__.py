@@ -28,6 +28,8 @@ Modules:
   attention  -- the decode and causal-prefill definitions.
   paged      -- decode over a paged cache ("Multi-Query Attention (MQA)"
                 glossary, "PagedAttention").
+  mla        -- absorbed multi-head latent attention decode ("Evolution of AI
+                Attention Mechanisms", "Generation 3: MLA").
 
 Pinning: every function here is checked by `-m "not gpu"` tests against
 closed forms, invariants the pages fix, a library routine that computes the
@@ -35,7 +37,7 @@ same definition, and brute force on tiny inputs.  No function is parity
 unpinned.
 """
 
-from . import attention, codecs, paged  # noqa: F401
+from . import attention, codecs, mla, paged  # noqa: F401
 from .attention import (  # noqa: F401
     attend_one_row,
     decode,
@@ -51,4 +53,5 @@ from .codecs import (  # noqa: F401
     int4_unpack,
     int8_to_f64,
 )
+from .mla import mla_decode  # noqa: F401
 from .paged import decode_paged, gather_logical_cache  # noqa: F401

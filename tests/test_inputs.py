@@ -63,3 +63,12 @@ def test_int_cache_generator_shapes_and_poison(kind):
     assert pin.k_pages.shape[-1] == dc and pin.k_pages.dtype == want
     spare = sorted(set(range(pin.num_pages)) - {int(x) for x in pin.block_table.flatten()})
     assert torch.isnan(pin.k_scale_pages[spare]).all()
+
+
+def test_mla_inputs():
+    wl = inputs.MlaWorkload("m", B=2, h_q=32, d_c=64, S_max=40, lens=(1, 40), seed=3)
+    x = inputs.make_mla_inputs(wl, seq_lens=[40, 7], poison_tail=True)
+    assert x.q.shape == (2, 32, 64) and x.c_kv.shape == (2, 40, 64) and x.c_kv.dtype == torch.bfloat16
+    assert torch.isnan(x.c_kv[1, 7:]).all() and torch.isfinite(x.c_kv[1, :7]).all()
+    y = inputs.make_mla_inputs(wl, seq_lens=[40, 7], poison_tail=True)
+    assert torch.equal(x.q, y.q)

@@ -102,6 +102,55 @@ PREFILL_WORKLOADS = {GQA_PREFILL_BF16.name: GQA_PREFILL_BF16}
 
 
 @dataclass(frozen=True)
+class MlaWorkload:
+    """Absorbed multi-head latent attention decode: h query heads (already
+    moved into the latent space) over one latent cache row of d_c values per
+    token, which serves as both keys and values."""
+    name: str
+    B: int
+    h_q: int
+    d_c: int
+    S_max: int
+    lens: Tuple[int, int]
+    seed: int
+
+    @property
+    def scale(self):
+        return 1.0 / float(self.d_c) ** 0.5  # the latent dimension, as in the absorbed form's code
+
+
+# 32 heads over a 512-value latent (the MLA module's defaults), ragged lengths.
+MLA_DECODE_BF16 = MlaWorkload("mla_decode_bf16", B=32, h_q=32, d_c=512, S_max=16384, lens=(4096, 16384), seed=8)
+MLA_WORKLOADS = {MLA_DECODE_BF16.name: MLA_DECODE_BF16}
+
+
+@dataclass
+class MlaInputs:
+    wl: MlaWorkload
+    q: torch.Tensor         # [B, h_q, d_c] bf16 (absorbed queries)
+    c_kv: torch.Tensor      # [B, S_max, d_c] bf16 latent cache
+    seq_lens: torch.Tensor  # [B] int32
+
+
+def make_mla_inputs(wl, device="cpu", seq_lens=None, poison_tail=False, seed=None):
+    seed = wl.seed if seed is None else seed
+    g = _gen(device, seed)
+    if seq_lens is None:
+        lens = draw_lengths(wl.B, wl.lens[0], wl.lens[1], seed)
+    else:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int32).reshape(wl.B)
+    q = torch.randn((wl.B, wl.h_q, wl.d_c), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty((wl.B, wl.S_max, wl.d_c), dtype=torch.bfloat16, device=device)
+    for b in range(wl.B):
+        c[b] = torch.randn((wl.S_max, wl.d_c), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    if poison_tail:
+        for b in range(wl.B):
+            n = int(min(max(int(lens[b]), 0), wl.S_max))
+            c[b, n:] = float("nan")
+    return MlaInputs(wl, q, c, lens.to(device))
+
+
+@dataclass(frozen=True)
 class PagedDecodeWorkload:
     """A decode workload whose cache lives in a pool of fixed-size pages."""
     name: str
