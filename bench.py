@@ -264,6 +264,55 @@ def bench_decode_paged(pwl, steps, warmup, use_graph=False):
     }
 
 
+def bench_decode_mla(wl, steps, warmup, use_graph=False):
+    """attn_decode_mla (absorbed latent attention): a step reads the visible
+    latent rows once (they are the keys and the values of every head)."""
+    dev = torch.device("cuda")
+    x = inputs.make_mla_inputs(wl, device=dev)
+    lens = x.seq_lens.cpu().tolist()
+    nbytes = roofline.mla_latent_bytes(wl.d_c, lens)
+    cache_bytes = x.c_kv.numel() * x.c_kv.element_size()
+    ncopies = min(16, max(2, math.ceil(4 * MALL_BYTES / cache_bytes) + 1))
+    cs = [x.c_kv] + [x.c_kv.clone() for _ in range(ncopies - 1)]
+    desc = binding.mla_desc(x.q, x.c_kv)
+    ws = torch.empty(binding.attn_decode_mla_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x.q)
+    calls = [binding.prepare_decode_mla(x.q, cs[c], x.seq_lens, wl.scale, out, ws) for c in range(ncopies)]
+    part_calls = [binding.prepare_decode_mla_partials(x.q, cs[c], x.seq_lens, wl.scale, ws) for c in range(ncopies)]
+
+    def step(i):
+        calls[i % ncopies]()
+
+    def partials(i):
+        part_calls[i % ncopies]()
+
+    ms_step, ev_ms = time_steps(step, steps, warmup, use_graph)
+    _, kernel_ms = time_steps(partials, steps, 2, use_graph)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    flops = roofline.mla_flops(wl.h_q, wl.d_c, lens)
+    return {
+        "workload": wl.name,
+        "value": nbytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "ms_per_step": ms_step,
+        "pct_hbm_peak": 100.0 * nbytes / (ms_step * 1e-3) / 1e9 / roofline.HBM_PEAK_GBPS,
+        "latent_bytes": nbytes,
+        "sum_L": int(sum(lens)),
+        "n_split": binding.attn_decode_mla_num_splits(desc),
+        "kv_copies_rotated": ncopies,
+        "event_ms_per_step": ev_ms,
+        "split_kernel_ms": kernel_ms,
+        "combine_ms_approx": ev_ms - kernel_ms,
+        "split_kernel_tflops": flops / (kernel_ms * 1e-3) / 1e12,
+        "roofline": {"bound": "hbm", "kernel": "gqa_mla_decode_split", "achieved": achieved,
+                     "peak": roofline.HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / roofline.HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(f"mla_decode_split:{wl.name}")},
+        "dtype": "bf16",
+        "config": {"workload": wl.name, "B": wl.B, "h_q": wl.h_q, "d_c": wl.d_c, "S_max": wl.S_max,
+                   "seed": wl.seed},
+    }
+
+
 def bench_prefill(wl, steps, warmup, use_graph=False):
     dev = torch.device("cuda")
     x = inputs.make_prefill_inputs(wl, device=dev)
@@ -411,6 +460,18 @@ def _workload_launches():
         grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
         out.append((("gqa_decode_combine", (str(wl.d_h), "true"), grid),
                     (f"decode_combine:{pwl.name}", pwl.name, None, None)))
+    for wl in inputs.MLA_WORKLOADS.values():
+        qd = torch.empty((wl.B, wl.h_q, wl.d_c), dtype=torch.bfloat16, device="meta")
+        cd = torch.empty((wl.B, wl.S_max, wl.d_c), dtype=torch.bfloat16, device="meta")
+        ns = binding.attn_decode_mla_num_splits(binding.mla_desc(qd, cd))
+        hpc = 64 if wl.h_q > 32 else 32
+        lens = inputs.draw_lengths(wl.B, *wl.lens, wl.seed).tolist()
+        out.append((("gqa_mla_decode_split", (str(wl.d_c), str(hpc // 32)), ns * 512),
+                    (f"mla_decode_split:{wl.name}", wl.name, roofline.mla_latent_bytes(wl.d_c, lens), "bytes")))
+        n_slabs = wl.B * -(-wl.h_q // hpc)
+        grid = n_slabs * -(-(hpc * wl.d_c // 4) // 256) * 256
+        out.append((("gqa_decode_combine", (str(wl.d_c), "true"), grid),
+                    (f"decode_combine:{wl.name}", wl.name, None, None)))
     for wl in inputs.PREFILL_WORKLOADS.values():
         G = wl.h_q // wl.n_kv
         hc = math.gcd(G, 8)
@@ -547,7 +608,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=MAIN, choices=sorted(inputs.DECODE_WORKLOADS) + sorted(
-        inputs.QUANT_DECODE_WORKLOADS) + sorted(inputs.PAGED_WORKLOADS) + sorted(inputs.PREFILL_WORKLOADS))
+        inputs.QUANT_DECODE_WORKLOADS) + sorted(inputs.PAGED_WORKLOADS) + sorted(inputs.MLA_WORKLOADS) + sorted(
+        inputs.PREFILL_WORKLOADS))
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -585,6 +647,8 @@ def main(argv=None):
             return bench_prefill(inputs.PREFILL_WORKLOADS[name], steps, warmup, use_graph)
         if name in inputs.PAGED_WORKLOADS:
             return bench_decode_paged(inputs.PAGED_WORKLOADS[name], steps, warmup, use_graph)
+        if name in inputs.MLA_WORKLOADS:
+            return bench_decode_mla(inputs.MLA_WORKLOADS[name], steps, warmup, use_graph)
         wl = {**inputs.DECODE_WORKLOADS, **inputs.QUANT_DECODE_WORKLOADS}[name]
         return bench_decode(wl, steps, warmup, use_graph, args.n_split)
 
@@ -592,7 +656,7 @@ def main(argv=None):
     others = {}
     if not args.only_main:
         for name in (list(inputs.DECODE_WORKLOADS) + list(inputs.QUANT_DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS)
-                     + list(inputs.PREFILL_WORKLOADS)):
+                     + list(inputs.MLA_WORKLOADS) + list(inputs.PREFILL_WORKLOADS)):
             if name == args.workload:
                 continue
             others[name] = run(name, max(5, min(args.steps, 20)), 2)

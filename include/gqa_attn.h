@@ -194,6 +194,51 @@ gqa_status attn_decode_paged(const gqa_paged_desc* d, const void* q, const void*
                              const int32_t* seq_lens, float scale, void* out, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------- latent-attention decode --
+ * One decode step of multi-head latent attention in its absorbed form
+ * ("Evolution of AI Attention Mechanisms", section "Generation 3: MLA"): the
+ * cache holds one latent vector c_kv of d_c values per token, and each head's
+ * query has already been moved into the latent space (q_abs,h = W_k,h^T q_h,
+ * with W_k,h the head's rows of the key up-projection).  Every head then
+ * attends to the latent rows, which serve as its keys and its values:
+ *
+ *     o_c,h = softmax(scale * q_abs,h . c_kv^T) c_kv   (over the L_b tokens)
+ *
+ * The value up-projection W_v,h and the output projection are applied by the
+ * caller afterwards.  This is MQA with one shared K = V head of width d_c.
+ *
+ * Shapes (row-major, innermost last):
+ *   q_abs    [B, h_q, d_c]    bfloat16
+ *   c_kv     [B, S_max, d_c]  bfloat16
+ *   seq_lens [B] int32 (device), clamped to [0, S_max]; L_b = 0 gives a
+ *            zero row
+ *   out      [B, h_q, d_c]    bfloat16
+ * d_c = 256 or 512; dtype must be GQA_BF16.  Products on bf16 matrix cores
+ * with float32 accumulation; each latent row is read from memory once for
+ * both products and for all heads (up to 64 heads per pass over the cache;
+ * h_q > 64 takes ceil(h_q / 64) passes).  Split, workspace and
+ * reproducibility are those of attn_decode, with slabs (sequence, chunk of
+ * up to 64 heads) and 32-token tiles.
+ */
+typedef struct gqa_mla_desc {
+  int32_t B, h_q, S_max, d_c;
+  int32_t dtype;   /* GQA_BF16 */
+  int32_t n_split; /* as in gqa_decode_desc */
+} gqa_mla_desc;
+
+int32_t attn_decode_mla_num_splits(const gqa_mla_desc* d);
+size_t attn_decode_mla_workspace_bytes(const gqa_mla_desc* d);
+gqa_status attn_decode_mla(const gqa_mla_desc* d, const void* q_abs, const void* c_kv, const int32_t* seq_lens,
+                           float scale, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* The two halves of attn_decode_mla (split kernel, then combine kernel),
+ * with the same roles and arguments as attn_decode_partials and
+ * attn_decode_combine. */
+gqa_status attn_decode_mla_partials(const gqa_mla_desc* d, const void* q_abs, const void* c_kv,
+                                    const int32_t* seq_lens, float scale, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+gqa_status attn_decode_mla_combine(const gqa_mla_desc* d, const int32_t* seq_lens, const void* workspace,
+                                   size_t workspace_bytes, void* out, hipStream_t stream);
+
 /* ------------------------------------------------------- causal prefill --
  * Causal self-attention over whole prompts, the mode of the library call
  * flash_attn_func(q, k, v, causal=True, softmax_scale=...) in "Flash

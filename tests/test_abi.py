@@ -212,3 +212,54 @@ def test_int_caches_are_accepted_with_scales(lib, kt):
     assert call_decode(lib, desc, ks=ALIGNED, vs=MISALIGNED) == 4
     assert call_decode(lib, dd(qt=0, kt=kt)) == 3
     assert call_paged(lib, pgd(kt=kt), ks=None, vs=None) == 1
+
+
+def mld(B=2, h_q=32, S=64, d_c=512, dt=1, ns=0):
+    return binding.gqa_mla_desc(B, h_q, S, d_c, dt, ns)
+
+
+def call_mla(lib, desc, q=ALIGNED, c=ALIGNED, lens=ALIGNED, out=ALIGNED, ws=ALIGNED, ws_bytes=None, scale=1.0):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_mla_workspace_bytes(ctypes.byref(desc)) if desc is not None else 0
+    p = ctypes.byref(desc) if desc is not None else None
+    return lib.attn_decode_mla(p, q, c, lens, scale, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(B=0), 2), (dict(h_q=0), 2), (dict(S=-3), 2), (dict(d_c=128), 2), (dict(d_c=576), 2), (dict(ns=-1), 2),
+    (dict(dt=0), 3), (dict(dt=2), 3),
+])
+def test_mla_descriptor_errors(lib, bad, code):
+    desc = mld(**bad)
+    assert call_mla(lib, desc) == code
+    assert lib.attn_decode_mla_workspace_bytes(ctypes.byref(desc)) == 0
+    assert lib.attn_decode_mla_num_splits(ctypes.byref(desc)) == -1
+
+
+def test_mla_pointer_and_value_errors(lib):
+    desc = mld()
+    assert call_mla(lib, None) == 1
+    assert call_mla(lib, desc, q=None) == 1
+    assert call_mla(lib, desc, c=None) == 1
+    assert call_mla(lib, desc, lens=None) == 1
+    assert call_mla(lib, desc, out=None) == 1
+    assert call_mla(lib, desc, c=MISALIGNED) == 4
+    assert call_mla(lib, desc, lens=ALIGNED + 2) == 4
+    assert call_mla(lib, desc, ws=None) == 5
+    assert call_mla(lib, desc, ws_bytes=16) == 5
+    assert call_mla(lib, desc, scale=float("inf")) == 7
+
+
+def test_mla_plan(lib):
+    """Head chunks of up to 64 heads; the workspace holds (W + slabs) rows of
+    d_c partial values per chunk head plus (m, l), like the decode workspace."""
+    for B, h_q, S, d_c, ns in ((32, 32, 16384, 512, 0), (4, 16, 100, 256, 0), (3, 96, 1000, 512, 5),
+                               (1, 128, 64, 512, 10 ** 6)):
+        desc = mld(B=B, h_q=h_q, S=S, d_c=d_c, ns=ns)
+        hpc = 64 if h_q > 32 else 32
+        slabs = B * -(-h_q // hpc)
+        W = min(ns or 256, slabs * -(-S // 32))
+        assert lib.attn_decode_mla_num_splits(ctypes.byref(desc)) == W
+        rows = (W + slabs) * hpc
+        o_bytes = -(-rows * d_c * 4 // 256) * 256
+        assert lib.attn_decode_mla_workspace_bytes(ctypes.byref(desc)) == o_bytes + rows * 8

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     GqaError,
     attn_decode,
     attn_decode_combine,
+    attn_decode_mla,
     attn_decode_num_splits,
     attn_decode_partials,
     attn_decode_workspace_bytes,

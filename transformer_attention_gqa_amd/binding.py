@@ -23,7 +23,8 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE"
           5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE"}
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
             "attn_decode_combine", "attn_decode_paged_num_splits", "attn_decode_paged_workspace_bytes",
-            "attn_decode_paged", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
+            "attn_decode_paged", "attn_decode_mla_num_splits", "attn_decode_mla_workspace_bytes",
+            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
 
 
 class GqaError(RuntimeError):
@@ -42,6 +43,11 @@ class gqa_paged_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+
+
+class gqa_mla_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("S_max", ctypes.c_int32), ("d_c", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
 
 
 class gqa_prefill_desc(ctypes.Structure):
@@ -76,6 +82,15 @@ def load_library(path=LIB_PATH):
     lib.attn_decode_paged_workspace_bytes.argtypes, lib.attn_decode_paged_workspace_bytes.restype = [gd], sz
     lib.attn_decode_paged.argtypes = [gd, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]
     lib.attn_decode_paged.restype = ctypes.c_int
+    md = ctypes.POINTER(gqa_mla_desc)
+    lib.attn_decode_mla_num_splits.argtypes, lib.attn_decode_mla_num_splits.restype = [md], i32
+    lib.attn_decode_mla_workspace_bytes.argtypes, lib.attn_decode_mla_workspace_bytes.restype = [md], sz
+    lib.attn_decode_mla.argtypes = [md, vp, vp, vp, f32, vp, vp, sz, vp]
+    lib.attn_decode_mla.restype = ctypes.c_int
+    lib.attn_decode_mla_partials.argtypes = [md, vp, vp, vp, f32, vp, sz, vp]
+    lib.attn_decode_mla_partials.restype = ctypes.c_int
+    lib.attn_decode_mla_combine.argtypes = [md, vp, vp, sz, vp, vp]
+    lib.attn_decode_mla_combine.restype = ctypes.c_int
     lib.attn_prefill_causal.argtypes = [pd, vp, vp, vp, f32, vp, vp]
     lib.attn_prefill_causal.restype = ctypes.c_int
     lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [ctypes.c_int], cp
@@ -331,6 +346,74 @@ def prepare_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out,
             _ptr(block_table), _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
             ctypes.c_size_t(ws_bytes))
     call = PreparedCall(lib.attn_decode_paged, args, stream, out)
+    call._keep = (desc,)
+    return call
+
+
+def mla_desc(q_abs, c_kv, n_split=0):
+    """Descriptor for q_abs [B, h_q, d_c] and c_kv [B, S_max, d_c]."""
+    B, h_q, d_c = q_abs.shape
+    return gqa_mla_desc(B, h_q, c_kv.shape[1], d_c, _dtype_code(q_abs), n_split)
+
+
+def attn_decode_mla_num_splits(desc):
+    return load_library().attn_decode_mla_num_splits(ctypes.byref(desc))
+
+
+def attn_decode_mla_workspace_bytes(desc):
+    return load_library().attn_decode_mla_workspace_bytes(ctypes.byref(desc))
+
+
+def _mla_checks(q_abs, c_kv, seq_lens, out):
+    _require(q_abs, "q_abs", 3)
+    _require(c_kv, "c_kv", 3)
+    if c_kv.dtype != q_abs.dtype or c_kv.shape[0] != q_abs.shape[0] or c_kv.shape[2] != q_abs.shape[2]:
+        raise ValueError("c_kv must be [B, S_max, d_c] typed and sized like q_abs [B, h_q, d_c]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q_abs.shape[0],) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor of shape [B]")
+    if out.shape != q_abs.shape or out.dtype != q_abs.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q_abs")
+
+
+def attn_decode_mla(q_abs, c_kv, seq_lens, scale, out=None, workspace=None, n_split=0, stream=None):
+    """o_c[B, h_q, d_c] = absorbed latent-attention decode step (see attn_decode_mla in gqa_attn.h)."""
+    if out is None:
+        out = torch.empty_like(q_abs)
+    _mla_checks(q_abs, c_kv, seq_lens, out)
+    desc = mla_desc(q_abs, c_kv, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(attn_decode_mla_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                device=q_abs.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().attn_decode_mla(ctypes.byref(desc), _ptr(q_abs), _ptr(c_kv), _ptr(seq_lens),
+                                          float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def prepare_decode_mla(q_abs, c_kv, seq_lens, scale, out, workspace, n_split=0, stream=None):
+    """PreparedCall of attn_decode_mla."""
+    _mla_checks(q_abs, c_kv, seq_lens, out)
+    desc = mla_desc(q_abs, c_kv, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < attn_decode_mla_workspace_bytes(desc):
+        raise ValueError("workspace smaller than attn_decode_mla_workspace_bytes")
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q_abs), _ptr(c_kv), _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+            _ptr(workspace), ctypes.c_size_t(ws_bytes))
+    call = PreparedCall(lib.attn_decode_mla, args, stream, out)
+    call._keep = (desc,)
+    return call
+
+
+def prepare_decode_mla_partials(q_abs, c_kv, seq_lens, scale, workspace, n_split=0, stream=None):
+    """PreparedCall of attn_decode_mla_partials (split kernel only)."""
+    _mla_checks(q_abs, c_kv, seq_lens, q_abs)
+    desc = mla_desc(q_abs, c_kv, n_split)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q_abs), _ptr(c_kv), _ptr(seq_lens), ctypes.c_float(scale), _ptr(workspace),
+            ctypes.c_size_t(ws_bytes))
+    call = PreparedCall(lib.attn_decode_mla_partials, args, stream)
     call._keep = (desc,)
     return call
 

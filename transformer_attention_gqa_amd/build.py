@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libgqa_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "decode.hip", "mla.hip", "prefill.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

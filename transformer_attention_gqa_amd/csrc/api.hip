@@ -199,6 +199,51 @@ gqa_status paged_to_decode_desc(const gqa_paged_desc* pd, gqa_decode_desc* d, in
   return validate_decode_desc(d);
 }
 
+// ---- absorbed latent-attention decode
+struct MlaPlan {
+  int hb;               // 32-head blocks per workgroup
+  int heads_per_chunk;  // 32 * hb
+  int n_hchunk;         // head chunks per sequence
+  long n_slabs;         // B * n_hchunk
+  int W;
+};
+
+gqa_status validate_mla_desc(const gqa_mla_desc* d) {
+  if (!d) return GQA_ERR_NULL;
+  if (d->B <= 0 || d->h_q <= 0 || d->S_max <= 0 || d->d_c <= 0 || d->n_split < 0) return GQA_ERR_SHAPE;
+  if (d->d_c != 256 && d->d_c != 512) return GQA_ERR_SHAPE;
+  if (d->dtype != GQA_BF16) return GQA_ERR_DTYPE;
+  if ((int64_t)d->B * d->h_q > (int64_t)1 << 30) return GQA_ERR_SHAPE;
+  if ((int64_t)d->B * d->S_max > (int64_t)1 << 40) return GQA_ERR_SHAPE;
+  if (d->S_max > (1 << 30)) return GQA_ERR_SHAPE;
+  return GQA_OK;
+}
+
+MlaPlan plan_mla(const gqa_mla_desc* d) {
+  MlaPlan p{};
+  p.hb = d->h_q > 32 ? 2 : 1;
+  p.heads_per_chunk = 32 * p.hb;
+  p.n_hchunk = (d->h_q + p.heads_per_chunk - 1) / p.heads_per_chunk;
+  p.n_slabs = (long)d->B * p.n_hchunk;
+  const long max_tiles = p.n_slabs * ((d->S_max + kTileMfma - 1) / kTileMfma);
+  long W = d->n_split > 0 ? (long)d->n_split : kDefaultWorkgroups;
+  if (W > max_tiles) W = max_tiles;
+  if (W > kMaxWorkgroups) W = kMaxWorkgroups;
+  if (W < 1) W = 1;
+  p.W = (int)W;
+  return p;
+}
+
+WorkspaceLayout mla_workspace_layout(const gqa_mla_desc* d, const MlaPlan& p) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)(p.W + p.n_slabs) * p.heads_per_chunk;
+  WorkspaceLayout l;
+  l.o_off = 0;
+  l.ml_off = up(rows * d->d_c * sizeof(float));
+  l.total = l.ml_off + rows * 2 * sizeof(float);
+  return l;
+}
+
 }  // namespace
 }  // namespace gqa
 
@@ -319,6 +364,94 @@ gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const v
     return GQA_ERR_HIP;
   }
   return GQA_OK;
+}
+
+int32_t attn_decode_mla_num_splits(const gqa_mla_desc* d) {
+  if (validate_mla_desc(d) != GQA_OK) return -1;
+  return plan_mla(d).W;
+}
+
+size_t attn_decode_mla_workspace_bytes(const gqa_mla_desc* d) {
+  if (validate_mla_desc(d) != GQA_OK) return 0;
+  return mla_workspace_layout(d, plan_mla(d)).total;
+}
+
+gqa_status attn_decode_mla_partials(const gqa_mla_desc* d, const void* q_abs, const void* c_kv,
+                                    const int32_t* seq_lens, float scale, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  gqa_status st = validate_mla_desc(d);
+  if (st != GQA_OK) return st;
+  if (!q_abs || !c_kv || !seq_lens) return GQA_ERR_NULL;
+  if (misaligned(q_abs) || misaligned(c_kv)) return GQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0) return GQA_ERR_ALIGN;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
+  const MlaPlan p = plan_mla(d);
+  const WorkspaceLayout wl = mla_workspace_layout(d, p);
+  if (!workspace || workspace_bytes < wl.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+  MlaArgs a;
+  a.q = q_abs;
+  a.c = c_kv;
+  a.seq_lens = seq_lens;
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+  a.qk_scale_log2 = (float)((double)scale * kLog2e);
+  a.B = d->B;
+  a.h_q = d->h_q;
+  a.S_max = d->S_max;
+  a.n_hchunk = p.n_hchunk;
+  a.heads_per_chunk = p.heads_per_chunk;
+  const hipError_t e = launch_mla_decode_split(a, d->d_c, p.hb, p.W, stream);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return GQA_ERR_HIP;
+  }
+  return GQA_OK;
+}
+
+gqa_status attn_decode_mla_combine(const gqa_mla_desc* d, const int32_t* seq_lens, const void* workspace,
+                                   size_t workspace_bytes, void* out, hipStream_t stream) {
+  gqa_status st = validate_mla_desc(d);
+  if (st != GQA_OK) return st;
+  if (!seq_lens || !out) return GQA_ERR_NULL;
+  if (misaligned(out)) return GQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0) return GQA_ERR_ALIGN;
+  const MlaPlan p = plan_mla(d);
+  const WorkspaceLayout wl = mla_workspace_layout(d, p);
+  if (!workspace || workspace_bytes < wl.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+  // the GQA combine with one K/V head: slab (b, hc) merges into heads
+  // hc * heads_per_chunk ... of sequence b
+  CombineArgs c;
+  c.part_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + wl.o_off);
+  c.part_ml = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + wl.ml_off);
+  c.seq_lens = seq_lens;
+  c.out = out;
+  c.B = d->B;
+  c.h_q = d->h_q;
+  c.n_kv = 1;
+  c.S_max = d->S_max;
+  c.n_hchunk = p.n_hchunk;
+  c.heads_per_chunk = p.heads_per_chunk;
+  c.tile = kTileMfma;
+  c.W = p.W;
+  const hipError_t e = launch_decode_combine(c, d->d_c, true, stream);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return GQA_ERR_HIP;
+  }
+  return GQA_OK;
+}
+
+gqa_status attn_decode_mla(const gqa_mla_desc* d, const void* q_abs, const void* c_kv, const int32_t* seq_lens,
+                           float scale, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  gqa_status st = validate_mla_desc(d);
+  if (st != GQA_OK) return st;
+  if (!out) return GQA_ERR_NULL;
+  if (misaligned(out)) return GQA_ERR_ALIGN;
+  st = attn_decode_mla_partials(d, q_abs, c_kv, seq_lens, scale, workspace, workspace_bytes, stream);
+  if (st != GQA_OK) return st;
+  return attn_decode_mla_combine(d, seq_lens, workspace, workspace_bytes, out, stream);
 }
 
 const char* gqa_status_string(gqa_status s) {

@@ -45,11 +45,27 @@ struct CombineArgs {
   int B, h_q, n_kv, S_max, n_hchunk, heads_per_chunk, tile, W;
 };
 
+// Absorbed latent-attention decode: one latent row c[b][t][0..D) per token
+// serves as key and value of every query head.  Slabs are (sequence b, head
+// chunk hc), n_hchunk per sequence, and use the decode schedule and partial
+// layout above (n_kv = 1).
+struct MlaArgs {
+  const void* q;   // [B][h_q][D] bf16, absorbed queries
+  const void* c;   // [B][S_max][D] bf16, latent cache
+  const int32_t* seq_lens;
+  float* part_o;   // [W + n_slabs][heads_per_chunk][D]
+  float* part_ml;  // [W + n_slabs][heads_per_chunk][2]
+  float qk_scale_log2;
+  int B, h_q, S_max, n_hchunk, heads_per_chunk;
+};
+
 // kind: 0 = float32 Q/K/V, 1 = bf16 Q/K/V; bf16 Q with 2 = e4m3, 3 = int8 or
 // 4 = packed int4 K/V (each with per-row scales).
 // hb: 16-head blocks per workgroup on the matrix-core paths (1 or 2).
 // W: number of workgroups (balanced key ranges).
 hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int W, hipStream_t stream);
+// hb: 32-head blocks per workgroup (1 or 2); D = 256 or 512.
+hipError_t launch_mla_decode_split(const MlaArgs& a, int D, int hb, int W, hipStream_t stream);
 hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream);
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S, int h_q, int n_kv, int D, hipStream_t stream);

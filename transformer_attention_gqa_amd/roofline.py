@@ -16,6 +16,12 @@ Per-layer KV-cache size ("Evolution of AI Attention Mechanisms", section
 keeping one K/V head and GQA keeping g of them ("MQA (Multi-Query
 Attention)" and "GQA (Grouped-Query Attention)" sections).
 
+Latent attention ("Evolution of AI Attention Mechanisms", section
+"Generation 3: MLA"): the cache keeps one latent vector of d_c values per
+token instead of per-head keys and values; in the absorbed decode that row is
+both key and value of every head, so a step reads it once:
+2 * d_c * sum L bytes in bf16, for 4 * h_q * d_c flops per token.
+
 Causal prefill FLOPs count only the key/query pairs the causal mask keeps:
 S (S + 1) / 2 pairs per (batch, query head), 4 * d_h flops each.
 """
@@ -58,6 +64,16 @@ def decode_scale_bytes(kv_dtype, n_kv, seq_lens):
 
 def decode_flops(h_q, d_h, seq_lens):
     return 4 * h_q * d_h * sum(int(x) for x in seq_lens)
+
+
+def mla_latent_bytes(d_c, seq_lens, bytes_per_elem=2):
+    """Latent-cache bytes one absorbed decode step must read."""
+    return int(bytes_per_elem * d_c * sum(int(x) for x in seq_lens))
+
+
+def mla_flops(h_q, d_c, seq_lens):
+    """Scores and weighted sum over the latent rows: 4 * h_q * d_c per token."""
+    return 4 * h_q * d_c * sum(int(x) for x in seq_lens)
 
 
 def prefill_causal_flops(B, S, h_q, d_h):
