@@ -52,11 +52,13 @@ def test_mla_matches_oracle(d_c, h_q):
     assert torch.count_nonzero(out[3]) == 0
 
 
-@pytest.mark.parametrize("n_split", [1, 2, 5, 31, 10 ** 6])
-def test_mla_split_counts(n_split):
-    """Ranges that cross sequence boundaries (few splits) and ranges of at
+@pytest.mark.parametrize("h_q,d_c", [(32, 512), (64, 256), (64, 512)])
+@pytest.mark.parametrize("n_split", [1, 2, 5, 7, 31, 10 ** 6])
+def test_mla_split_counts(n_split, h_q, d_c):
+    """Ranges that cross sequence boundaries at every position of the kernel's
+    rotation of in-flight tiles (few splits of 51 tiles), and ranges of at
     most one tile (more splits than tiles)."""
-    inp = inputs.make_mla_inputs(wl(B=3, h_q=32, d_c=512, S=1000, seed=310), device=DEV,
+    inp = inputs.make_mla_inputs(wl(B=3, h_q=h_q, d_c=d_c, S=1000, seed=310), device=DEV,
                                  seq_lens=[1000, 517, 64], poison_tail=True)
     check(inp, n_split=n_split)
 

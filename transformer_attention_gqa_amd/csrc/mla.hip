@@ -32,6 +32,8 @@ namespace {
 constexpr int kMlaTile = 32;   // tokens per tile
 constexpr int kMlaWaves = 8;   // wavefronts per workgroup
 constexpr float kMlaSlack = 8.0f;  // log2 units the running max may lag the true max
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // The tiles of one (sequence, head chunk) slab that a workgroup's range covers.
 struct MlaSegment {
@@ -112,10 +114,14 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
   // ---- tile loads: lane (row ld_row, chunk ld_chunk) of each instruction
   const int ld_row = lane / LPR, ld_chunk = lane % LPR;
   const unsigned lane_off = ld_row * (2 * D) + 2 * dsl + 16 * ld_chunk;
-  u32x4 creg[NLD];
+  // NSET register sets of NLD loads each: while a wave computes one tile
+  // from LDS, the next NSET tiles are in flight (64 heads at d_c = 512 leave
+  // registers for one set only)
+  constexpr int NSET = HB == 1 ? 3 : (D == 512 ? 1 : 2);
+  u32x4 cr0[NLD], cr1[NSET >= 2 ? NLD : 1], cr2[NSET == 3 ? NLD : 1];
   // a tile's first row is the base of a buffer resource that ends at the
   // segment's last valid row: rows past it read as zero without an access
-  auto issue = [&](const MlaSegment& s, int tile) {
+  auto issue = [&](u32x4* creg, const MlaSegment& s, int tile) {
     const int tt0 = s.t_begin + tile * kMlaTile;
     const size_t row0 = (size_t)uniform((long long)((size_t)s.b * a.S_max + tt0));
     const int nvalid = uniform(min(kMlaTile, s.t_end - tt0));
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
 #pragma unroll
     for (int u = 0; u < NLD; ++u) creg[u] = buffer_load_x4_nt(rc, lane_off + u * RPL * (2 * D));
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](const u32x4* creg, int buf) {
     wave_lds_fence();
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
@@ -180,24 +186,36 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
     }
   };
 
-  // ---- prologue: the first tile in LDS, the second in flight
+  // ---- prologue: the first tile in LDS, the next NSET in flight
   MlaSegment cur = mla_segment(a, ll, lo, hi, w, lane);
-  MlaSegment ld = cur;  // segment of the tile being loaded
+  MlaSegment ld = cur;  // segment of the tile issued last
   int cur0 = 0, ld0 = 0;  // local index of each segment's first tile
   load_q(cur);
-  issue(ld, 0);
-  stage(0);
-  auto prefetch = [&](int k) {  // issue local tile k (k <= n_local - 1)
+  // issue local tile k; past the range, loads against an empty buffer range
+  // (zeros, no memory access), so that every step issues the same loads
+  auto prefetch = [&](u32x4* creg, int k) {
+    if (k >= n_local) {
+      const auto none = make_rsrc(a.c, 0);
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) creg[u] = buffer_load_x4_nt(none, lane_off + u * RPL * (2 * D));
+      return;
+    }
     if (k - ld0 >= ld.ntile) {
       ld0 += ld.ntile;
       ld = mla_segment(a, ll, lo + ld0, hi, w, lane);
     }
-    issue(ld, k - ld0);
+    issue(creg, ld, k - ld0);
   };
-  if (n_local > 1) prefetch(1);
+  issue(cr0, ld, 0);
+  if constexpr (NSET >= 2) prefetch(cr1, 1);
+  if constexpr (NSET == 3) prefetch(cr2, 2);
+  stage(cr0, 0);
+  prefetch(cr0, NSET);
   reset();
 
-  for (int k = 0; k < n_local; ++k) {
+  // one tile: compute it from LDS, stage the next one from `next` (which
+  // then takes the tile NSET further on), close the segment at its end
+  auto step = [&](int k, u32x4* next) {
     const int buf = k & 1;
     const int tl = k - cur0;
     const int tt0 = cur.t_begin + tl * kMlaTile;
@@ -285,11 +303,8 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
         }
       }
     }
-    // ---- the next tile into the other slab, the one after it in flight
-    if (k + 1 < n_local) {
-      stage(buf ^ 1);
-      if (k + 2 < n_local) prefetch(k + 2);
-    }
+    stage(next, buf ^ 1);
+    prefetch(next, k + 1 + NSET);
     // ---- segment end: one partial per head, then the next sequence
     if (tl + 1 == cur.ntile) {
       write_partials(cur);
@@ -297,9 +312,34 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
         cur0 = k + 1;
         cur = mla_segment(a, ll, lo + cur0, hi, w, lane);
         load_q(cur);
+        // wait for the new query here, once per segment: left pending, it
+        // would make every tile wait for all loads in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         reset();
       }
     }
+  };
+  // the register sets rotate with period NSET: whole groups of NSET steps in
+  // a loop without early exits (each set then has the same loads issued after
+  // it on every path, so a stage waits only for its own set), the remainder
+  // after it
+  int k = 0;
+  if constexpr (NSET == 1) {
+    for (; k < n_local; ++k) step(k, cr0);
+  } else if constexpr (NSET == 2) {
+    for (; k + 2 <= n_local; k += 2) {
+      step(k, cr1);
+      step(k + 1, cr0);
+    }
+    if (k < n_local) step(k, cr1);
+  } else {
+    for (; k + 3 <= n_local; k += 3) {
+      step(k, cr1);
+      step(k + 1, cr2);
+      step(k + 2, cr0);
+    }
+    if (k < n_local) step(k, cr1);
+    if (k + 1 < n_local) step(k + 1, cr2);
   }
 }
 
