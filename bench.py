@@ -402,7 +402,7 @@ CALIB_GRID = (1 << 30) // 16  # threads of the calibration kernel (4 floats per 
 
 def kernel_identity(name):
     """'void gqa::k<128, 1, false, 8>(gqa::Args)' -> ('k', ('128', '1', 'false', '8'))."""
-    name = name.strip()
+    name = name.strip().replace("(anonymous namespace)::", "")
     if name.startswith("void "):
         name = name[5:]
     name = name.split("(")[0]
