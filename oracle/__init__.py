@@ -30,6 +30,9 @@ Modules:
                 glossary, "PagedAttention").
   mla        -- absorbed multi-head latent attention decode ("Evolution of AI
                 Attention Mechanisms", "Generation 3: MLA").
+  masked     -- prefill with general masks: causal or not, key lengths, a
+                dense attention mask ("MHA Implementation", "Flash Attention
+                Usage").
 
 Pinning: every function here is checked by `-m "not gpu"` tests against
 closed forms, invariants the pages fix, a library routine that computes the
@@ -37,7 +40,7 @@ same definition, and brute force on tiny inputs.  No function is parity
 unpinned.
 """
 
-from . import attention, codecs, mla, paged  # noqa: F401
+from . import attention, codecs, masked, mla, paged  # noqa: F401
 from .attention import (  # noqa: F401
     attend_one_row,
     decode,
@@ -48,10 +51,12 @@ from .attention import (  # noqa: F401
 from .codecs import (  # noqa: F401
     bf16_bits_to_f64,
     dequantize_fp8_cache,
+    dequantize_fp8_heads,
     dequantize_int_cache,
     e4m3fn_to_f64,
     int4_unpack,
     int8_to_f64,
 )
+from .masked import prefill, visible_keys  # noqa: F401
 from .mla import mla_decode  # noqa: F401
 from .paged import decode_paged, gather_logical_cache  # noqa: F401

@@ -76,6 +76,20 @@ def dequantize_fp8_cache(codes, scales):
     return vals * scales.astype(np.float64)[..., None]
 
 
+def dequantize_fp8_heads(codes, descale):
+    """Token-major fp8 tensor codes [B, S, H, d] uint8 and float32 descale
+    factors [B, H] (one per batch entry and head, the granularity of the
+    FlashAttention-3 FP8 path named in "Flash Attention 3 Features") ->
+    float64 values decode(code) * descale[b, h], exact in float64."""
+    descale = np.asarray(descale)
+    if descale.dtype != np.float32:
+        raise TypeError("fp8 descale factors must be float32")
+    vals = e4m3fn_to_f64(codes)
+    if vals.ndim != 4 or descale.shape != (vals.shape[0], vals.shape[2]):
+        raise ValueError("descale must be [B, H] for codes [B, S, H, d]")
+    return vals * descale.astype(np.float64)[:, None, :, None]
+
+
 def int8_to_f64(codes):
     """int8 codes -> float64 (exact)."""
     codes = np.asarray(codes)
