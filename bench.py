@@ -345,6 +345,41 @@ def bench_prefill(wl, steps, warmup, use_graph=False):
     }
 
 
+def bench_prefill_masked(wl, steps, warmup, use_graph=False):
+    """attn_prefill with general masks; flops count only the visible (query,
+    key) pairs (causal rule, key lengths and mask combined)."""
+    dev = torch.device("cuda")
+    x = inputs.make_masked_prefill_inputs(wl, device=dev)
+    out = torch.empty_like(x.q)
+    pairs = roofline.visible_pairs(wl.S_q, wl.S_k, wl.causal, None if x.kv_lens is None else x.kv_lens.cpu(),
+                                   None if x.mask is None else x.mask.cpu())
+    flops = roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs)
+    call = binding.prepare_prefill(x.q, x.k, x.v, wl.scale, out, causal=wl.causal, kv_lens=x.kv_lens, mask=x.mask)
+
+    def step(i):
+        call()
+
+    ms_step, k_ms = time_steps(step, steps, warmup, use_graph)
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    peak = roofline.MFMA_PEAK_TFLOPS["bf16"]
+    return {
+        "workload": wl.name,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_step": ms_step,
+        "pct_mfma_peak": 100.0 * flops / (ms_step * 1e-3) / 1e12 / peak,
+        "visible_pairs": pairs,
+        "visible_flops": flops,
+        "kernel_ms": k_ms,
+        "roofline": {"bound": "mfma", "kernel": "gqa_prefill_masked_kernel", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": measured_traffic(f"prefill_masked:{wl.name}")},
+        "dtype": "bf16",
+        "config": {"workload": wl.name, "B": wl.B, "S_q": wl.S_q, "S_k": wl.S_k, "h_q": wl.h_q, "n_kv": wl.n_kv,
+                   "d_h": wl.d_h, "causal": wl.causal, "kv_lens": wl.kv_lens, "mask": wl.mask, "seed": wl.seed},
+    }
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """A plain elementwise kernel of known traffic (reads nbytes, writes nbytes)
     for scaling hardware byte counters: dst = -src over float32."""
@@ -481,6 +516,18 @@ def _workload_launches():
         out.append((("gqa_prefill_causal_kernel", (str(wl.d_h), str(hc)), grid),
                     (f"prefill_causal:{wl.name}", wl.name, roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h),
                      "flops")))
+    for wl in inputs.MASKED_PREFILL_WORKLOADS.values():
+        G = wl.h_q // wl.n_kv
+        hc = math.gcd(G, 8)
+        bm = 32 * (8 // hc)
+        n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S_q // bm))
+        grid = -(-n_wg // 8) * 8 * 512
+        lens = inputs.draw_lengths(wl.B, *wl.kv_lens, wl.seed) if wl.kv_lens else None
+        mask = inputs.draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, wl.seed, wl.doc_lens) if wl.mask else None
+        pairs = roofline.visible_pairs(wl.S_q, wl.S_k, wl.causal, lens, mask)
+        out.append((("gqa_prefill_masked_kernel", (str(wl.d_h), str(hc)), grid),
+                    (f"prefill_masked:{wl.name}", wl.name, roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs),
+                     "flops")))
     return out
 
 
@@ -609,7 +656,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=MAIN, choices=sorted(inputs.DECODE_WORKLOADS) + sorted(
         inputs.QUANT_DECODE_WORKLOADS) + sorted(inputs.PAGED_WORKLOADS) + sorted(inputs.MLA_WORKLOADS) + sorted(
-        inputs.PREFILL_WORKLOADS))
+        inputs.PREFILL_WORKLOADS) + sorted(inputs.MASKED_PREFILL_WORKLOADS))
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--n-split", type=int, default=0, help="decode: force the number of key ranges (0 = library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -649,6 +696,8 @@ def main(argv=None):
             return bench_decode_paged(inputs.PAGED_WORKLOADS[name], steps, warmup, use_graph)
         if name in inputs.MLA_WORKLOADS:
             return bench_decode_mla(inputs.MLA_WORKLOADS[name], steps, warmup, use_graph)
+        if name in inputs.MASKED_PREFILL_WORKLOADS:
+            return bench_prefill_masked(inputs.MASKED_PREFILL_WORKLOADS[name], steps, warmup, use_graph)
         wl = {**inputs.DECODE_WORKLOADS, **inputs.QUANT_DECODE_WORKLOADS}[name]
         return bench_decode(wl, steps, warmup, use_graph, args.n_split)
 
@@ -656,7 +705,8 @@ def main(argv=None):
     others = {}
     if not args.only_main:
         for name in (list(inputs.DECODE_WORKLOADS) + list(inputs.QUANT_DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS)
-                     + list(inputs.MLA_WORKLOADS) + list(inputs.PREFILL_WORKLOADS)):
+                     + list(inputs.MLA_WORKLOADS) + list(inputs.PREFILL_WORKLOADS)
+                     + list(inputs.MASKED_PREFILL_WORKLOADS)):
             if name == args.workload:
                 continue
             others[name] = run(name, max(5, min(args.steps, 20)), 2)

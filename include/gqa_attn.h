@@ -258,6 +258,42 @@ typedef struct gqa_prefill_desc {
 gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const void* k, const void* v, float scale,
                                void* out, hipStream_t stream);
 
+/* --------------------------------------------- prefill, general masks --
+ * Prefill attention with the masks of the pages' interfaces: the module's
+ * attention_mask (scores where the mask is 0 become -inf before the softmax;
+ * "Evolution of AI Attention Mechanisms", "MHA Implementation") and
+ * flash_attn_func's causal flag ("Flash Attention Usage").  The module
+ * concatenates cached keys ahead of the new ones, so S_k may exceed S_q.
+ *
+ * Shapes (token-major):
+ *   q, out   [B, S_q, h_q, d_h]   bfloat16
+ *   k, v     [B, S_k, n_kv, d_h]  bfloat16
+ *   kv_lens  [B] int32 (device) or NULL: keys c >= kv_lens[b] (clamped to
+ *            [0, S_k]) are invisible to every row of sequence b and are
+ *            never read, so padding may hold anything
+ *   mask     [B, S_q, S_k] uint8 (device) or NULL, shared by all heads: key c
+ *            is invisible to query row r where mask[b][r][c] == 0 (any
+ *            nonzero byte keeps it); needs S_k % 4 == 0
+ * causal = 1 adds the causal rule aligned at the end of the keys: query row
+ * r sees keys c <= r + S_k - S_q (c <= r when S_q = S_k).  The conditions
+ * combine by AND.  A query row that sees no key gets a zero output row.
+ * Keys hidden only by the causal rule or the mask are read and multiplied
+ * by a zero weight, so their values must be finite.
+ * dtype must be GQA_BF16 and q/k/v_descale NULL.  Products on bf16 matrix
+ * cores, float32 statistics, out rounded to bf16.  Key tiles past every
+ * row's visible prefix are skipped; a dense mask is read for every tile
+ * that is computed.
+ */
+typedef struct gqa_attn_desc {
+  int32_t B, S_q, S_k, h_q, n_kv, d_h;
+  int32_t dtype;  /* GQA_BF16 */
+  int32_t causal; /* 0 or 1 */
+} gqa_attn_desc;
+
+gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, const void* v,
+                        const float* q_descale, const float* k_descale, const float* v_descale,
+                        const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, hipStream_t stream);
+
 /* ------------------------------------------------------------- errors --- */
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status s);

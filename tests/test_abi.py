@@ -263,3 +263,33 @@ def test_mla_plan(lib):
         rows = (W + slabs) * hpc
         o_bytes = -(-rows * d_c * 4 // 256) * 256
         assert lib.attn_decode_mla_workspace_bytes(ctypes.byref(desc)) == o_bytes + rows * 8
+
+
+def ad(B=2, S_q=64, S_k=64, h_q=8, n_kv=2, d=128, dt=1, causal=1):
+    return binding.gqa_attn_desc(B, S_q, S_k, h_q, n_kv, d, dt, causal)
+
+
+def call_prefill(lib, desc, q=ALIGNED, k=ALIGNED, v=ALIGNED, qd=None, kd=None, vd=None, lens=None, mask=None,
+                 out=ALIGNED, scale=1.0):
+    p = ctypes.byref(desc) if desc is not None else None
+    return lib.attn_prefill(p, q, k, v, qd, kd, vd, lens, mask, scale, out, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(B=0), 2), (dict(S_q=0), 2), (dict(S_k=-1), 2), (dict(h_q=12, n_kv=8), 2), (dict(d=96), 2),
+    (dict(causal=2), 2), (dict(dt=0), 3), (dict(dt=2), 3),
+])
+def test_prefill_descriptor_errors(lib, bad, code):
+    assert call_prefill(lib, ad(**bad)) == code
+
+
+def test_prefill_pointer_mask_and_value_errors(lib):
+    assert call_prefill(lib, None) == 1
+    assert call_prefill(lib, ad(), k=None) == 1
+    assert call_prefill(lib, ad(), out=None) == 1
+    assert call_prefill(lib, ad(), v=MISALIGNED) == 4
+    assert call_prefill(lib, ad(), mask=MISALIGNED) == 4
+    assert call_prefill(lib, ad(), lens=ALIGNED + 2) == 4
+    assert call_prefill(lib, ad(S_k=66), mask=ALIGNED) == 2   # mask rows are read 4 keys at a time
+    assert call_prefill(lib, ad(), qd=ALIGNED) == 3            # descale factors only with fp8 operands
+    assert call_prefill(lib, ad(), scale=-1.0) == 7

@@ -24,7 +24,7 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE"
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
             "attn_decode_combine", "attn_decode_paged_num_splits", "attn_decode_paged_workspace_bytes",
             "attn_decode_paged", "attn_decode_mla_num_splits", "attn_decode_mla_workspace_bytes",
-            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "gqa_status_string", "gqa_last_hip_error")
+            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "attn_prefill", "gqa_status_string", "gqa_last_hip_error")
 
 
 class GqaError(RuntimeError):
@@ -48,6 +48,12 @@ class gqa_paged_desc(ctypes.Structure):
 class gqa_mla_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("S_max", ctypes.c_int32), ("d_c", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+
+
+class gqa_attn_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S_q", ctypes.c_int32), ("S_k", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32)]
 
 
 class gqa_prefill_desc(ctypes.Structure):
@@ -92,6 +98,9 @@ def load_library(path=LIB_PATH):
     lib.attn_decode_mla_combine.argtypes = [md, vp, vp, sz, vp, vp]
     lib.attn_decode_mla_combine.restype = ctypes.c_int
     lib.attn_prefill_causal.argtypes = [pd, vp, vp, vp, f32, vp, vp]
+    ad = ctypes.POINTER(gqa_attn_desc)
+    lib.attn_prefill.argtypes = [ad, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
+    lib.attn_prefill.restype = ctypes.c_int
     lib.attn_prefill_causal.restype = ctypes.c_int
     lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [ctypes.c_int], cp
     lib.gqa_last_hip_error.argtypes, lib.gqa_last_hip_error.restype = [], cp
@@ -445,5 +454,43 @@ def prepare_prefill_causal(q, k, v, scale, out, stream=None):
     lib = load_library()
     call = PreparedCall(lib.attn_prefill_causal, (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
                                                   ctypes.c_float(scale), _ptr(out)), stream, out)
+    call._keep = (desc,)
+    return call
+
+
+def _attn_desc(q, k, v, out, causal, kv_lens, mask):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _require(t, name, 4)
+    B, S_q, h_q, d = q.shape
+    if k.shape != v.shape or k.dtype != v.dtype or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k/v must be [B, S_k, n_kv, d] matching q [B, S_q, h_q, d]")
+    if out.shape != q.shape or out.dtype != torch.bfloat16:
+        raise ValueError("out must be a bf16 tensor shaped like q")
+    S_k = k.shape[1]
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.shape != (B,) or not kv_lens.is_contiguous()):
+        raise ValueError("kv_lens must be a contiguous int32 tensor of shape [B]")
+    if mask is not None and (mask.dtype not in (torch.uint8, torch.bool) or tuple(mask.shape) != (B, S_q, S_k)
+                             or not mask.is_contiguous()):
+        raise ValueError("mask must be a contiguous uint8/bool tensor of shape [B, S_q, S_k]")
+    return gqa_attn_desc(B, S_q, S_k, h_q, k.shape[2], d, _dtype_code(q), 1 if causal else 0)
+
+
+def attn_prefill(q, k, v, scale, causal=True, kv_lens=None, mask=None, out=None, stream=None):
+    """out[B, S_q, h_q, d] = attention of q [B,S_q,h_q,d] over k/v [B,S_k,n_kv,d] (bf16) with the causal rule
+    (end-aligned), key lengths and a dense [B, S_q, S_k] mask (see attn_prefill in gqa_attn.h)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    desc = _attn_desc(q, k, v, out, causal, kv_lens, mask)
+    _check(load_library().attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), None, None, None,
+                                       _ptr(kv_lens), _ptr(mask), float(scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def prepare_prefill(q, k, v, scale, out, causal=True, kv_lens=None, mask=None, stream=None):
+    """PreparedCall of attn_prefill."""
+    desc = _attn_desc(q, k, v, out, causal, kv_lens, mask)
+    lib = load_library()
+    call = PreparedCall(lib.attn_prefill, (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), None, None, None,
+                                           _ptr(kv_lens), _ptr(mask), ctypes.c_float(scale), _ptr(out)), stream, out)
     call._keep = (desc,)
     return call

@@ -454,6 +454,33 @@ gqa_status attn_decode_mla(const gqa_mla_desc* d, const void* q_abs, const void*
   return attn_decode_mla_combine(d, seq_lens, workspace, workspace_bytes, out, stream);
 }
 
+gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, const float* v_descale, const int32_t* kv_lens, const uint8_t* mask,
+                        float scale, void* out, hipStream_t stream) {
+  if (!d) return GQA_ERR_NULL;
+  if (d->B <= 0 || d->S_q <= 0 || d->S_k <= 0 || d->h_q <= 0 || d->n_kv <= 0 || d->d_h <= 0) return GQA_ERR_SHAPE;
+  if (d->h_q % d->n_kv != 0) return GQA_ERR_SHAPE;
+  if (d->d_h != 64 && d->d_h != 128) return GQA_ERR_SHAPE;
+  if (d->causal != 0 && d->causal != 1) return GQA_ERR_SHAPE;
+  if ((int64_t)d->B * d->S_q * d->h_q > (int64_t)1 << 31) return GQA_ERR_SHAPE;
+  if ((int64_t)d->B * d->S_k * d->n_kv > (int64_t)1 << 31) return GQA_ERR_SHAPE;
+  // 4-key mask words; a workgroup's mask rows (up to 256) within a 31-bit buffer range
+  if (mask && (d->S_k % 4 != 0 || d->S_k > (1 << 23))) return GQA_ERR_SHAPE;
+  if (d->dtype != GQA_BF16) return GQA_ERR_DTYPE;
+  if (q_descale || k_descale || v_descale) return GQA_ERR_DTYPE;
+  if (!q || !k || !v || !out) return GQA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(mask)) return GQA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0) return GQA_ERR_ALIGN;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
+  const hipError_t e = launch_prefill_masked(q, k, v, out, (float)((double)scale * kLog2e), d->B, d->S_q, d->S_k,
+                                             d->h_q, d->n_kv, d->d_h, d->causal, kv_lens, mask, stream);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return GQA_ERR_HIP;
+  }
+  return GQA_OK;
+}
+
 const char* gqa_status_string(gqa_status s) {
   switch (s) {
     case GQA_OK: return "GQA_OK";

@@ -69,5 +69,10 @@ hipError_t launch_mla_decode_split(const MlaArgs& a, int D, int hb, int W, hipSt
 hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream);
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S, int h_q, int n_kv, int D, hipStream_t stream);
+// General masks: S_q query rows, S_k keys, optional end-aligned causal rule,
+// key lengths [B] and dense mask [B][S_q][S_k] (nonzero = visible).
+hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
+                                 int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
+                                 const uint8_t* mask, hipStream_t stream);
 
 }  // namespace gqa

@@ -388,6 +388,101 @@ def make_prefill_inputs(wl, device="cpu", seed=None):
     return PrefillInputs(wl, q, k, v)
 
 
+@dataclass(frozen=True)
+class MaskedPrefillWorkload:
+    """Prefill with general masks: S_q queries over S_k keys (cached keys come
+    first), the causal rule optional, ragged key lengths (padding) and a dense
+    mask shared by all heads.
+
+    mask kinds: None; "random" (each byte 1 with probability 3/4, seeded);
+    "docs" (packed documents: consecutive spans of random length in
+    doc_lens, a row sees only keys of its own span)."""
+    name: str
+    B: int
+    S_q: int
+    S_k: int
+    h_q: int
+    n_kv: int
+    d_h: int
+    causal: bool
+    seed: int
+    kv_lens: Optional[Tuple[int, int]] = None
+    mask: Optional[str] = None
+    doc_lens: Tuple[int, int] = (512, 2048)
+
+    @property
+    def G(self):
+        return self.h_q // self.n_kv
+
+    @property
+    def scale(self):
+        return 1.0 / float(self.d_h) ** 0.5
+
+
+# c4's shape without the causal rule, padded to ragged key lengths
+GQA_PREFILL_PADDED = MaskedPrefillWorkload("gqa_prefill_padded_bf16", B=4, S_q=4096, S_k=4096, h_q=32, n_kv=8,
+                                           d_h=128, causal=False, seed=9, kv_lens=(2048, 4096))
+# c4 with packed documents of 512..2048 tokens (dense block-diagonal mask on top of the causal rule)
+GQA_PREFILL_DOCS = MaskedPrefillWorkload("gqa_prefill_docs_bf16", B=4, S_q=4096, S_k=4096, h_q=32, n_kv=8,
+                                         d_h=128, causal=True, seed=10, mask="docs")
+MASKED_PREFILL_WORKLOADS = {w.name: w for w in (GQA_PREFILL_PADDED, GQA_PREFILL_DOCS)}
+
+
+@dataclass
+class MaskedPrefillInputs:
+    wl: MaskedPrefillWorkload
+    q: torch.Tensor                  # [B, S_q, h_q, d] bf16
+    k: torch.Tensor                  # [B, S_k, n_kv, d] bf16
+    v: torch.Tensor
+    kv_lens: Optional[torch.Tensor]  # [B] int32
+    mask: Optional[torch.Tensor]     # [B, S_q, S_k] uint8
+
+
+def draw_mask(kind, B, S_q, S_k, seed, doc_lens=(512, 2048)):
+    """uint8 [B, S_q, S_k] from a CPU generator (1 = visible)."""
+    g = _gen("cpu", seed * 7919 + 29)
+    if kind == "random":
+        return (torch.rand((B, S_q, S_k), generator=g) < 0.75).to(torch.uint8)
+    if kind == "docs":
+        if S_q != S_k:
+            raise ValueError("document masks need S_q == S_k")
+        doc = torch.empty((B, S_k), dtype=torch.int64)
+        for b in range(B):
+            pos, i = 0, 0
+            while pos < S_k:
+                n = int(torch.randint(doc_lens[0], doc_lens[1] + 1, (1,), generator=g))
+                doc[b, pos:pos + n] = i
+                pos, i = pos + n, i + 1
+        return (doc[:, :, None] == doc[:, None, :]).to(torch.uint8)
+    raise ValueError(f"unknown mask kind {kind}")
+
+
+def make_masked_prefill_inputs(wl, device="cpu", kv_lens=None, mask=None, poison_padding=False, seed=None):
+    """Seeded q/k/v (N(0,1) -> bf16), key lengths (given, drawn from wl.kv_lens, or
+    none) and a mask (given, drawn by wl.mask's kind, or none).  poison_padding
+    fills key/value rows at or past each key length with NaN."""
+    seed = wl.seed if seed is None else seed
+    g = _gen(device, seed)
+    q = torch.randn((wl.B, wl.S_q, wl.h_q, wl.d_h), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((wl.B, wl.S_k, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((wl.B, wl.S_k, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    if kv_lens is None and wl.kv_lens is not None:
+        kv_lens = draw_lengths(wl.B, wl.kv_lens[0], wl.kv_lens[1], seed)
+    if kv_lens is not None:
+        kv_lens = torch.as_tensor(kv_lens, dtype=torch.int32).reshape(wl.B)
+        if poison_padding:
+            for b in range(wl.B):
+                n = int(min(max(int(kv_lens[b]), 0), wl.S_k))
+                k[b, n:] = float("nan")
+                v[b, n:] = float("nan")
+        kv_lens = kv_lens.to(device)
+    if mask is None and wl.mask is not None:
+        mask = draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, seed, wl.doc_lens)
+    if mask is not None:
+        mask = torch.as_tensor(mask).to(torch.uint8).contiguous().to(device)
+    return MaskedPrefillInputs(wl, q, k, v, kv_lens, mask)
+
+
 def stored_numpy(t):
     """A tensor's stored encoding as a numpy array: bf16 -> uint16 bit patterns,
     fp8 and packed int4 codes stay uint8, int8 codes int8, float32/int32 as is.
