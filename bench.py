@@ -350,18 +350,19 @@ def bench_prefill_masked(wl, steps, warmup, use_graph=False):
     key) pairs (causal rule, key lengths and mask combined)."""
     dev = torch.device("cuda")
     x = inputs.make_masked_prefill_inputs(wl, device=dev)
-    out = torch.empty_like(x.q)
-    pairs = roofline.visible_pairs(wl.S_q, wl.S_k, wl.causal, None if x.kv_lens is None else x.kv_lens.cpu(),
+    pairs = roofline.visible_pairs(wl.B, wl.S_q, wl.S_k, wl.causal, None if x.kv_lens is None else x.kv_lens.cpu(),
                                    None if x.mask is None else x.mask.cpu())
     flops = roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs)
-    call = binding.prepare_prefill(x.q, x.k, x.v, wl.scale, out, causal=wl.causal, kv_lens=x.kv_lens, mask=x.mask)
+    out = torch.empty(x.q.shape, dtype=torch.bfloat16, device=dev)
+    call = binding.prepare_prefill(x.q, x.k, x.v, wl.scale, out, causal=wl.causal, kv_lens=x.kv_lens, mask=x.mask,
+                                   q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale)
 
     def step(i):
         call()
 
     ms_step, k_ms = time_steps(step, steps, warmup, use_graph)
     achieved = flops / (k_ms * 1e-3) / 1e12
-    peak = roofline.MFMA_PEAK_TFLOPS["bf16"]
+    peak = roofline.MFMA_PEAK_TFLOPS[wl.dtype]  # a contraction takes its own dtype's peak
     return {
         "workload": wl.name,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -371,12 +372,14 @@ def bench_prefill_masked(wl, steps, warmup, use_graph=False):
         "visible_pairs": pairs,
         "visible_flops": flops,
         "kernel_ms": k_ms,
-        "roofline": {"bound": "mfma", "kernel": "gqa_prefill_masked_kernel", "achieved": achieved, "peak": peak,
+        "roofline": {"bound": "mfma", "kernel": "gqa_prefill_fp8_kernel" if wl.dtype == "fp8"
+                     else "gqa_prefill_masked_kernel", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": measured_traffic(f"prefill_masked:{wl.name}")},
-        "dtype": "bf16",
+        "dtype": wl.dtype,
         "config": {"workload": wl.name, "B": wl.B, "S_q": wl.S_q, "S_k": wl.S_k, "h_q": wl.h_q, "n_kv": wl.n_kv,
-                   "d_h": wl.d_h, "causal": wl.causal, "kv_lens": wl.kv_lens, "mask": wl.mask, "seed": wl.seed},
+                   "d_h": wl.d_h, "causal": wl.causal, "kv_lens": wl.kv_lens, "mask": wl.mask, "dtype": wl.dtype,
+                   "seed": wl.seed},
     }
 
 
@@ -524,8 +527,10 @@ def _workload_launches():
         grid = -(-n_wg // 8) * 8 * 512
         lens = inputs.draw_lengths(wl.B, *wl.kv_lens, wl.seed) if wl.kv_lens else None
         mask = inputs.draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, wl.seed, wl.doc_lens) if wl.mask else None
-        pairs = roofline.visible_pairs(wl.S_q, wl.S_k, wl.causal, lens, mask)
-        out.append((("gqa_prefill_masked_kernel", (str(wl.d_h), str(hc)), grid),
+        pairs = roofline.visible_pairs(wl.B, wl.S_q, wl.S_k, wl.causal, lens, mask)
+        kname, targs = (("gqa_prefill_fp8_kernel", (str(hc),)) if wl.dtype == "fp8"
+                        else ("gqa_prefill_masked_kernel", (str(wl.d_h), str(hc))))
+        out.append(((kname, targs, grid),
                     (f"prefill_masked:{wl.name}", wl.name, roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs),
                      "flops")))
     return out
@@ -547,20 +552,28 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
         by_key.setdefault(key, []).append(ent)
     info = {ent[0]: (key, ent) for key, ent in launches}  # counter key -> (launch key, entry)
 
+    order = run_order(MAIN)
+
     def resolve(stream):
-        """(launch key, row) in dispatch order -> (counter key, row) for our kernels."""
-        cur = None
+        """(launch key, row) in dispatch order -> (counter key, row) for our kernels.
+
+        The default run times the workloads one after another in run_order(),
+        each preceded by warm-up matrix products and its own input set-up, so
+        the k-th unbroken run of library launches belongs to the k-th
+        workload; that settles launches two workloads share (same kernel and
+        grid)."""
+        seg, in_ours = -1, False
         for key, r in stream:
             ents = by_key.get(key)
             if not ents:
+                in_ours = False
                 continue
-            if len(ents) == 1:
-                cur = ents[0][1]
-                yield ents[0][0], r
-            else:
-                match = [e for e in ents if e[1] == cur]
-                if match:
-                    yield match[0][0], r
+            if not in_ours:
+                seg, in_ours = seg + 1, True
+            wname = order[seg] if seg < len(order) else None
+            match = [e for e in ents if e[1] == wname]
+            if match:
+                yield match[0][0], r
 
     def ordered(rs):
         return sorted(rs, key=lambda r: int(r["Dispatch_Id"]))
@@ -649,6 +662,16 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
     return summary
 
 
+def all_workloads():
+    return (list(inputs.DECODE_WORKLOADS) + list(inputs.QUANT_DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS)
+            + list(inputs.MLA_WORKLOADS) + list(inputs.PREFILL_WORKLOADS) + list(inputs.MASKED_PREFILL_WORKLOADS))
+
+
+def run_order(main_name):
+    """Workloads in the order one default run times them."""
+    return [main_name] + [n for n in all_workloads() if n != main_name]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -704,11 +727,7 @@ def main(argv=None):
     main_res = run(args.workload, args.steps, args.warmup)
     others = {}
     if not args.only_main:
-        for name in (list(inputs.DECODE_WORKLOADS) + list(inputs.QUANT_DECODE_WORKLOADS) + list(inputs.PAGED_WORKLOADS)
-                     + list(inputs.MLA_WORKLOADS) + list(inputs.PREFILL_WORKLOADS)
-                     + list(inputs.MASKED_PREFILL_WORKLOADS)):
-            if name == args.workload:
-                continue
+        for name in run_order(args.workload)[1:]:
             others[name] = run(name, max(5, min(args.steps, 20)), 2)
             torch.cuda.empty_cache()
 

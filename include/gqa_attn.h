@@ -279,14 +279,23 @@ gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const v
  * combine by AND.  A query row that sees no key gets a zero output row.
  * Keys hidden only by the causal rule or the mask are read and multiplied
  * by a zero weight, so their values must be finite.
- * dtype must be GQA_BF16 and q/k/v_descale NULL.  Products on bf16 matrix
- * cores, float32 statistics, out rounded to bf16.  Key tiles past every
- * row's visible prefix are skipped; a dense mask is read for every tile
- * that is computed.
+ * dtype GQA_BF16: q/k/v bfloat16, q/k/v_descale NULL.  Products on bf16
+ * matrix cores, float32 statistics, out rounded to bf16.
+ * dtype GQA_FP8_E4M3 (the FP8 mode listed for FlashAttention-3 in "Flash
+ * Attention 3 Features"): q/k/v hold OCP E4M3 codes (same shapes, one byte
+ * per element) and the values are code * descale with float32 factors
+ *   q_descale [B, h_q], k_descale [B, n_kv], v_descale [B, n_kv] (device);
+ * d_h must be 128.  Both products run on fp8 matrix cores: the scores from
+ * the codes (the descale factors fold into the score scale and the output),
+ * and the weighted sum with the softmax weights rounded to E4M3 (relative
+ * error up to 2^-4 per weight, normal range), float32 accumulation, out
+ * bf16.
+ * Key tiles past every row's visible prefix are skipped, and a wave skips
+ * the products of a tile the dense mask hides from all of its rows.
  */
 typedef struct gqa_attn_desc {
   int32_t B, S_q, S_k, h_q, n_kv, d_h;
-  int32_t dtype;  /* GQA_BF16 */
+  int32_t dtype;  /* GQA_BF16 or GQA_FP8_E4M3 */
   int32_t causal; /* 0 or 1 */
 } gqa_attn_desc;
 

@@ -100,3 +100,40 @@ def sample_rows(B, S, h_q, n, seed):
 
 def sync():
     torch.cuda.synchronize()
+
+
+def masked_prefill_values(inp):
+    """q, k, v of a masked-prefill input as float64 values (fp8 codes through
+    the oracle's per-head dequantiser)."""
+    if inp.wl.dtype == "fp8":
+        return tuple(oracle.dequantize_fp8_heads(inputs.stored_numpy(t), inputs.stored_numpy(d))
+                     for t, d in ((inp.q, inp.q_descale), (inp.k, inp.k_descale), (inp.v, inp.v_descale)))
+    return to_f64(inp.q), to_f64(inp.k), to_f64(inp.v)
+
+
+def fp8_prefill_bound(q, k, v, scale, triples, causal, kv_lens, mask):
+    """Per-element error bound of the fp8 prefill at the (b, r, j) rows, from
+    the arithmetic: the weights are rounded to e4m3 (relative error <= 2^-4 in
+    the normal range, absolute <= 2^-10 below 2^-6, in units where the largest
+    weight is at least 1), the output to bf16 (2^-8 relative), plus 2^-7 for
+    float32 accumulation.  With exact weights w_i = p_i / l:
+        |dO_d| <= 2^-4 sum_i w_i |v_id| + 2^-10 sum_{p_i < 2^-6} |v_id| / l
+                  + 2^-8 |O_d| + 2^-7."""
+    out = []
+    S_q, S_k = q.shape[1], k.shape[1]
+    G = q.shape[2] // k.shape[2]
+    for b, r, j in triples:
+        vis = oracle.visible_keys(S_q, S_k, causal, None if kv_lens is None else kv_lens[b],
+                                  None if mask is None else mask[b])[r]
+        if not vis.any():
+            out.append(np.full(q.shape[3], 2.0 ** -7))
+            continue
+        kk, vv = k[b, vis, j // G], v[b, vis, j // G]
+        s = scale * (kk @ q[b, r, j])
+        p = np.exp(s - s.max())
+        lsum = p.sum()
+        o = (p / lsum) @ vv
+        small = p < 2.0 ** -6
+        out.append(2.0 ** -4 * ((p / lsum) @ np.abs(vv)) + 2.0 ** -10 * np.abs(vv[small]).sum(0) / lsum
+                   + 2.0 ** -8 * np.abs(o) + 2.0 ** -7)
+    return np.stack(out)

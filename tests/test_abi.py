@@ -277,10 +277,18 @@ def call_prefill(lib, desc, q=ALIGNED, k=ALIGNED, v=ALIGNED, qd=None, kd=None, v
 
 @pytest.mark.parametrize("bad,code", [
     (dict(B=0), 2), (dict(S_q=0), 2), (dict(S_k=-1), 2), (dict(h_q=12, n_kv=8), 2), (dict(d=96), 2),
-    (dict(causal=2), 2), (dict(dt=0), 3), (dict(dt=2), 3),
+    (dict(causal=2), 2), (dict(dt=0), 3), (dict(dt=3), 3), (dict(dt=2, d=64), 2),
 ])
 def test_prefill_descriptor_errors(lib, bad, code):
     assert call_prefill(lib, ad(**bad)) == code
+
+
+def test_prefill_fp8_needs_aligned_descale_factors(lib):
+    """fp8 operands take three descale arrays; bf16 operands take none."""
+    assert call_prefill(lib, ad(dt=2)) == 1
+    assert call_prefill(lib, ad(dt=2), qd=ALIGNED, kd=ALIGNED) == 1
+    assert call_prefill(lib, ad(dt=2), qd=ALIGNED, kd=ALIGNED + 2, vd=ALIGNED) == 4
+    assert call_prefill(lib, ad(dt=1), vd=ALIGNED) == 3
 
 
 def test_prefill_pointer_mask_and_value_errors(lib):

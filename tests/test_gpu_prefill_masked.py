@@ -18,21 +18,50 @@ DEV = "cuda"
 TOL = pu.TOL["bf16"]
 
 
-def wl(B, S_q, S_k, h_q, n_kv, d, causal, seed, mask=None, doc_lens=(512, 2048)):
+def wl(B, S_q, S_k, h_q, n_kv, d, causal, seed, mask=None, doc_lens=(512, 2048), dtype="bf16"):
     return inputs.MaskedPrefillWorkload("masked", B=B, S_q=S_q, S_k=S_k, h_q=h_q, n_kv=n_kv, d_h=d, causal=causal,
-                                        seed=seed, mask=mask, doc_lens=doc_lens)
+                                        seed=seed, mask=mask, doc_lens=doc_lens, dtype=dtype)
 
 
 def run(inp):
     w = inp.wl
-    return binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, causal=w.causal, kv_lens=inp.kv_lens, mask=inp.mask)
+    return binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, causal=w.causal, kv_lens=inp.kv_lens, mask=inp.mask,
+                                q_descale=inp.q_descale, k_descale=inp.k_descale, v_descale=inp.v_descale)
 
 
-def oracle_full(inp):
+def _lens_mask(inp):
+    return (None if inp.kv_lens is None else inp.kv_lens.cpu().numpy(),
+            None if inp.mask is None else inp.mask.cpu().numpy())
+
+
+def compare(inp, out, triples=None):
+    """bf16: max-abs error <= 2e-2 against the oracle.  fp8: every element
+    within the arithmetic's bound (parity_utils.fp8_prefill_bound) and the
+    relative RMS error below 0.1 (a wrong key or head mapping gives ~1)."""
     w = inp.wl
-    return oracle.prefill(pu.to_f64(inp.q), pu.to_f64(inp.k), pu.to_f64(inp.v), w.scale, causal=w.causal,
-                          kv_lens=None if inp.kv_lens is None else inp.kv_lens.cpu().numpy(),
-                          mask=None if inp.mask is None else inp.mask.cpu().numpy())
+    q, k, v = pu.masked_prefill_values(inp)
+    lens, mask = _lens_mask(inp)
+    if triples is None:
+        ref = oracle.prefill(q, k, v, w.scale, causal=w.causal, kv_lens=lens, mask=mask)
+        got = out
+    else:
+        ref = omasked.prefill_rows(q, k, v, w.scale, triples, causal=w.causal, kv_lens=lens, mask=mask)
+        got = torch.stack([out[b, r, j] for b, r, j in triples])
+    if w.dtype != "fp8":
+        err = pu.max_err(got, ref)
+        assert err <= TOL, f"max abs err {err}"
+        return
+    g = got.detach().float().cpu().double().numpy()
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    if triples is None:
+        triples = [(b, r, j) for b in range(w.B) for r in range(w.S_q) for j in range(w.h_q)]
+        g = g.reshape(-1, w.d_h)
+        ref = ref.reshape(-1, w.d_h)
+    bound = pu.fp8_prefill_bound(q, k, v, w.scale, triples, w.causal, lens, mask)
+    excess = np.abs(g - ref) - bound
+    assert np.all(excess <= 0), f"fp8 bound exceeded by {excess.max()} at row {triples[int(np.argmax(excess.max(1)))]}"
+    rel = np.sqrt(np.mean((g - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30)
+    assert rel <= 0.1, f"relative rms error {rel}"
 
 
 def check(inp):
@@ -41,8 +70,7 @@ def check(inp):
           f"mask={'none' if inp.mask is None else 'dense'}", flush=True)
     out = run(inp)
     pu.sync()
-    err = pu.max_err(out, oracle_full(inp))
-    assert err <= TOL, f"max abs err {err}"
+    compare(inp, out)
     return out
 
 
@@ -109,11 +137,26 @@ def test_full_size_sampled(name):
     print(f"[prefill_masked] full size {w}", flush=True)
     out = run(inp)
     pu.sync()
-    trip = pu.sample_rows(w.B, w.S_q, w.h_q, 48, seed=460)
-    q, k, v = pu.to_f64(inp.q), pu.to_f64(inp.k), pu.to_f64(inp.v)
-    lens = None if inp.kv_lens is None else inp.kv_lens.cpu().numpy()
-    mask = None if inp.mask is None else inp.mask.cpu().numpy()
-    ref = omasked.prefill_rows(q, k, v, w.scale, trip, causal=w.causal, kv_lens=lens, mask=mask)
-    got = torch.stack([out[b, r, j] for b, r, j in trip])
-    err = pu.max_err(got, ref)
-    assert err <= TOL, f"max abs err {err}"
+    compare(inp, out, pu.sample_rows(w.B, w.S_q, w.h_q, 48, seed=460))
+
+
+@pytest.mark.parametrize("h_q,n_kv", [(8, 8), (8, 4), (8, 2), (16, 2), (6, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_head_chunks_and_lengths(h_q, n_kv, causal):
+    """fp8 operands over every head-chunk size, key lengths 200, 1, 0 and 77
+    (NaN codes past each length)."""
+    inp = inputs.make_masked_prefill_inputs(wl(4, 200, 200, h_q, n_kv, 128, causal, seed=470 + h_q + n_kv,
+                                               dtype="fp8"), device=DEV, kv_lens=[200, 1, 0, 77],
+                                            poison_padding=True)
+    out = check(inp)
+    assert torch.count_nonzero(out[2]) == 0
+
+
+@pytest.mark.parametrize("kind", ["random", "docs"])
+def test_fp8_masks_and_key_counts(kind):
+    w = wl(2, 150, 300, 8, 2, 128, True, seed=480, mask=kind, doc_lens=(16, 80), dtype="fp8")
+    m = inputs.draw_mask(kind, 2, 150, 300, 480, (16, 80)) if kind == "random" else None
+    if kind == "docs":  # documents over the keys; the queries are the last 150 positions
+        full = inputs.draw_mask("docs", 2, 300, 300, 480, (16, 80))
+        m = full[:, 150:, :].contiguous()
+    check(inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=[300, 222], mask=m))

@@ -63,3 +63,16 @@ def test_int_cache_bytes():
     assert roofline.decode_kv_bytes("int8", 8, 128, lens) == 2147483648
     assert roofline.decode_kv_bytes("int4", 8, 128, lens) == 1073741824
     assert roofline.decode_scale_bytes("int4", 8, lens) == roofline.decode_scale_bytes("fp8", 8, lens) == 67108864
+
+
+def test_visible_pairs_closed_forms():
+    """Causal S x S keeps S(S+1)/2 pairs per sequence; more keys than queries
+    shift the diagonal; key lengths and a mask cut pairs out."""
+    import torch
+    assert roofline.visible_pairs(4, 4096, 4096, True) == 4 * 4096 * 4097 // 2
+    assert roofline.visible_pairs(1, 2, 5, True) == 4 + 5
+    assert roofline.visible_pairs(2, 3, 3, False, [1, 3]) == 3 * 1 + 3 * 3
+    m = torch.zeros(1, 2, 4, dtype=torch.uint8)
+    m[0, 1, 0] = m[0, 1, 3] = 7
+    assert roofline.visible_pairs(1, 2, 4, True, None, m) == 1
+    assert roofline.prefill_masked_flops(32, 128, 10) == 4 * 32 * 128 * 10

@@ -466,6 +466,8 @@ def _attn_desc(q, k, v, out, causal, kv_lens, mask):
         raise ValueError("k/v must be [B, S_k, n_kv, d] matching q [B, S_q, h_q, d]")
     if out.shape != q.shape or out.dtype != torch.bfloat16:
         raise ValueError("out must be a bf16 tensor shaped like q")
+    if q.dtype != k.dtype:
+        raise ValueError("q and k/v must have the same dtype (bf16, or uint8 e4m3 codes)")
     S_k = k.shape[1]
     if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.shape != (B,) or not kv_lens.is_contiguous()):
         raise ValueError("kv_lens must be a contiguous int32 tensor of shape [B]")
@@ -475,22 +477,40 @@ def _attn_desc(q, k, v, out, causal, kv_lens, mask):
     return gqa_attn_desc(B, S_q, S_k, h_q, k.shape[2], d, _dtype_code(q), 1 if causal else 0)
 
 
-def attn_prefill(q, k, v, scale, causal=True, kv_lens=None, mask=None, out=None, stream=None):
-    """out[B, S_q, h_q, d] = attention of q [B,S_q,h_q,d] over k/v [B,S_k,n_kv,d] (bf16) with the causal rule
-    (end-aligned), key lengths and a dense [B, S_q, S_k] mask (see attn_prefill in gqa_attn.h)."""
+def _descale_checks(q, k, descales):
+    if q.dtype != torch.uint8:
+        if any(d is not None for d in descales):
+            raise ValueError("descale factors go with fp8 (uint8 e4m3 code) operands only")
+        return
+    B, h_q, n_kv = q.shape[0], q.shape[2], k.shape[2]
+    for name, d, H in zip(("q_descale", "k_descale", "v_descale"), descales, (h_q, n_kv, n_kv)):
+        if d is None or d.dtype != torch.float32 or tuple(d.shape) != (B, H) or not d.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape [B, {H}]")
+
+
+def attn_prefill(q, k, v, scale, causal=True, kv_lens=None, mask=None, out=None, q_descale=None, k_descale=None,
+                 v_descale=None, stream=None):
+    """out[B, S_q, h_q, d] (bf16) = attention of q [B,S_q,h_q,d] over k/v [B,S_k,n_kv,d] with the causal rule
+    (end-aligned), key lengths and a dense [B, S_q, S_k] mask.  Operands are bf16, or uint8 e4m3 codes with
+    per-(batch, head) descale factors (see attn_prefill in gqa_attn.h)."""
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     desc = _attn_desc(q, k, v, out, causal, kv_lens, mask)
-    _check(load_library().attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), None, None, None,
-                                       _ptr(kv_lens), _ptr(mask), float(scale), _ptr(out), _stream(stream)))
+    _descale_checks(q, k, (q_descale, k_descale, v_descale))
+    _check(load_library().attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale),
+                                       _ptr(k_descale), _ptr(v_descale), _ptr(kv_lens), _ptr(mask), float(scale),
+                                       _ptr(out), _stream(stream)))
     return out
 
 
-def prepare_prefill(q, k, v, scale, out, causal=True, kv_lens=None, mask=None, stream=None):
+def prepare_prefill(q, k, v, scale, out, causal=True, kv_lens=None, mask=None, q_descale=None, k_descale=None,
+                    v_descale=None, stream=None):
     """PreparedCall of attn_prefill."""
     desc = _attn_desc(q, k, v, out, causal, kv_lens, mask)
+    _descale_checks(q, k, (q_descale, k_descale, v_descale))
     lib = load_library()
-    call = PreparedCall(lib.attn_prefill, (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), None, None, None,
-                                           _ptr(kv_lens), _ptr(mask), ctypes.c_float(scale), _ptr(out)), stream, out)
+    call = PreparedCall(lib.attn_prefill, (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale),
+                                           _ptr(k_descale), _ptr(v_descale), _ptr(kv_lens), _ptr(mask),
+                                           ctypes.c_float(scale), _ptr(out)), stream, out)
     call._keep = (desc,)
     return call

@@ -466,14 +466,24 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
   if ((int64_t)d->B * d->S_k * d->n_kv > (int64_t)1 << 31) return GQA_ERR_SHAPE;
   // 4-key mask words; a workgroup's mask rows (up to 256) within a 31-bit buffer range
   if (mask && (d->S_k % 4 != 0 || d->S_k > (1 << 23))) return GQA_ERR_SHAPE;
-  if (d->dtype != GQA_BF16) return GQA_ERR_DTYPE;
-  if (q_descale || k_descale || v_descale) return GQA_ERR_DTYPE;
+  const bool fp8 = d->dtype == GQA_FP8_E4M3;
+  if (d->dtype != GQA_BF16 && !fp8) return GQA_ERR_DTYPE;
+  if (!fp8 && (q_descale || k_descale || v_descale)) return GQA_ERR_DTYPE;
+  if (fp8 && d->d_h != 128) return GQA_ERR_SHAPE;
   if (!q || !k || !v || !out) return GQA_ERR_NULL;
+  if (fp8 && (!q_descale || !k_descale || !v_descale)) return GQA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(mask)) return GQA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0) return GQA_ERR_ALIGN;
+  if (((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
+        reinterpret_cast<uintptr_t>(v_descale)) & 3u) != 0)
+    return GQA_ERR_ALIGN;
   if (bad_scale(scale)) return GQA_ERR_VALUE;
-  const hipError_t e = launch_prefill_masked(q, k, v, out, (float)((double)scale * kLog2e), d->B, d->S_q, d->S_k,
-                                             d->h_q, d->n_kv, d->d_h, d->causal, kv_lens, mask, stream);
+  const float sl2 = (float)((double)scale * kLog2e);
+  const hipError_t e =
+      fp8 ? launch_prefill_fp8(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->causal, kv_lens, mask,
+                               q_descale, k_descale, v_descale, stream)
+          : launch_prefill_masked(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal,
+                                  kv_lens, mask, stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;

@@ -74,5 +74,10 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
 hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                                  const uint8_t* mask, hipStream_t stream);
+// fp8 (e4m3) q/k/v with per-(batch, head) descale factors, d = 128, general masks.
+hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
+                              int S_q, int S_k, int h_q, int n_kv, int causal, const int32_t* kv_lens,
+                              const uint8_t* mask, const float* q_descale, const float* k_descale,
+                              const float* v_descale, hipStream_t stream);
 
 }  // namespace gqa

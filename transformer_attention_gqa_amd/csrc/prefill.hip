@@ -47,6 +47,10 @@ struct PrefillArgs {
   int causal;               // query r sees keys c <= r + S_k - S_q
   const int32_t* kv_lens;   // [B] or null: keys c >= kv_lens[b] are invisible and never read
   const uint8_t* mask;      // [B][S][S_k] or null: key c invisible to row r where 0
+  // fp8 kernel: q/k/v hold e4m3 codes; value = code * descale[b][head]
+  const float* q_descale;   // [B][h_q]
+  const float* k_descale;   // [B][n_kv]
+  const float* v_descale;   // [B][n_kv]
 };
 
 constexpr int kBN = 64;  // keys per tile
@@ -57,14 +61,34 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // range visible.  GEN = true: S_q and S_k independent, the causal rule
 // optional and end-aligned, optional key lengths and dense mask; rows can
 // then have no visible key at all (zero output).
-template <int D, int HC, bool GEN>
+// F8: q, k, v are OCP e4m3 codes with one descale factor per (batch, head)
+// (the FP8 mode of FlashAttention-3, "Flash Attention 3 Features"); both
+// products run on v_mfma_f32_32x32x64_f8f6f4, P rounded to e4m3 (kept <= 256
+// by the reference max, below the format's 448), d = 128 only.
+template <int D, int HC, bool GEN, bool F8 = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
+  static_assert(!F8 || (D == 128 && GEN), "the fp8 body serves d = 128 with general masks");
   constexpr int RB = kWaves / HC;  // 32-row blocks per head in one workgroup
   constexpr int BM = 32 * RB;    // query rows per workgroup
-  constexpr int CH = D / 8;      // 16-byte chunks per K/V row
-  constexpr int KS = D / 16;     // k-steps of the score product
+  constexpr int EB = F8 ? 1 : 2; // bytes per element
+  constexpr int ROWB = D * EB;   // bytes per K/V row
+  constexpr int CH = ROWB / 16;  // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;     // k-steps of the bf16 score product
+  constexpr int KS8 = D / 64;    // k-steps of the fp8 score product
   constexpr int NT = D / 32;     // 32-wide d tiles of the PV product
-  constexpr int TILE_BYTES = kBN * D * 2;
+  constexpr int TILE_BYTES = kBN * ROWB;
+  // chunk swizzle of a tile row: bf16 rows use swz; fp8 rows are 128 bytes,
+  // two per 256-byte bank window, and rows r, r + 2 of a 4-row group go to
+  // different row halves, so the score reads (16 rows, one chunk) and the
+  // transposed V reads (16 rows x 2 chunks) hit 16 chunk positions
+  auto sw = [](int r) {
+    if constexpr (F8) {
+      const int j = (r >> 1) & 7;
+      return ((j & 1) << 2) | (j >> 1);
+    } else {
+      return swz<CH>(r);
+    }
+  };
   // two K/V buffers as four distinct LDS objects, selected at compile time,
   // so the compiler can tell the tile being read from the one being filled
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
@@ -101,11 +125,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   const int S = a.S;                     // query rows
   const int SK = GEN ? a.S_k : a.S;      // keys
   const size_t q_row_stride = (size_t)a.h_q * D;   // elements between consecutive tokens of q/out
-  const size_t kv_row_stride = (size_t)a.n_kv * D;
+  const size_t kv_row_bytes = (size_t)a.n_kv * ROWB;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): Q[qrow][16ks + 8h2 .. +7]
-  u32x4 qf[KS];
-  {
+  // ---- Q fragments (B operand of S^T = K Q^T).  bf16: Q[qrow][16ks + 8h2 ..
+  // +7]; fp8: Q[qrow][64ks + 32h2 .. +31] (the K fragments take the same k order)
+  u32x4 qf[F8 ? 1 : KS];
+  i32x8 qf8[F8 ? KS8 : 1];
+  float qk_log2 = a.qk_scale_log2, out_scale = 1.0f;
+  if constexpr (!F8) {
     const uint16_t* qp = a.q + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D + 8 * h2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -113,6 +140,20 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       if (qrow < S) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
       qf[ks] = v;
     }
+  } else {
+    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D +
+                     32 * h2;
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (qrow < S) {
+        lo = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
+        hi = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
+      }
+      qf8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    qk_log2 *= a.q_descale[(size_t)b * a.h_q + head] * a.k_descale[(size_t)b * a.n_kv + g];
+    out_scale = a.v_descale[(size_t)b * a.n_kv + g];
   }
 
   const int row_end = min(qb * BM + BM, S);        // exclusive, over the whole workgroup
@@ -134,8 +175,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   const int wave_kmin = kend_of(row0);       // ... and all of them see keys below this
   const int lane_kend = kend_of(qrow);
 
-  const uint16_t* kbase = a.k + (size_t)b * SK * kv_row_stride + (size_t)g * D;
-  const uint16_t* vbase = a.v + (size_t)b * SK * kv_row_stride + (size_t)g * D;
+  const char* kbase = reinterpret_cast<const char*>(a.k) + ((size_t)b * SK * a.n_kv + g) * ROWB;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + ((size_t)b * SK * a.n_kv + g) * ROWB;
   // ---- K/V tiles go straight from global memory into LDS (no VGPR staging).
   // One wave instruction fills 1 KiB of LDS at (wave-uniform base + lane*16),
   // i.e. 64/CH consecutive tile rows; each lane picks the global 16-byte chunk
@@ -159,18 +200,18 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
 #pragma unroll
   for (int u = 0; u < NINS; ++u) {
     const int r = (u * kWaves + wave) * RPI + dma_r;
-    dma_off[u] = (uint32_t)(r * kv_row_stride + (dma_c ^ swz<CH>(r)) * 8);
+    dma_off[u] = (uint32_t)(r * kv_row_bytes + (dma_c ^ sw(r)) * 16);
   }
   auto dma_tile = [&](int j, char* kdst, char* vdst) {
     const int key0 = j * kBN;
     if (key0 + kBN <= kv_n) {
-      const uint16_t* kt = kbase + (size_t)key0 * kv_row_stride;
-      const uint16_t* vt = vbase + (size_t)key0 * kv_row_stride;
+      const char* kt = kbase + (size_t)key0 * kv_row_bytes;
+      const char* vt = vbase + (size_t)key0 * kv_row_bytes;
 #pragma unroll
       for (int u = 0; u < NINS; ++u) {
         const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
-        __builtin_amdgcn_global_load_lds(kt + dma_off[u], (lds_void*)(kdst + r0 * (2 * D)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + dma_off[u], (lds_void*)(vdst + r0 * (2 * D)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kt + dma_off[u], (lds_void*)(kdst + r0 * ROWB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + dma_off[u], (lds_void*)(vdst + r0 * ROWB), 16, 0, 0);
       }
     } else {
 #pragma unroll
@@ -178,10 +219,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
         const int r0 = (u * kWaves + wave) * RPI;
         const int r = r0 + dma_r;
         const int key = min(key0 + r, kv_n - 1);
-        const int c = dma_c ^ swz<CH>(r);         // logical chunk stored at this slot
-        const size_t off = (size_t)key * kv_row_stride + c * 8;
-        __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(kdst + r0 * (2 * D)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(vdst + r0 * (2 * D)), 16, 0, 0);
+        const int c = dma_c ^ sw(r);              // logical chunk stored at this slot
+        const size_t off = (size_t)key * kv_row_bytes + c * 16;
+        __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(kdst + r0 * ROWB), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(vdst + r0 * ROWB), 16, 0, 0);
       }
     }
   };
@@ -272,10 +313,27 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
           sacc[0][r] = 0.f;
           sacc[1][r] = 0.f;
         }
+        if constexpr (F8) {
+          // K[key][64ks + 32h2 .. +31]: two 16-byte reads; the swizzle of a
+          // row is the same for both halves (32 rows apart)
+          const char* kp0 = kt + l32 * ROWB;
+          const int swk = sw(l32);
+#pragma unroll
+          for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+              const char* kp = kp0 + kh * 32 * ROWB;
+              const u32x4 lo = lds_load<u32x4>(kp + (((4 * ks + 2 * h2) ^ swk) << 4));
+              const u32x4 hi = lds_load<u32x4>(kp + (((4 * ks + 2 * h2 + 1) ^ swk) << 4));
+              const i32x8 kf8 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+              sacc[kh] = mfma32_fp8(kf8, qf8[ks], sacc[kh]);
+            }
+        } else {
         // swz(krow) is the same for both halves (32 is a multiple of 16)
-        const char* kp0 = kt + l32 * (2 * D);
+        const char* kp0 = kt + l32 * ROWB;
         auto kfrag = [&](int kh, int ks) {
-          return lds_load<u32x4>(kp0 + kh * 32 * (2 * D) + (((2 * ks + h2) ^ swz<CH>(l32)) << 4));
+          return lds_load<u32x4>(kp0 + kh * 32 * ROWB + (((2 * ks + h2) ^ sw(l32)) << 4));
         };
         u32x4 kf[KS][2];
         kf[0][0] = kfrag(0, 0);
@@ -293,6 +351,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
           sacc[0] = mfma32(kf[ks][0], qf[ks], sacc[0]);
           sacc[1] = mfma32(kf[ks][1], qf[ks], sacc[1]);
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);    // then the products of step ks
+        }
         }
         if (diag) {
 #pragma unroll
@@ -325,7 +384,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(__builtin_fmaf(sacc[kh][r], a.qk_scale_log2, -mref));
+            const float p = fast_exp2(__builtin_fmaf(sacc[kh][r], qk_log2, -mref));
             sacc[kh][r] = p;
             psum += p;
           }
@@ -345,7 +404,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       bool slow = j == 0;
       if (!slow) {
         psum = probs(sacc, m);
-        slow = __builtin_amdgcn_ballot_w64(!(psum <= 0x1p30f)) != 0;  // also catches inf / NaN
+        // bound: bf16 P has range to spare; e4m3 P must stay below its 448
+        // maximum, which psum <= 256 guarantees for every p of the tile
+        slow = __builtin_amdgcn_ballot_w64(!(psum <= (F8 ? 256.0f : 0x1p30f))) != 0;  // also catches inf / NaN
         if (slow) scores(sacc);
       }
       if (slow) {
@@ -354,7 +415,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kh][r]);
-        mt = wave_max_xor(mt, 32) * a.qk_scale_log2;  // scale > 0 keeps the order
+        mt = wave_max_xor(mt, 32) * qk_log2;  // scale > 0 keeps the order
         const float m_new = fmaxf(m, mt);
         if constexpr (!GEN) {
           // finite: key 0 is visible to every row
@@ -376,6 +437,41 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
         }
       }
       l += psum;
+      if constexpr (F8) {
+        // ---- O^T += V^T P^T on one 64-key product per 32-wide d tile.  P
+        // byte b = 16kh + r of a lane is the score register sacc[kh][r], key
+        // 32kh + 8(r/4) + 4h2 + r%4.  ds_read_b64_tr_b8 hands output lane
+        // 16gg + 8u + c byte j of source lane 16gg + 2j + u (byte c of its 8):
+        // source lane (gg, j, u) therefore reads, for read t (bytes 8t..8t+7),
+        // key 32(t/2) + 16(t%2) + 8(j/4) + 4(gg/2) + j%4 at d columns
+        // 32dt + 16(gg%2) + 8u .. +7, so that output lane l holds d = 32dt +
+        // l%32 for exactly the keys of its P bytes.
+        i32x8 pf8;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const f32x16& sp = sacc[w >> 2];
+          const int r0 = 4 * (w & 3);
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(sp[r0], sp[r0 + 1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(sp[r0 + 2], sp[r0 + 3], x, true);
+          pf8[w] = x;
+        }
+        const int gg = lane >> 4, jj = (lane & 15) >> 1, uu = lane & 1;
+        const int vkey = 8 * (jj >> 2) + 4 * (gg >> 1) + (jj & 3);  // plus 16t: same swizzle for every t
+        const int swv = sw(vkey);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int chunk = (2 * nt + (gg & 1)) ^ swv;
+          i32x8 vf8;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(vt + (16 * t + vkey) * ROWB + (chunk << 4) + 8 * uu));
+            vf8[2 * t] = r[0];
+            vf8[2 * t + 1] = r[1];
+          }
+          o[nt] = mfma32_fp8(vf8, pf8, o[nt]);
+        }
+      } else {
       // ---- O^T += V^T P^T, 4 k-steps of 16 keys
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -390,11 +486,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
           const int c = col >> 3, w = col & 7;
           const int ra = 16 * p + 4 * h2 + (s16 >> 2);
           const int rbw = ra + 8;
-          const u32x2 va = lds_read_tr16(vt + ra * (2 * D) + ((c ^ swz<CH>(ra)) << 4) + 2 * w);
-          const u32x2 vb = lds_read_tr16(vt + rbw * (2 * D) + ((c ^ swz<CH>(rbw)) << 4) + 2 * w);
+          const u32x2 va = lds_read_tr16(vt + ra * ROWB + ((c ^ sw(ra)) << 4) + 2 * w);
+          const u32x2 vb = lds_read_tr16(vt + rbw * ROWB + ((c ^ sw(rbw)) << 4) + 2 * w);
           const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
           o[nt] = mfma32(vf, pf, o[nt]);
         }
+      }
       }
     }
     dma_wait();
@@ -407,7 +504,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
 
   // ---- epilogue: O / l -> bf16, rows < S only
   const float lt = l + __shfl_xor(l, 32, 64);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv = lt > 0.f ? out_scale / lt : 0.f;  // fp8: the V descale folds in here
   if (qrow < S) {
     uint16_t* op = a.out + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D;
 #pragma unroll
@@ -431,6 +528,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_causal_kernel(Pref
 template <int D, int HC>
 __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_masked_kernel(PrefillArgs a) {
   prefill_body<D, HC, true>(a);
+}
+
+template <int HC>
+__global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_fp8_kernel(PrefillArgs a) {
+  prefill_body<128, HC, true, true>(a);
 }
 
 static int gcd_int(int x, int y) {
@@ -464,6 +566,9 @@ static PrefillArgs prefill_args(const void* q, const void* k, const void* v, voi
   a.causal = 1;
   a.kv_lens = nullptr;
   a.mask = nullptr;
+  a.q_descale = nullptr;
+  a.k_descale = nullptr;
+  a.v_descale = nullptr;
   return a;
 }
 
@@ -511,6 +616,27 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
     else GQA_LAUNCH_PREFILL(64, 1);
   }
 #undef GQA_LAUNCH_PREFILL
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
+                              int S_q, int S_k, int h_q, int n_kv, int causal, const int32_t* kv_lens,
+                              const uint8_t* mask, const float* q_descale, const float* k_descale,
+                              const float* v_descale, hipStream_t stream) {
+  const int HC = gcd_int(h_q / n_kv, kWaves);
+  PrefillArgs a = prefill_args(q, k, v, out, qk_scale_log2, B, S_q, h_q, n_kv, HC);
+  a.S_k = S_k;
+  a.causal = causal;
+  a.kv_lens = kv_lens;
+  a.mask = mask;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  const dim3 grid(a.n_wg_pad), block(kWaves * 64);
+  if (HC == 8) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<8>), grid, block, 0, stream, a);
+  else if (HC == 4) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<4>), grid, block, 0, stream, a);
+  else if (HC == 2) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<2>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((gqa_prefill_fp8_kernel<1>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

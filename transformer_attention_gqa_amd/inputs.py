@@ -409,6 +409,7 @@ class MaskedPrefillWorkload:
     kv_lens: Optional[Tuple[int, int]] = None
     mask: Optional[str] = None
     doc_lens: Tuple[int, int] = (512, 2048)
+    dtype: str = "bf16"  # or "fp8": e4m3 codes with one descale factor per (batch, head)
 
     @property
     def G(self):
@@ -425,17 +426,34 @@ GQA_PREFILL_PADDED = MaskedPrefillWorkload("gqa_prefill_padded_bf16", B=4, S_q=4
 # c4 with packed documents of 512..2048 tokens (dense block-diagonal mask on top of the causal rule)
 GQA_PREFILL_DOCS = MaskedPrefillWorkload("gqa_prefill_docs_bf16", B=4, S_q=4096, S_k=4096, h_q=32, n_kv=8,
                                          d_h=128, causal=True, seed=10, mask="docs")
-MASKED_PREFILL_WORKLOADS = {w.name: w for w in (GQA_PREFILL_PADDED, GQA_PREFILL_DOCS)}
+# c4 (causal, B=4, S=4096, 32 query / 8 K/V heads, d=128) on fp8 codes
+GQA_PREFILL_FP8 = MaskedPrefillWorkload("gqa_prefill_causal_fp8", B=4, S_q=4096, S_k=4096, h_q=32, n_kv=8, d_h=128,
+                                        causal=True, seed=11, dtype="fp8")
+MASKED_PREFILL_WORKLOADS = {w.name: w for w in (GQA_PREFILL_PADDED, GQA_PREFILL_DOCS, GQA_PREFILL_FP8)}
 
 
 @dataclass
 class MaskedPrefillInputs:
     wl: MaskedPrefillWorkload
-    q: torch.Tensor                  # [B, S_q, h_q, d] bf16
-    k: torch.Tensor                  # [B, S_k, n_kv, d] bf16
+    q: torch.Tensor                  # [B, S_q, h_q, d] bf16 (fp8: uint8 e4m3 codes)
+    k: torch.Tensor                  # [B, S_k, n_kv, d] bf16 (fp8: uint8 codes)
     v: torch.Tensor
     kv_lens: Optional[torch.Tensor]  # [B] int32
     mask: Optional[torch.Tensor]     # [B, S_q, S_k] uint8
+    q_descale: Optional[torch.Tensor] = None  # [B, h_q] float32 (fp8 only)
+    k_descale: Optional[torch.Tensor] = None  # [B, n_kv] float32
+    v_descale: Optional[torch.Tensor] = None
+
+
+def quantize_e4m3_heads(x):
+    """float32 [B, S, H, d] -> (uint8 e4m3 codes, float32 descale [B, H]): one
+    absmax factor per (batch, head), descale = amax / 448 (amax = 0 -> 1),
+    code = RNE(x / descale)."""
+    x = x.float()
+    amax = x.abs().amax(dim=(1, 3))
+    descale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax)).float()
+    y = (x / descale[:, None, :, None]).clamp(-FP8_MAX, FP8_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), descale
 
 
 def draw_mask(kind, B, S_q, S_k, seed, doc_lens=(512, 2048)):
@@ -463,9 +481,15 @@ def make_masked_prefill_inputs(wl, device="cpu", kv_lens=None, mask=None, poison
     fills key/value rows at or past each key length with NaN."""
     seed = wl.seed if seed is None else seed
     g = _gen(device, seed)
-    q = torch.randn((wl.B, wl.S_q, wl.h_q, wl.d_h), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn((wl.B, wl.S_k, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn((wl.B, wl.S_k, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((wl.B, wl.S_q, wl.h_q, wl.d_h), generator=g, device=device, dtype=torch.float32)
+    k = torch.randn((wl.B, wl.S_k, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((wl.B, wl.S_k, wl.n_kv, wl.d_h), generator=g, device=device, dtype=torch.float32)
+    descales = (None, None, None)
+    if wl.dtype == "fp8":
+        (q, dq), (k, dk), (v, dv) = quantize_e4m3_heads(q), quantize_e4m3_heads(k), quantize_e4m3_heads(v)
+        descales = (dq, dk, dv)
+    else:
+        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
     if kv_lens is None and wl.kv_lens is not None:
         kv_lens = draw_lengths(wl.B, wl.kv_lens[0], wl.kv_lens[1], seed)
     if kv_lens is not None:
@@ -473,14 +497,18 @@ def make_masked_prefill_inputs(wl, device="cpu", kv_lens=None, mask=None, poison
         if poison_padding:
             for b in range(wl.B):
                 n = int(min(max(int(kv_lens[b]), 0), wl.S_k))
-                k[b, n:] = float("nan")
-                v[b, n:] = float("nan")
+                if wl.dtype == "fp8":
+                    k[b, n:] = POISON_CODE["fp8"]
+                    v[b, n:] = POISON_CODE["fp8"]
+                else:
+                    k[b, n:] = float("nan")
+                    v[b, n:] = float("nan")
         kv_lens = kv_lens.to(device)
     if mask is None and wl.mask is not None:
         mask = draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, seed, wl.doc_lens)
     if mask is not None:
         mask = torch.as_tensor(mask).to(torch.uint8).contiguous().to(device)
-    return MaskedPrefillInputs(wl, q, k, v, kv_lens, mask)
+    return MaskedPrefillInputs(wl, q, k, v, kv_lens, mask, *descales)
 
 
 def stored_numpy(t):

@@ -80,7 +80,7 @@ def prefill_causal_flops(B, S, h_q, d_h):
     return 4 * B * h_q * d_h * S * (S + 1) // 2
 
 
-def visible_pairs(S_q, S_k, causal, kv_lens=None, mask=None):
+def visible_pairs(B, S_q, S_k, causal, kv_lens=None, mask=None):
     """Number of (batch, query row, key) pairs a general-mask prefill must
     compute: the causal rule (end-aligned), key lengths and dense mask
     combined.  Host-side accounting with torch (CPU)."""
@@ -88,7 +88,6 @@ def visible_pairs(S_q, S_k, causal, kv_lens=None, mask=None):
     r = torch.arange(S_q)[:, None]
     c = torch.arange(S_k)[None, :]
     vis = (c <= r + (S_k - S_q)) if causal else torch.ones(S_q, S_k, dtype=torch.bool)
-    B = len(kv_lens) if kv_lens is not None else (mask.shape[0] if mask is not None else 1)
     vis = vis[None].expand(B, S_q, S_k)
     if kv_lens is not None:
         vis = vis & (c[None] < torch.as_tensor(kv_lens).reshape(B, 1, 1).cpu())
