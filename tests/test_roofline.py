@@ -73,6 +73,7 @@ def test_visible_pairs_closed_forms():
     assert roofline.visible_pairs(1, 2, 5, True) == 4 + 5
     assert roofline.visible_pairs(2, 3, 3, False, [1, 3]) == 3 * 1 + 3 * 3
     m = torch.zeros(1, 2, 4, dtype=torch.uint8)
-    m[0, 1, 0] = m[0, 1, 3] = 7
-    assert roofline.visible_pairs(1, 2, 4, True, None, m) == 1
+    m[0, 1, 0] = m[0, 1, 3] = 7   # row 1 (key position 3) sees keys 0..3: both kept keys count
+    m[0, 0, 3] = 1                # row 0 (key position 2) cannot see key 3
+    assert roofline.visible_pairs(1, 2, 4, True, None, m) == 2
     assert roofline.prefill_masked_flops(32, 128, 10) == 4 * 32 * 128 * 10
