@@ -804,31 +804,42 @@ struct SlabPieces {
 // Merges the partials of one slab into its nh output rows (heads head0 ..
 // head0 + nh - 1 of sequence b).  Thread tid of nthreads takes the elements
 // tid, tid + nthreads, ... of the nh x D/4 grid of 4-column groups; each
-// element folds the pieces in one pass with a running maximum.
+// element folds the pieces with a running maximum, four at a time with all
+// eight loads of a batch in flight together (indices past the last piece
+// repeat it and are skipped).
 template <int D, bool OUT_BF16>
 __device__ __forceinline__ void merge_slab(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                            void* __restrict__ out, int hpc, int h_q, int b, int head0, int nh,
                                            const SlabPieces& sp, int tid, int nthreads) {
   constexpr int D4 = D / 4;
+  constexpr int PB = 4;  // pieces per batch
   for (int e = tid; e < nh * D4; e += nthreads) {
     const int hl = e / D4, d4 = e - hl * D4;
     float M = kNegInf, denom = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int p = 0; p < sp.n; ++p) {
-      const size_t row = (size_t)sp.slot(p) * hpc + hl;
-      const float ms = part_ml[row * 2], ls = part_ml[row * 2 + 1];
-      const f32x4 os = *reinterpret_cast<const f32x4*>(part_o + row * D + 4 * d4);
-      if (ms == kNegInf) continue;  // a piece that saw no visible key
-      if (ms > M) {
-        const float r = M == kNegInf ? 0.f : fast_exp2(M - ms);
-        acc *= r;
-        denom *= r;
-        M = ms;
+    for (int p0 = 0; p0 < sp.n; p0 += PB) {
+      f32x2 ml[PB];
+      f32x4 os[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const size_t row = (size_t)sp.slot(min(p0 + u, sp.n - 1)) * hpc + hl;
+        ml[u] = *reinterpret_cast<const f32x2*>(part_ml + row * 2);
+        os[u] = *reinterpret_cast<const f32x4*>(part_o + row * D + 4 * d4);
       }
-      const float f = fast_exp2(ms - M);
-      acc += f * os;
-      denom += f * ls;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const float ms = ml[u][0], ls = ml[u][1];
+        if (p0 + u >= sp.n || ms == kNegInf) continue;  // past the last piece, or a piece with no visible key
+        if (ms > M) {
+          const float r = M == kNegInf ? 0.f : fast_exp2(M - ms);
+          acc *= r;
+          denom *= r;
+          M = ms;
+        }
+        const float f = fast_exp2(ms - M);
+        acc += f * os[u];
+        denom += f * ls;
+      }
     }
     acc *= denom > 0.f ? 1.0f / denom : 0.f;
     const size_t idx = ((size_t)b * h_q + head0 + hl) * D + 4 * d4;
@@ -857,7 +868,10 @@ __global__ __launch_bounds__(256) void gqa_decode_combine(CombineArgs c) {
   const int G = c.h_q / c.n_kv;
   const int hloc0 = hc * c.heads_per_chunk;
   const int nh = min(c.heads_per_chunk, G - hloc0);
-  const int nt = seq_tiles(c.seq_lens, b, c.S_max, c.tile);
+  const LaneLens ll = load_lane_lens(c.seq_lens, c.B, c.S_max, lane);
+  long long T, before_b;
+  int nt;
+  slab_position(ll, c.seq_lens, c.B, c.S_max, c.tile, spb, b, lane, T, before_b, nt);
   const int tid = blockIdx.y * 256 + threadIdx.x;
   if (nt == 0) {  // empty sequence: zero rows
     const SlabPieces none(sigma, 0, 0, 1, 1);
@@ -865,8 +879,7 @@ __global__ __launch_bounds__(256) void gqa_decode_combine(CombineArgs c) {
                                    none, tid, gridDim.y * 256);
     return;
   }
-  const long long T = tiles_before(c.seq_lens, c.B, c.S_max, c.tile, spb, lane);
-  const long long first = tiles_before(c.seq_lens, b, c.S_max, c.tile, spb, lane) + (long long)slab_in_b * nt;
+  const long long first = before_b + (long long)slab_in_b * nt;
   const SlabPieces sp(sigma, first, nt, T, c.W);
   merge_slab<D, OUT_BF16>(c.part_o, c.part_ml, c.out, c.heads_per_chunk, c.h_q, b, g * G + hloc0, nh, sp,
                                  tid, gridDim.y * 256);

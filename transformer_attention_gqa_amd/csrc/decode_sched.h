@@ -120,4 +120,22 @@ static __device__ void locate_tile_cached(const LaneLens& ll, const int32_t* seq
   base_out = __shfl(incl, first, 64) - (long long)nt_out * spb;
 }
 
+// For sequence b: the tiles of all slabs of all sequences (T), those of the
+// sequences before b, and b's tiles per slab -- one length load per lane when
+// B <= 64.
+static __device__ void slab_position(const LaneLens& ll, const int32_t* seq_lens, int B, int S_max, int tile,
+                                     int spb, int b, int lane, long long& T, long long& before_b, int& nt_b) {
+  if (!ll.fits) {
+    T = tiles_before(seq_lens, B, S_max, tile, spb, lane);
+    before_b = tiles_before(seq_lens, b, S_max, tile, spb, lane);
+    nt_b = seq_tiles(seq_lens, b, S_max, tile);
+    return;
+  }
+  const int nt = (ll.len + tile - 1) / tile;
+  const long long own = (long long)nt * spb;
+  T = wave_sum_ll(own);
+  before_b = wave_sum_ll(lane < b ? own : 0);
+  nt_b = __shfl(nt, b, 64);
+}
+
 }  // namespace gqa
