@@ -9,19 +9,21 @@
 // h query heads.  A token costs d_c * 2 bytes, read once for both products.
 //
 // Work decomposition (MI355X): the same persistent balanced schedule as the
-// GQA decode (one slab per sequence, all heads in one workgroup).  The 8
-// wavefronts of a workgroup work on the same 32-token tile, wave w owning the
-// latent slice [w * d_c / 8, (w + 1) * d_c / 8):
-//  * each wave loads only its slice of the tile (a 128-byte piece of every
-//    token row at d_c = 512) into a private LDS slab, which serves as its
-//    share of K (scores) and of V (weighted sum);
-//  * partial scores S^T[token][head] over the slice come from
-//    v_mfma_f32_32x32x16_bf16; the 8 partials are summed through LDS (each
-//    wave sums a quarter of the tile's rows, two barriers per tile) and every
-//    wave runs the same online softmax on the full scores;
+// GQA decode (slabs of one sequence and one chunk of up to 64 heads, all
+// heads of a chunk in one workgroup).  The 8 wavefronts of a workgroup share
+// each 32-token tile:
+//  * wave w loads the latent slice [w * d_c / 8, (w + 1) * d_c / 8) of every
+//    row of the tile (a 128-byte piece at d_c = 512) and writes it into the
+//    workgroup's LDS copy of the tile (three tiles resident: the one in use
+//    and the next two);
+//  * the scores S^T[token][head] of the tile are cut into 16-token x 16-head
+//    blocks over the full latent width, one block per wave, on
+//    v_mfma_f32_16x16x32_bf16; they go to LDS and, after one barrier, every
+//    wave reads the scores of all heads and runs the same online softmax;
 //  * the weighted sum O^T[latent][head] += C^T P^T runs on the wave's own
-//    slice, so a wave's accumulator holds d_c / 8 latent values of every head
-//    and the partial results need no merge across waves.
+//    latent slice (v_mfma_f32_32x32x16_bf16), so a wave's accumulator holds
+//    d_c / 8 latent values of every head and the partials need no merge
+//    across waves.
 #include "decode_sched.h"
 #include "gqa_device.h"
 #include "gqa_launch.h"
@@ -68,20 +70,22 @@ __device__ __forceinline__ MlaSegment mla_segment(const MlaArgs& a, const LaneLe
 template <int D, int HB>
 __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a) {
   constexpr int NW = kMlaWaves;
-  constexpr int DS = D / NW;        // latent values per wave
-  constexpr int RB = 2 * DS;        // bytes of one token's slice
-  constexpr int CHS = RB / 16;      // 16-byte chunks per slice row
-  constexpr int SWS = 256 / RB;     // slice rows per 256-byte bank window
-  constexpr int KSW = DS / 16;      // k-steps of the partial score product
-  constexpr int NT = DS / 32;       // 32-wide latent tiles of the weighted sum
-  constexpr int HPC = 32 * HB;      // query heads per chunk
-  constexpr int LPR = RB / 16;      // lanes per row of the tile load
-  constexpr int RPL = 64 / LPR;     // rows per load instruction
+  constexpr int DS = D / NW;          // latent values per wave (weighted sum, loads)
+  constexpr int ROWB = 2 * D;         // bytes of a token row
+  constexpr int HPC = 32 * HB;        // query heads per chunk
+  constexpr int NT = DS / 32;         // 32-wide latent tiles of the wave's weighted sum
+  constexpr int NBLK = 2 * (HPC / 16);  // score blocks: 2 token halves x HPC/16 head groups
+  constexpr int KSPLIT = NW / NBLK;   // waves per block, each over 1/KSPLIT of the latent width
+  constexpr int KQ = D / 32 / KSPLIT; // k-steps of a wave's share of a 16 x 16 score block
+  constexpr int SROW = kMlaTile + 4;  // floats per score row (padded: 16 rows -> 16 bank positions)
+  constexpr int LPR = 2 * DS / 16;    // lanes per row of a slice load
+  constexpr int RPL = 64 / LPR;       // rows per load instruction
   constexpr int NLD = kMlaTile / RPL;
-  static_assert(NT >= 1 && NLD >= 1 && NLD * RPL == kMlaTile, "latent slice shape");
-  __shared__ __attribute__((aligned(16))) char slab[NW][2][kMlaTile * RB];
-  __shared__ __attribute__((aligned(16))) f32x4 part[NW][HB][4][64];  // partial scores, accumulator layout
-  __shared__ __attribute__((aligned(16))) f32x4 fin[HB][4][64];       // summed scores
+  // register sets of tile loads in flight (64 heads at d_c = 512 leave room for one)
+  constexpr int NSET = D == 512 ? (HB == 1 ? 2 : 1) : (HB == 1 ? 3 : 2);
+  static_assert(NT >= 1 && NLD >= 1 && NLD * RPL == kMlaTile && NBLK * KSPLIT == NW, "latent tile shape");
+  __shared__ __attribute__((aligned(16))) char tiles[3][kMlaTile * ROWB];
+  __shared__ __attribute__((aligned(16))) float sc[2][KSPLIT][HPC * SROW];  // partial scores per latent share
 
   const int W = gridDim.x;
   const int w = blockIdx.x;
@@ -98,26 +102,16 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
   const int n_local = (int)(hi - lo);
   const int dsl = wave * DS;  // first latent index of this wave's slice
 
-  // slice row r, chunk c sits at chunk position c ^ swz_row(r).  SWS rows
-  // share a 256-byte window of 16 chunk positions; swz_row permutes the chunk
-  // positions of the rows that share a window position, so the 16 lanes of a
-  // score fragment read (16 consecutive rows, one chunk) hit 16 positions.
-  // With 8 chunks per row it also sends rows r and r + 2 of a 4-row group to
-  // different halves of the row, so the transposed reads of the weighted sum
-  // (4 consecutive rows x 4 consecutive chunks) hit 16 positions as well.
-  auto swz_row = [](int r) {
-    const int j = (r / SWS) % CHS;
-    if constexpr (CHS == 8) return ((j & 1) << 2) | (j >> 1);
-    else return j;
-  };
+  // Row r, chunk c of a tile sits at chunk position c ^ swz(r) (swz permutes
+  // the 16 positions of a 256-byte window): the score reads (16 rows, one
+  // chunk) and the transposed reads of the weighted sum (4 rows x 4 chunks)
+  // each hit 16 positions.
+  auto tile_off = [](int r, int c) { return r * ROWB + ((c ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 4); };
+  auto tile_at = [&](const char* t, int r, int c) { return t + tile_off(r, c); };
 
-  // ---- tile loads: lane (row ld_row, chunk ld_chunk) of each instruction
+  // ---- tile loads: this wave's slice, lane (row ld_row, chunk ld_chunk of the slice)
   const int ld_row = lane / LPR, ld_chunk = lane % LPR;
-  const unsigned lane_off = ld_row * (2 * D) + 2 * dsl + 16 * ld_chunk;
-  // NSET register sets of NLD loads each: while a wave computes one tile
-  // from LDS, the next NSET tiles are in flight (64 heads at d_c = 512 leave
-  // registers for one set only)
-  constexpr int NSET = HB == 1 ? 3 : (D == 512 ? 1 : 2);
+  const unsigned lane_off = ld_row * ROWB + 2 * dsl + 16 * ld_chunk;
   u32x4 cr0[NLD], cr1[NSET >= 2 ? NLD : 1], cr2[NSET == 3 ? NLD : 1];
   // a tile's first row is the base of a buffer resource that ends at the
   // segment's last valid row: rows past it read as zero without an access
@@ -125,33 +119,33 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
     const int tt0 = s.t_begin + tile * kMlaTile;
     const size_t row0 = (size_t)uniform((long long)((size_t)s.b * a.S_max + tt0));
     const int nvalid = uniform(min(kMlaTile, s.t_end - tt0));
-    const auto rc = make_rsrc(static_cast<const char*>(a.c) + row0 * (2 * D), nvalid * (2 * D));
+    const auto rc = make_rsrc(static_cast<const char*>(a.c) + row0 * ROWB, nvalid * ROWB);
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) creg[u] = buffer_load_x4_nt(rc, lane_off + u * RPL * (2 * D));
+    for (int u = 0; u < NLD; ++u) creg[u] = buffer_load_x4_nt(rc, lane_off + u * RPL * ROWB);
   };
-  auto stage = [&](const u32x4* creg, int buf) {
-    wave_lds_fence();
+  // this wave's slice of a staged tile into the workgroup's copy; readers see
+  // it after the next barrier
+  auto stage = [&](const u32x4* creg, char* t) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int r = u * RPL + ld_row;
-      lds_store(slab[wave][buf] + r * RB + ((ld_chunk ^ swz_row(r)) << 4), creg[u]);
+      lds_store(t + tile_off(r, dsl / 8 + ld_chunk), creg[u]);
     }
-    wave_lds_fence();
   };
 
-  // ---- query fragments of the slice (B operand of S^T = C Q^T); heads past
-  // h_q in the last chunk read as zero
-  u32x4 qf[HB][KSW];
+  // ---- score share of this wave: tokens 16 tb .. +15 of the tile, heads
+  // 16 hq .. +15 of the chunk, latent values [kq0, kq0 + D / KSPLIT); B
+  // operand fragments Q[head][kq0 + 32 ks + 8 gi .. +7], zero past h_q
+  const int blk = wave % NBLK, ksh = wave / NBLK;
+  const int tb = blk & 1, hq = blk >> 1;
+  const int kq0 = ksh * (D / KSPLIT);
+  u32x4 qf[KQ];
   auto load_q = [&](const MlaSegment& s) {
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (size_t)s.b * a.h_q * D + dsl + 8 * h2;
+    const int head = s.hc * HPC + 16 * hq + s16;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((size_t)s.b * a.h_q + head) * D + kq0 + 8 * gi;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const int head = s.hc * HPC + 32 * hb + l32;
-#pragma unroll
-      for (int ks = 0; ks < KSW; ++ks)
-        qf[hb][ks] = head < a.h_q ? *reinterpret_cast<const u32x4*>(qb + (size_t)head * D + 16 * ks)
-                                  : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ks = 0; ks < KQ; ++ks)
+      qf[ks] = head < a.h_q ? *reinterpret_cast<const u32x4*>(qb + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
   };
 
   f32x16 o[HB][NT];
@@ -186,7 +180,8 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
     }
   };
 
-  // ---- prologue: the first tile in LDS, the next NSET in flight
+  // ---- prologue: tiles 0 and 1 in LDS, the next NSET in flight (tile t in
+  // register set t % NSET)
   MlaSegment cur = mla_segment(a, ll, lo, hi, w, lane);
   MlaSegment ld = cur;  // segment of the tile issued last
   int cur0 = 0, ld0 = 0;  // local index of each segment's first tile
@@ -197,7 +192,7 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
     if (k >= n_local) {
       const auto none = make_rsrc(a.c, 0);
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) creg[u] = buffer_load_x4_nt(none, lane_off + u * RPL * (2 * D));
+      for (int u = 0; u < NLD; ++u) creg[u] = buffer_load_x4_nt(none, lane_off + u * RPL * ROWB);
       return;
     }
     if (k - ld0 >= ld.ntile) {
@@ -206,71 +201,63 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
     }
     issue(creg, ld, k - ld0);
   };
+  auto set_of = [&](int t) -> u32x4* {  // (t is a compile-time residue where it matters)
+    if constexpr (NSET == 1) return cr0;
+    else if constexpr (NSET == 2) return (t & 1) ? cr1 : cr0;
+    else return t % 3 == 0 ? cr0 : (t % 3 == 1 ? cr1 : cr2);
+  };
   issue(cr0, ld, 0);
   if constexpr (NSET >= 2) prefetch(cr1, 1);
   if constexpr (NSET == 3) prefetch(cr2, 2);
-  stage(cr0, 0);
+  stage(cr0, tiles[0]);
   prefetch(cr0, NSET);
+  stage(set_of(1), tiles[1]);
+  prefetch(set_of(1), 1 + NSET);
   reset();
+  __syncthreads();  // every wave's slice of tile 0 written before its scores are read
 
-  // one tile: compute it from LDS, stage the next one from `next` (which
-  // then takes the tile NSET further on), close the segment at its end
+  // one tile: its scores (score waves), one barrier, softmax and weighted sum
+  // (every wave), then stage tile k + 2 from `next` (which takes tile k + 2 +
+  // NSET) and close the segment at its end
   auto step = [&](int k, u32x4* next) {
-    const int buf = k & 1;
+    const char* ts = tiles[k % 3];
+    float (*sk)[HPC * SROW] = sc[k & 1];
     const int tl = k - cur0;
     const int tt0 = cur.t_begin + tl * kMlaTile;
-    const char* cs = slab[wave][buf];
-    // ---- partial scores over this wave's slice: lane holds tokens
-    // 8(r/4) + 4h2 + r%4 of head 32hb + l32
-    f32x16 s[HB];
+    {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int row = 16 * tb + s16;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[hb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSW; ++ks) {
-      const u32x4 kf = lds_load<u32x4>(cs + l32 * RB + (((2 * ks + h2) ^ swz_row(l32)) << 4));
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) s[hb] = mfma32(kf, qf[hb][ks], s[hb]);
-    }
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        part[wave][hb][r4][lane] = f32x4{s[hb][4 * r4], s[hb][4 * r4 + 1], s[hb][4 * r4 + 2], s[hb][4 * r4 + 3]};
-    __syncthreads();
-    // ---- sum the partials: thread e of the workgroup takes element e
-    for (int e = threadIdx.x; e < HB * 4 * 64; e += NW * 64) {
-      const int hb = e / 256, r4 = (e / 64) % 4, ln = e % 64;
-      f32x4 acc = part[0][hb][r4][ln];
-#pragma unroll
-      for (int wv = 1; wv < NW; ++wv) acc += part[wv][hb][r4][ln];
-      fin[hb][r4][ln] = acc;
+      for (int ks = 0; ks < KQ; ++ks)
+        acc = mfma16(lds_load<u32x4>(tile_at(ts, row, kq0 / 8 + 4 * ks + gi)), qf[ks], acc);
+      // lane holds the share's S^T[token 16 tb + 4 gi + i][head 16 hq + s16]
+      lds_store(sk[ksh] + (16 * hq + s16) * SROW + 16 * tb + 4 * gi, acc);
     }
     __syncthreads();
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 v = fin[hb][r4][lane];
-        s[hb][4 * r4] = v[0];
-        s[hb][4 * r4 + 1] = v[1];
-        s[hb][4 * r4 + 2] = v[2];
-        s[hb][4 * r4 + 3] = v[3];
-      }
     // ---- online softmax (the same on every wave) and the weighted sum of
     // this wave's slice; O and l share a reference max that moves only when a
-    // tile's max exceeds it by more than kMlaSlack
+    // tile's max exceeds it by more than kMlaSlack.  Lane (l32, h2) takes
+    // head 32 hb + l32, tokens 8 (r/4) + 4 h2 + r%4.
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
+      f32x16 s;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v = lds_load<f32x4>(sk[0] + (32 * hb + l32) * SROW + 8 * r4 + 4 * h2);
+#pragma unroll
+        for (int q = 1; q < KSPLIT; ++q) v += lds_load<f32x4>(sk[q] + (32 * hb + l32) * SROW + 8 * r4 + 4 * h2);
+        s[4 * r4] = v[0];
+        s[4 * r4 + 1] = v[1];
+        s[4 * r4 + 2] = v[2];
+        s[4 * r4 + 3] = v[3];
+      }
       if (tt0 + kMlaTile > cur.t_end) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s[hb][r] = tt0 + 8 * (r >> 2) + 4 * h2 + (r & 3) < cur.t_end ? s[hb][r] : kNegInf;
+        for (int r = 0; r < 16; ++r) s[r] = tt0 + 8 * (r >> 2) + 4 * h2 + (r & 3) < cur.t_end ? s[r] : kNegInf;
       }
       float mt = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[hb][r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
       mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
       const bool grow = mt > m[hb] + kMlaSlack;
       const float m_new = grow ? mt : m[hb];
@@ -279,8 +266,8 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[hb][r] = fast_exp2(__builtin_fmaf(s[hb][r], a.qk_scale_log2, -m_new));
-        psum += s[hb][r];
+        s[r] = fast_exp2(__builtin_fmaf(s[r], a.qk_scale_log2, -m_new));
+        psum += s[r];
       }
       l[hb] = l[hb] * alpha + psum;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -290,21 +277,23 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
       // O^T += C^T P^T, two k-steps of 16 tokens (token order as in S)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const u32x4 pf = {pack_bf16x2(s[hb][8 * p + 0], s[hb][8 * p + 1]), pack_bf16x2(s[hb][8 * p + 2], s[hb][8 * p + 3]),
-                          pack_bf16x2(s[hb][8 * p + 4], s[hb][8 * p + 5]), pack_bf16x2(s[hb][8 * p + 6], s[hb][8 * p + 7])};
+        const u32x4 pf = {pack_bf16x2(s[8 * p + 0], s[8 * p + 1]), pack_bf16x2(s[8 * p + 2], s[8 * p + 3]),
+                          pack_bf16x2(s[8 * p + 4], s[8 * p + 5]), pack_bf16x2(s[8 * p + 6], s[8 * p + 7])};
         const int ra = 16 * p + 4 * h2 + (s16 >> 2), rb = ra + 8;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const int col = 32 * n + 16 * (gi & 1) + 4 * (s16 & 3);
+          const int col = dsl + 32 * n + 16 * (gi & 1) + 4 * (s16 & 3);
           const int c = col >> 3, wsub = col & 7;
-          const u32x2 va = lds_read_tr16(cs + ra * RB + ((c ^ swz_row(ra)) << 4) + 2 * wsub);
-          const u32x2 vb = lds_read_tr16(cs + rb * RB + ((c ^ swz_row(rb)) << 4) + 2 * wsub);
+          const u32x2 va = lds_read_tr16(tile_at(ts, ra, c) + 2 * wsub);
+          const u32x2 vb = lds_read_tr16(tile_at(ts, rb, c) + 2 * wsub);
           o[hb][n] = mfma32(u32x4{va[0], va[1], vb[0], vb[1]}, pf, o[hb][n]);
         }
       }
     }
-    stage(next, buf ^ 1);
-    prefetch(next, k + 1 + NSET);
+    // ---- tile k + 2 into the buffer tile k - 1 used (every wave is past its
+    // reads: they precede this step's barrier); readers see it after the next
+    stage(next, tiles[(k + 2) % 3]);
+    prefetch(next, k + 2 + NSET);
     // ---- segment end: one partial per head, then the next sequence
     if (tl + 1 == cur.ntile) {
       write_partials(cur);
@@ -319,27 +308,27 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
       }
     }
   };
-  // the register sets rotate with period NSET: whole groups of NSET steps in
-  // a loop without early exits (each set then has the same loads issued after
-  // it on every path, so a stage waits only for its own set), the remainder
-  // after it
+  // step k stages tile k + 2 from set (k + 2) % NSET: whole groups of NSET
+  // steps in a loop without early exits (each set then has the same loads
+  // issued after it on every path, so a stage waits only for its own set),
+  // the remainder after it
   int k = 0;
   if constexpr (NSET == 1) {
     for (; k < n_local; ++k) step(k, cr0);
   } else if constexpr (NSET == 2) {
     for (; k + 2 <= n_local; k += 2) {
-      step(k, cr1);
-      step(k + 1, cr0);
+      step(k, cr0);
+      step(k + 1, cr1);
     }
-    if (k < n_local) step(k, cr1);
+    if (k < n_local) step(k, cr0);
   } else {
     for (; k + 3 <= n_local; k += 3) {
-      step(k, cr1);
-      step(k + 1, cr2);
-      step(k + 2, cr0);
+      step(k, cr2);
+      step(k + 1, cr0);
+      step(k + 2, cr1);
     }
-    if (k < n_local) step(k, cr1);
-    if (k + 1 < n_local) step(k + 1, cr2);
+    if (k < n_local) step(k, cr2);
+    if (k + 1 < n_local) step(k + 1, cr0);
   }
 }
 
