@@ -100,9 +100,8 @@ __device__ __forceinline__ Segment make_segment(const DecodeArgs& a, const LaneL
   nt = uniform(nt);
   L = uniform(L);
   base = uniform(base);
-  const long long local = t - base;
-  const int slab_in_b = (int)(local / nt);
-  const int tile0 = (int)(local - (long long)slab_in_b * nt);
+  int slab_in_b, tile0;
+  split_local(t - base, nt, slab_in_b, tile0);
   Segment s;
   s.b = b;
   s.g = slab_in_b / a.n_hchunk;
@@ -160,8 +159,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 
   const LaneLens ll = load_lane_lens(a.seq_lens, a.B, a.S_max, lane);
   const long long T = uniform(total_tiles_cached(ll, a.seq_lens, a.B, a.S_max, kTile, spb, lane));
-  long long lo = (long long)w * T / W;
-  const long long hi = (long long)(w + 1) * T / W;
+  const TileRanges rg(T, W);
+  long long lo = rg.lo(w);
+  const long long hi = rg.lo(w + 1);
   if (lo >= hi) return;  // uniform over the workgroup
 
   char* kt = smem[wave][0];
@@ -623,8 +623,9 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
   const int spb = a.n_kv * a.n_hchunk;
   const int G = a.h_q / a.n_kv;
   const long long T = tiles_before(a.seq_lens, a.B, a.S_max, kTileF32, spb, lane);
-  const long long lo = (long long)w * T / W;
-  const long long hi = (long long)(w + 1) * T / W;
+  const TileRanges rg(T, W);
+  const long long lo = rg.lo(w);
+  const long long hi = rg.lo(w + 1);
   const float* qg = static_cast<const float*>(a.q);
   const float* kg = static_cast<const float*>(a.k);
   const float* vg = static_cast<const float*>(a.v);
@@ -633,9 +634,8 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
     int b, nt, L;
     long long base;
     locate_tile(a.seq_lens, a.B, a.S_max, kTileF32, spb, t, lane, b, base, nt, L);
-    const long long local = t - base;
-    const int slab_in_b = (int)(local / nt);
-    const int tile0 = (int)(local - (long long)slab_in_b * nt);
+    int slab_in_b, tile0;
+    split_local(t - base, nt, slab_in_b, tile0);
     const int seg = (int)min(hi - t, (long long)(nt - tile0));
     const int g = slab_in_b / a.n_hchunk;
     const int hc = slab_in_b - g * a.n_hchunk;
@@ -790,14 +790,15 @@ __global__ __launch_bounds__(256) void gqa_decode_split_f32(DecodeArgs a) {
 // workgroups from the owner of the slab's first tile to the owner of its last;
 // when T < W a range holds at most one tile and the owners go tile by tile.
 struct SlabPieces {
-  long long first, T, W, wa, sigma;
+  TileRanges rg;
+  long long first, wa, sigma;
   int nt, n;
-  __device__ __forceinline__ SlabPieces(long long sigma_, long long first_, int nt_, long long T_, long long W_)
-      : first(first_), T(T_), W(W_), wa(((first_ + 1) * W_ - 1) / T_), sigma(sigma_), nt(nt_) {
-    n = T >= W ? (int)(((first + nt) * W - 1) / T - wa + 1) : nt;
+  __device__ __forceinline__ SlabPieces(long long sigma_, long long first_, int nt_, long long T_, int W_)
+      : rg(T_, W_), first(first_), wa(rg.owner(first_)), sigma(sigma_), nt(nt_) {
+    n = nt == 0 ? 0 : T_ >= W_ ? (int)(rg.owner(first + nt - 1) - wa + 1) : nt;
   }
   __device__ __forceinline__ long long slot(int p) const {
-    return (T >= W ? wa + p : ((first + p + 1) * W - 1) / T) + sigma;
+    return (rg.T >= rg.W ? wa + p : rg.owner(first + p)) + sigma;
   }
 };
 

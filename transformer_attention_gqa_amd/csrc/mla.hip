@@ -54,9 +54,8 @@ __device__ __forceinline__ MlaSegment mla_segment(const MlaArgs& a, const LaneLe
   nt = uniform(nt);
   L = uniform(L);
   base = uniform(base);
-  const long long local = t - base;
-  const int hc = (int)(local / nt);
-  const int tile0 = (int)(local - (long long)hc * nt);
+  int hc, tile0;
+  split_local(t - base, nt, hc, tile0);
   MlaSegment s;
   s.b = b;
   s.hc = hc;
@@ -96,8 +95,9 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
 
   const LaneLens ll = load_lane_lens(a.seq_lens, a.B, a.S_max, lane);
   const long long T = uniform(total_tiles_cached(ll, a.seq_lens, a.B, a.S_max, kMlaTile, a.n_hchunk, lane));
-  const long long lo = (long long)w * T / W;
-  const long long hi = (long long)(w + 1) * T / W;
+  const TileRanges rg(T, W);
+  const long long lo = rg.lo(w);
+  const long long hi = rg.lo(w + 1);
   if (lo >= hi) return;  // uniform over the workgroup
   const int n_local = (int)(hi - lo);
   const int dsl = wave * DS;  // first latent index of this wave's slice
