@@ -128,6 +128,27 @@ def test_causal_without_masks_equals_causal_kernel():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_all_ones_mask_equals_causal_kernel():
+    """Every tile of an all-ones mask is fully visible, so the general kernel
+    skips the mask tiles and must reproduce attn_prefill_causal bit for bit."""
+    w = wl(2, 332, 332, 16, 4, 128, True, seed=452)  # a dense mask needs S_k % 4 == 0
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV,
+                                            mask=torch.ones((2, 332, 332), dtype=torch.uint8))
+    a = run(inp)
+    b = binding.attn_prefill_causal(inp.q, inp.k, inp.v, w.scale)
+    pu.sync()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_documents_with_full_tiles(causal):
+    """Documents of 96..300 tokens: row blocks see tiles that are hidden,
+    fully visible (no per-element mask) and partly visible, and the rows of a
+    block that starts a new document see nothing for several tiles."""
+    w = wl(2, 700, 700, 8, 2, 128, causal, seed=455, mask="docs", doc_lens=(96, 300))
+    check(inputs.make_masked_prefill_inputs(w, device=DEV))
+
+
 @pytest.mark.parametrize("name", sorted(inputs.MASKED_PREFILL_WORKLOADS))
 def test_full_size_sampled(name):
     """The benchmarked workloads in their launch configuration, on sampled

@@ -160,6 +160,10 @@ __device__ __forceinline__ u32x4 buffer_load_x4_nt(__amdgpu_buffer_rsrc_t r, uns
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCacheNonTemporal));
 }
 
+__device__ __forceinline__ u32x4 buffer_load_x4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }

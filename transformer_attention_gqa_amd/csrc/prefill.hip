@@ -65,7 +65,9 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // (the FP8 mode of FlashAttention-3, "Flash Attention 3 Features"); both
 // products run on v_mfma_f32_32x32x64_f8f6f4, P rounded to e4m3 (kept <= 256
 // by the reference max, below the format's 448), d = 128 only.
-template <int D, int HC, bool GEN, bool F8 = false>
+// MASK (with GEN): a dense mask is given; without it the mask machinery
+// (tile bitmaps, mask tiles, per-element masking) is compiled out.
+template <int D, int HC, bool GEN, bool F8 = false, bool MASK = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   static_assert(!F8 || (D == 128 && GEN), "the fp8 body serves d = 128 with general masks");
   constexpr int RB = kWaves / HC;  // 32-row blocks per head in one workgroup
@@ -98,7 +100,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // dense-mask tiles (GEN with a mask): BM rows x 64 key bytes, row words
   // permuted so a lane's 8 words (the keys of its score registers) are two
   // 16-byte reads: word w of a row sits at position (w & 1) * 8 + (w >> 1)
-  constexpr int MASK_BYTES = GEN ? BM * kBN : 16;
+  constexpr int MASK_BYTES = GEN && MASK ? BM * kBN : 16;
   __shared__ __attribute__((aligned(16))) char sm0[MASK_BYTES];
   __shared__ __attribute__((aligned(16))) char sm1[MASK_BYTES];
 
@@ -241,7 +243,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // rows: one shared 32-bit lane offset, the row and key offsets in a scalar;
   // rows past S read as zero (their output is dropped) and keys past S_k
   // read whatever follows (they are invisible by the key prefix).
-  const bool has_mask = GEN && a.mask != nullptr;
+  constexpr bool has_mask = GEN && MASK;
   constexpr int MROWS_PER_WAVE = BM / kWaves;  // mask rows each wave loads per tile
   static_assert(!GEN || MROWS_PER_WAVE % 4 == 0, "mask rows split into 4-row instructions");
   const int mpos = lane & 15;
@@ -270,7 +272,87 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     return u32x4x2{lo, hi};
   };
 
-  if (n_tiles == 0) {  // no row of the workgroup sees a key: zero rows
+  // ---- with a dense mask: which key tiles any row of the workgroup can see.
+  // Bit j of s_vis is set when some mask byte of rows [blk0, row_end) over
+  // the keys of tile j is nonzero; the loop below visits only those tiles,
+  // so a tile hidden from the whole block (most tiles of a batch of packed
+  // documents) costs neither its K/V and mask loads nor a barrier.  Bit j of
+  // s_full is set when none of those bytes is zero: such a tile (the inside
+  // of a document) needs no mask tile and no per-element mask.  Bytes a row
+  // cannot see by the causal rule or the key length still count (a tile
+  // visited for nothing, or masked needlessly, gives the same result).
+  // Blocks with more tiles than the bitmaps hold visit every tile, masked.
+  constexpr int kVisWords = has_mask ? 256 : 1;  // up to 8192 key tiles
+  __shared__ uint32_t s_vis[kVisWords];
+  __shared__ uint32_t s_full[kVisWords];
+  const bool skip_tiles = has_mask && n_tiles <= kVisWords * 32;
+  int n_steps = n_tiles;  // key tiles the loop visits
+  if (skip_tiles) {
+    for (int i = tid; i < kVisWords; i += kWaves * 64) {
+      s_vis[i] = 0u;
+      s_full[i] = 0u;
+    }
+    __syncthreads();
+    const int nrows = min(BM, S - blk0);
+    constexpr int TPI = 4;  // tiles per wave and pass: their loads are in flight together
+    for (int j0 = wave; j0 < n_tiles; j0 += TPI * kWaves) {
+      uint32_t any[TPI], zero[TPI];
+#pragma unroll
+      for (int u = 0; u < TPI; ++u) {
+        any[u] = 0u;
+        zero[u] = 0u;
+      }
+      for (int r = lane; r < nrows; r += 64) {
+#pragma unroll
+        for (int u = 0; u < TPI; ++u) {
+          const unsigned off = (unsigned)(r * SK + (j0 + u * kWaves) * kBN);
+#pragma unroll
+          for (int i = 0; i < kBN / 16; ++i) {
+            const u32x4 mv = buffer_load_x4(mrsrc, off + 16 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              any[u] |= mv[e];
+              zero[u] |= (mv[e] - 0x01010101u) & ~mv[e] & 0x80808080u;  // nonzero iff a byte is 0
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TPI; ++u) {
+        const int j = j0 + u * kWaves;
+        const bool vis = __builtin_amdgcn_ballot_w64(any[u] != 0u) != 0;
+        const bool full = __builtin_amdgcn_ballot_w64(zero[u] != 0u) == 0;
+        if (j < n_tiles && lane == 0) {
+          if (vis) atomicOr(&s_vis[j >> 5], 1u << (j & 31));
+          if (full) atomicOr(&s_full[j >> 5], 1u << (j & 31));
+        }
+      }
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int i = lane; i < (n_tiles + 31) / 32; i += 64) cnt += __popc(s_vis[i]);
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) cnt += __shfl_xor(cnt, msk, 64);
+    n_steps = __builtin_amdgcn_readfirstlane(cnt);
+  }
+  // the key tile visited after tile j (n_tiles: none)
+  // after the first visited tile a row can still lack a visible key only
+  // under a dense mask, or with the causal rule and fewer keys than queries
+  const bool may_unset = GEN && (has_mask || (a.causal && SK < S));
+  // tile j needs the per-element mask
+  auto masked_tile = [&](int j) { return has_mask && !(skip_tiles && ((s_full[j >> 5] >> (j & 31)) & 1u)); };
+  auto next_tile_of = [&](int j) {
+    if (!skip_tiles) return j + 1;
+    int t = j + 1;
+    while (t < n_tiles) {
+      const uint32_t bits = s_vis[t >> 5] >> (t & 31);
+      if (bits != 0u) return __builtin_amdgcn_readfirstlane(t + (int)__builtin_ctz(bits));
+      t = (t | 31) + 1;
+    }
+    return n_tiles;
+  };
+
+  if (n_steps == 0) {  // no row of the workgroup sees a key: zero rows
     if (qrow < S) {
       uint16_t* op = a.out + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D;
 #pragma unroll
@@ -280,24 +362,28 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     }
     return;
   }
-  dma_tile(0, sk0, sv0);
-  if (has_mask) dma_mask(0, sm0);
+  const int j_first = next_tile_of(-1);
+  dma_tile(j_first, sk0, sv0);
+  if (masked_tile(j_first)) dma_mask(j_first, sm0);
   dma_wait();
   __syncthreads();
 
-  // one key tile: compute from (kt, vt) while the next tile fills (kn, vn)
-  auto tile_step = [&](int j, const char* kt, const char* vt, const char* mt, char* kn, char* vn, char* mn) {
-    // the other buffer was last read in iteration j-1, before its closing barrier
-    if (j + 1 < n_tiles) {
-      dma_tile(j + 1, kn, vn);
-      if (has_mask) dma_mask(j + 1, mn);
+  // step k visits key tile j: compute from (kt, vt) while the next visited
+  // tile fills (kn, vn); returns that next tile
+  auto tile_step = [&](int k, int j, const char* kt, const char* vt, const char* mt, char* kn, char* vn, char* mn) {
+    // the other buffer was last read in step k-1, before its closing barrier
+    const int jn = next_tile_of(j);
+    if (k + 1 < n_steps) {
+      dma_tile(jn, kn, vn);
+      if (masked_tile(jn)) dma_mask(jn, mn);
     }
+    const bool tmask = masked_tile(j);  // the mask tile of j is in mt
     const int key0 = j * kBN;
     // no row of this wave sees a key of the tile (by the key prefix, or by a
     // mask that hides the whole tile from all its rows): nothing to do but
     // keep in step
     bool work = key0 < wave_kend;
-    if (GEN && work && has_mask) {
+    if (GEN && work && tmask) {
       const u32x4x2 mw = mask_words(mt);
       const uint32_t any = mw.lo[0] | mw.lo[1] | mw.lo[2] | mw.lo[3] | mw.hi[0] | mw.hi[1] | mw.hi[2] | mw.hi[3];
       work = __builtin_amdgcn_ballot_w64(any != 0u && qrow < S) != 0;
@@ -362,7 +448,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
               sacc[kh][r] = key >= lane_kend ? kNegInf : sacc[kh][r];
             }
         }
-        if (GEN && has_mask) {
+        if (GEN && tmask) {
           const u32x4x2 mw = mask_words(mt);
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh)
@@ -401,12 +487,26 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       // scores, moves m to the running max (one exchange with lane ^ 32),
       // rescales O and l, and takes p again.
       float psum = 0.f;
-      bool slow = j == 0;
+      bool slow = k == 0;
       if (!slow) {
-        psum = probs(sacc, m);
+        // with general masks a row may have seen no visible key yet (m =
+        // -inf): it stays on the fast path (p = 0) while its scores in this
+        // tile are all hidden, and takes the slow path at its first visible one
+        bool unset = false;
+        if constexpr (GEN) {
+          if (may_unset && __builtin_amdgcn_ballot_w64(m == kNegInf) != 0) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
+            unset = m == kNegInf && mx != kNegInf;
+          }
+        }
+        psum = probs(sacc, GEN && m == kNegInf ? 0.f : m);
         // bound: bf16 P has range to spare; e4m3 P must stay below its 448
         // maximum, which psum <= 256 guarantees for every p of the tile
-        slow = __builtin_amdgcn_ballot_w64(!(psum <= (F8 ? 256.0f : 0x1p30f))) != 0;  // also catches inf / NaN
+        slow = __builtin_amdgcn_ballot_w64(unset || !(psum <= (F8 ? 256.0f : 0x1p30f))) != 0;  // also catches inf / NaN
         if (slow) scores(sacc);
       }
       if (slow) {
@@ -496,10 +596,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     }
     dma_wait();
     __syncthreads();
+    return jn;
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile_step(j, sk0, sv0, sm0, sk1, sv1, sm1);
-    if (j + 1 < n_tiles) tile_step(j + 1, sk1, sv1, sm1, sk0, sv0, sm0);
+  int j = j_first;
+  for (int k = 0; k < n_steps; k += 2) {
+    j = tile_step(k, j, sk0, sv0, sm0, sk1, sv1, sm1);
+    if (k + 1 < n_steps) j = tile_step(k + 1, j, sk1, sv1, sm1, sk0, sv0, sm0);
   }
 
   // ---- epilogue: O / l -> bf16, rows < S only
@@ -525,14 +627,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_causal_kernel(Pref
   prefill_body<D, HC, false>(a);
 }
 
-template <int D, int HC>
+template <int D, int HC, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_masked_kernel(PrefillArgs a) {
-  prefill_body<D, HC, true>(a);
+  prefill_body<D, HC, true, false, MASK>(a);
 }
 
-template <int HC>
+template <int HC, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_fp8_kernel(PrefillArgs a) {
-  prefill_body<128, HC, true, true>(a);
+  prefill_body<128, HC, true, true, MASK>(a);
 }
 
 static int gcd_int(int x, int y) {
@@ -603,7 +705,11 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
   a.kv_lens = kv_lens;
   a.mask = mask;
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
-#define GQA_LAUNCH_PREFILL(DD, HH) hipLaunchKernelGGL((gqa_prefill_masked_kernel<DD, HH>), grid, block, 0, stream, a)
+#define GQA_LAUNCH_PREFILL(DD, HH)                                                                       \
+  do {                                                                                                   \
+    if (mask) hipLaunchKernelGGL((gqa_prefill_masked_kernel<DD, HH, true>), grid, block, 0, stream, a);  \
+    else hipLaunchKernelGGL((gqa_prefill_masked_kernel<DD, HH, false>), grid, block, 0, stream, a);      \
+  } while (0)
   if (D == 128) {
     if (HC == 8) GQA_LAUNCH_PREFILL(128, 8);
     else if (HC == 4) GQA_LAUNCH_PREFILL(128, 4);
@@ -633,10 +739,16 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void*
   a.k_descale = k_descale;
   a.v_descale = v_descale;
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
-  if (HC == 8) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<8>), grid, block, 0, stream, a);
-  else if (HC == 4) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<4>), grid, block, 0, stream, a);
-  else if (HC == 2) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<2>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((gqa_prefill_fp8_kernel<1>), grid, block, 0, stream, a);
+#define GQA_LAUNCH_FP8(HH)                                                                              \
+  do {                                                                                                  \
+    if (mask) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<HH, true>), grid, block, 0, stream, a);        \
+    else hipLaunchKernelGGL((gqa_prefill_fp8_kernel<HH, false>), grid, block, 0, stream, a);            \
+  } while (0)
+  if (HC == 8) GQA_LAUNCH_FP8(8);
+  else if (HC == 4) GQA_LAUNCH_FP8(4);
+  else if (HC == 2) GQA_LAUNCH_FP8(2);
+  else GQA_LAUNCH_FP8(1);
+#undef GQA_LAUNCH_FP8
   return hipGetLastError();
 }
 
