@@ -17,9 +17,11 @@
 //    workgroup's LDS copy of the tile (three tiles resident: the one in use
 //    and the next two);
 //  * the scores S^T[token][head] of the tile are cut into 16-token x 16-head
-//    blocks over the full latent width, one block per wave, on
-//    v_mfma_f32_16x16x32_bf16; they go to LDS and, after one barrier, every
-//    wave reads the scores of all heads and runs the same online softmax;
+//    blocks on v_mfma_f32_16x16x32_bf16; with fewer blocks than waves (32
+//    heads give 4) each block's latent width is split over 8 / blocks waves.
+//    The (partial) blocks go to LDS and, after one barrier, every wave reads
+//    the scores of all heads, summing the partials, and runs the same online
+//    softmax;
 //  * the weighted sum O^T[latent][head] += C^T P^T runs on the wave's own
 //    latent slice (v_mfma_f32_32x32x16_bf16), so a wave's accumulator holds
 //    d_c / 8 latent values of every head and the partials need no merge
