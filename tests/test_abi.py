@@ -206,8 +206,10 @@ def test_int_caches_are_accepted_with_scales(lib, kt):
     """INT8 (3) and INT4 (4) caches take bf16 Q and per-row scales, like FP8."""
     desc = dd(kt=kt)
     assert lib.attn_decode_num_splits(ctypes.byref(desc)) > 0
-    assert lib.attn_decode_workspace_bytes(ctypes.byref(desc)) == \
-        lib.attn_decode_workspace_bytes(ctypes.byref(dd(kt=2)))
+    ws = lib.attn_decode_workspace_bytes(ctypes.byref(desc))
+    assert ws > 0
+    if kt == 3:  # int8 shares fp8's plan; int4 schedules 64-token tiles (fewer ranges on a short cache)
+        assert ws == lib.attn_decode_workspace_bytes(ctypes.byref(dd(kt=2)))
     assert call_decode(lib, desc, ks=None, vs=ALIGNED) == 1
     assert call_decode(lib, desc, ks=ALIGNED, vs=MISALIGNED) == 4
     assert call_decode(lib, dd(qt=0, kt=kt)) == 3

@@ -78,8 +78,10 @@ DecodePlan plan_decode(const gqa_decode_desc* d) {
     p.hb = 1;
     p.heads_per_chunk = 16;
   } else {
-    p.tile = kTileMfma;
     p.hb = G > 16 ? 2 : 1;
+    // int4 with one block of 16 heads schedules 64-token tiles (two register
+    // halves per wave in the split kernel); the combine must use the same
+    p.tile = p.kind == 4 && p.hb == 1 ? 2 * kTileMfma : kTileMfma;
     p.heads_per_chunk = 16 * p.hb;
   }
   p.n_hchunk = (G + p.heads_per_chunk - 1) / p.heads_per_chunk;

@@ -136,6 +136,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   constexpr int NT = D / 16;  // 16-wide d tiles of the PV product
   constexpr int TILE_BYTES = kTile * D * 2;
   constexpr int HPC = 16 * HB;
+  // int4 with one block of 16 heads: 64-token tiles in two register halves (see below)
+  constexpr bool SPLIT2 = KVF == kKvInt4 && HB == 1;
+  constexpr int NH = SPLIT2 ? 2 : 1;  // register halves
+  constexpr int TT = NH * kTile;      // tokens per scheduled tile
   // 32 heads of a bf16 cache: one 32x32 score tile per 32 tokens on
   // v_mfma_f32_32x32x16_bf16 (the same shape as the prefill kernel with heads
   // in place of query rows); otherwise HB blocks of 16 heads on 16x16x32.
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   const int spb = a.n_kv * a.n_hchunk;
 
   const LaneLens ll = load_lane_lens(a.seq_lens, a.B, a.S_max, lane);
-  const long long T = uniform(total_tiles_cached(ll, a.seq_lens, a.B, a.S_max, kTile, spb, lane));
+  const long long T = uniform(total_tiles_cached(ll, a.seq_lens, a.B, a.S_max, TT, spb, lane));
   const TileRanges rg(T, W);
   long long lo = rg.lo(w);
   const long long hi = rg.lo(w + 1);
@@ -184,8 +188,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   const int ld_row = lane / LPR;
   const int ld_chunk = lane % LPR;
 
-  u32x4 kreg[NLD], vreg[NLD];
-  float ksc[2][4], vsc[2][4];
+  // An int4 tile (32 tokens) is only 2 KiB of K and 2 KiB of V, so with one
+  // tile in flight per wave the loads cannot cover the memory latency.  With
+  // one block of 16 heads the int4 path therefore schedules 64-token tiles
+  // held as two 32-token halves in separate registers: while one half is
+  // staged and computed, the next tile's same half is already loading, so
+  // two halves are always in flight.  The LDS slab still holds 32 tokens.
+  u32x4 kreg[NH][NLD], vreg[NH][NLD];
+  float ksc[NH][2][4], vsc[NH][2][4];
 
   // loads of tile `tile` of segment s into kreg/vreg (and its K/V scales).
   // The tile's first row is wave-uniform: it becomes the base of a buffer
@@ -193,16 +203,18 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // the end read as zero without a memory access (a cache tail may hold NaN)
   // and each load needs only a 32-bit lane offset.
   const unsigned lane_off = ld_row * ROWB + ld_chunk * 16;
-  auto issue_loads = [&](Segment& s, int tile) {
-    const int tt0 = s.t_begin + tile * kTile;
+  // (a half past the segment's end gets an empty range: its loads return
+  // zeros without a memory access, so every path issues the same loads)
+  auto issue_loads = [&](Segment& s, int tile, int half = 0) {
+    const int tt0 = s.t_begin + tile * TT + half * kTile;
     const size_t row0 = (size_t)uniform((long long)cache_row<PAGED>(a, s, tt0, lane));
-    const int nvalid = uniform(min(kTile, s.t_end - tt0));
+    const int nvalid = uniform(max(min(kTile, s.t_end - tt0), 0));
     const auto rk = make_rsrc(static_cast<const char*>(a.k) + row0 * ROWB, nvalid * ROWB);
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + row0 * ROWB, nvalid * ROWB);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      kreg[u] = buffer_load_x4_nt(rk, lane_off + u * RPL * ROWB);
-      vreg[u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
+      kreg[half][u] = buffer_load_x4_nt(rk, lane_off + u * RPL * ROWB);
+      vreg[half][u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
     }
     if constexpr (QUANT) {
       // lane (q4, .) needs the scales of rows 16h + 4q4 + i; rows past the end
@@ -213,8 +225,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ksc[h][i] = buffer_load_f32(rks, 16 * q4 + 4 * (16 * h + i));
-          vsc[h][i] = buffer_load_f32(rvs, 16 * q4 + 4 * (16 * h + i));
+          ksc[half][h][i] = buffer_load_f32(rks, 16 * q4 + 4 * (16 * h + i));
+          vsc[half][h][i] = buffer_load_f32(rvs, 16 * q4 + 4 * (16 * h + i));
         }
     }
   };
@@ -255,14 +267,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // Stage the tile whose loads were issued last into the wave's LDS slab as
   // bf16 (quantized codes are converted exactly) and take over its scales.
   float kscur[2][4], vscur[2][4];
-  auto stage = [&]() {
+  auto stage = [&](int half = 0) {
     if constexpr (QUANT) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          kscur[h][i] = ksc[h][i];
-          vscur[h][i] = vsc[h][i];
+          kscur[h][i] = ksc[half][h][i];
+          vscur[h][i] = vsc[half][h][i];
         }
     }
     wave_lds_fence();
@@ -272,14 +284,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       if constexpr (KVF == kKvFp8) {
         // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
         const int c0 = 2 * ld_chunk;
-        u32x2 t0 = e4m3x4_to_bf16x4(kreg[u][0]), t1 = e4m3x4_to_bf16x4(kreg[u][1]);
-        u32x2 t2 = e4m3x4_to_bf16x4(kreg[u][2]), t3 = e4m3x4_to_bf16x4(kreg[u][3]);
+        u32x2 t0 = e4m3x4_to_bf16x4(kreg[half][u][0]), t1 = e4m3x4_to_bf16x4(kreg[half][u][1]);
+        u32x2 t2 = e4m3x4_to_bf16x4(kreg[half][u][2]), t3 = e4m3x4_to_bf16x4(kreg[half][u][3]);
         const u32x4 klo = u32x4{t0[0], t0[1], t1[0], t1[1]};
         const u32x4 khi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-        t0 = e4m3x4_to_bf16x4(vreg[u][0]);
-        t1 = e4m3x4_to_bf16x4(vreg[u][1]);
-        t2 = e4m3x4_to_bf16x4(vreg[u][2]);
-        t3 = e4m3x4_to_bf16x4(vreg[u][3]);
+        t0 = e4m3x4_to_bf16x4(vreg[half][u][0]);
+        t1 = e4m3x4_to_bf16x4(vreg[half][u][1]);
+        t2 = e4m3x4_to_bf16x4(vreg[half][u][2]);
+        t3 = e4m3x4_to_bf16x4(vreg[half][u][3]);
         const u32x4 vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
         const u32x4 vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
         const int sw = swz<CH>(r);
@@ -293,8 +305,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         const int sw = swz<CH>(r);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const u32x2 k0 = i8x4_to_bf16x4(kreg[u][2 * h]), k1 = i8x4_to_bf16x4(kreg[u][2 * h + 1]);
-          const u32x2 v0 = i8x4_to_bf16x4(vreg[u][2 * h]), v1 = i8x4_to_bf16x4(vreg[u][2 * h + 1]);
+          const u32x2 k0 = i8x4_to_bf16x4(kreg[half][u][2 * h]), k1 = i8x4_to_bf16x4(kreg[half][u][2 * h + 1]);
+          const u32x2 v0 = i8x4_to_bf16x4(vreg[half][u][2 * h]), v1 = i8x4_to_bf16x4(vreg[half][u][2 * h + 1]);
           lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{k0[0], k0[1], k1[0], k1[1]});
           lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{v0[0], v0[1], v1[0], v1[1]});
         }
@@ -304,27 +316,30 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         const int sw = swz<CH>(r);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[u][h]));
-          lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(vreg[u][h]));
+          lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[half][u][h]));
+          lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(vreg[half][u][h]));
         }
       } else {
         const int pc = ld_chunk ^ swz<CH>(r);
-        lds_store(kt + r * (2 * D) + (pc << 4), kreg[u]);
-        lds_store(vt + r * (2 * D) + (pc << 4), vreg[u]);
+        lds_store(kt + r * (2 * D) + (pc << 4), kreg[half][u]);
+        lds_store(vt + r * (2 * D) + (pc << 4), vreg[half][u]);
       }
     }
     wave_lds_fence();
   };
 
-  Segment cur = make_segment<kTile, PAGED>(a, ll, lo, hi, w, spb, HPC, lane);
+  Segment cur = make_segment<TT, PAGED>(a, ll, lo, hi, w, spb, HPC, lane);
   QRows qc = load_q(cur);
   wave_lds_fence();  // the first tile's loads go out after the query rows'
-  if (wave < cur.ntile) issue_loads(cur, wave);
+  if (wave < cur.ntile) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) issue_loads(cur, wave, h);
+  }
 
   for (;;) {
     const bool has_next = lo + cur.ntile < hi;
     Segment nxt = cur;
-    if (has_next) nxt = make_segment<kTile, PAGED>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
+    if (has_next) nxt = make_segment<TT, PAGED>(a, ll, lo + cur.ntile, hi, w, spb, HPC, lane);
     const int t_begin = cur.t_begin, t_end = cur.t_end;
 
     // ---- prologue: wave i takes tiles i and i + NW.  It stages the first and
@@ -332,13 +347,18 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     // the workgroup waits for the segment's query rows, so that no wave's
     // second load waits for the slowest wave's first: at kernel start every
     // wave's first load is queued behind the whole chip's first burst.
+    // half h of tile idx of this segment, or else of the wave's first tile of the next
+    auto issue_next = [&](int idx, int h) {
+      if (idx < cur.ntile) issue_loads(cur, idx, h);
+      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave, h);
+    };
     int tile = wave, next_tile = wave + NW;
     if (tile < cur.ntile) {
-      stage();
-      if (next_tile < cur.ntile) issue_loads(cur, next_tile);
-      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
+      stage(0);
+      issue_next(next_tile, 0);
     } else if (has_next && wave < nxt.ntile) {
-      issue_loads(nxt, wave);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) issue_loads(nxt, wave, h);
     }
     QRows q_next = {};
     if (has_next) q_next = load_q(nxt);  // used at the segment switch, long after it lands
@@ -369,8 +389,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 
     // ---- compute the staged tile, then stage the one in flight and put the
     // wave's next tile (of this segment, else its first of the next) in flight
+    // Split int4 tiles: while half 0 of `tile` is computed, its half 1 and
+    // half 0 of next_tile are in flight; half 1 is staged (and next_tile's
+    // half 1 issued) before it is computed, in the next pass of the loop.
+    int half = 0;  // the staged half of `tile`
     while (tile < cur.ntile) {
-      const int tt0 = t_begin + tile * kTile;
+      const int tt0 = t_begin + tile * TT + (SPLIT2 ? half * kTile : 0);
       if constexpr (M32) {
         const int l32 = lane & 31, h2 = lane >> 5;
         // ---- S^T[32 tokens][32 heads] = K Q^T: lane holds tokens 8(r/4)+4h2+r%4 of head l32
@@ -521,12 +545,20 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
         }
       }
+      if constexpr (SPLIT2) {
+        if (half == 0) {
+          stage(1);
+          issue_next(next_tile, 1);
+          half = 1;
+          if (tt0 + kTile < t_end) continue;  // half 1 holds tokens: compute it next
+        }
+        half = 0;
+      }
       tile = next_tile;
       if (tile >= cur.ntile) break;
-      stage();
+      stage(0);
       next_tile = claim_tile();
-      if (next_tile < cur.ntile) issue_loads(cur, next_tile);
-      else if (has_next && wave < nxt.ntile) issue_loads(nxt, wave);
+      issue_next(next_tile, 0);
     }
 
     // ---- merge the waves of the workgroup, write one partial per head
