@@ -528,8 +528,9 @@ def _workload_launches():
         lens = inputs.draw_lengths(wl.B, *wl.kv_lens, wl.seed) if wl.kv_lens else None
         mask = inputs.draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, wl.seed, wl.doc_lens) if wl.mask else None
         pairs = roofline.visible_pairs(wl.B, wl.S_q, wl.S_k, wl.causal, lens, mask)
-        kname, targs = (("gqa_prefill_fp8_kernel", (str(hc),)) if wl.dtype == "fp8"
-                        else ("gqa_prefill_masked_kernel", (str(wl.d_h), str(hc))))
+        has_mask = "true" if wl.mask else "false"  # dense-mask instantiation of the kernel
+        kname, targs = (("gqa_prefill_fp8_kernel", (str(hc), has_mask)) if wl.dtype == "fp8"
+                        else ("gqa_prefill_masked_kernel", (str(wl.d_h), str(hc), has_mask)))
         out.append(((kname, targs, grid),
                     (f"prefill_masked:{wl.name}", wl.name, roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs),
                      "flops")))
