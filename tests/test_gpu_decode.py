@@ -94,6 +94,18 @@ def test_forced_splits_agree(n_split, kd):
     check_full(inp, n_split=n_split)
 
 
+@pytest.mark.parametrize("n_split", [0, 3, 10 ** 6])
+def test_int4_tile_halves(n_split):
+    """int4 with one block of 16 heads schedules 64-token tiles held as two
+    32-token register halves: lengths on both sides of every half boundary
+    (the second half empty, partly or wholly filled), with the key ranges
+    cut at the library's count, at 3, and at every tile."""
+    lens = [31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129]
+    w = wl("int4-halves", B=len(lens), h_q=16, n_kv=2, d=128, S=160, qd="bf16", kd="int4", seed=49)
+    inp = inputs.make_decode_inputs(w, device=DEV, seq_lens=lens, poison_tail=True)
+    check_full(inp, n_split=n_split)
+
+
 @pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_empty_and_overlong_lengths(kd):
     qd = "f32" if kd == "f32" else "bf16"
