@@ -106,6 +106,15 @@ def test_int4_tile_halves(n_split):
     check_full(inp, n_split=n_split)
 
 
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int4"])
+def test_more_than_64_sequences(kd):
+    """B > 64: the split and combine kernels find the slabs by scanning the
+    lengths 64 at a time instead of one lane per sequence."""
+    qd = "f32" if kd == "f32" else "bf16"
+    w = wl("wide", B=70, h_q=16, n_kv=2, d=64, S=160, qd=qd, kd=kd, lens=(0, 160), seed=51)
+    check_full(inputs.make_decode_inputs(w, device=DEV, poison_tail=True))
+
+
 @pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
 def test_empty_and_overlong_lengths(kd):
     qd = "f32" if kd == "f32" else "bf16"
