@@ -100,7 +100,8 @@ typedef enum gqa_status {
  * multiplies the score and the V scale the softmax weight.  Accumulation is
  * float32 throughout.
  *
- * Sequence split: the 32-token tiles (64 on the F32 path) of every
+ * Sequence split: the 32-token tiles (64 on the F32 path, and on the INT4
+ * path when a K/V head serves at most 16 query heads) of every
  * (sequence, kv-head) are concatenated and cut into n_split equal ranges, one
  * per workgroup, so ragged lengths are balanced across the GPU.  Each range
  * leaves an unnormalised partial (O_s, m_s, l_s) per head for every

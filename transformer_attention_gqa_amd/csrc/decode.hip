@@ -11,12 +11,13 @@
 // built around reading every K/V byte exactly once, evenly over the chip:
 //
 //  * the launch is one wide workgroup per compute unit (persistent); the
-//    32-token tiles of all (sequence, kv-head) slabs are concatenated and cut
+//    32-token tiles (64 for int4 with one block of 16 heads, held as two
+//    halves) of all (sequence, kv-head) slabs are concatenated and cut
 //    into equal ranges, one per workgroup, so ragged sequence lengths cost no
 //    load imbalance and no tail of lone workgroups (schedule: gqa_launch.h);
 //  * a workgroup serves every query head of the slab's group (up to 32) from a
 //    single read of each K/V tile;
-//  * its wavefronts take interleaved tiles; each tile arrives through 128-bit
+//  * its wavefronts take tiles as they become free; each tile arrives through 128-bit
 //    non-temporal loads (16 lanes cover one contiguous 256-byte cache row), is
 //    written once to the wave's private LDS slab with an XOR chunk swizzle,
 //    and is consumed from there by the matrix cores while the next tile is
