@@ -252,7 +252,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   const int blk0 = qb * BM;
   const __amdgpu_buffer_rsrc_t mrsrc =
       make_rsrc(has_mask ? a.mask + ((size_t)b * S + blk0) * SK : static_cast<const uint8_t*>(nullptr),
-                has_mask ? min(BM, S - blk0) * SK : 0);
+                // up to 256 rows x 2^23 keys = 2^31 bytes: formed unsigned
+                has_mask ? (int)((unsigned)min(BM, S - blk0) * (unsigned)SK) : 0);
   auto dma_mask = [&](int j, char* mdst) {
     if constexpr (GEN) {
       const int key0 = j * kBN;
@@ -305,7 +306,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       for (int r = lane; r < nrows; r += 64) {
 #pragma unroll
         for (int u = 0; u < TPI; ++u) {
-          const unsigned off = (unsigned)(r * SK + (j0 + u * kWaves) * kBN);
+          const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((j0 + u * kWaves) * kBN);
 #pragma unroll
           for (int i = 0; i < kBN / 16; ++i) {
             const u32x4 mv = buffer_load_x4(mrsrc, off + 16 * i);
