@@ -479,7 +479,7 @@ def _workload_launches():
             targs = (str(wl.d_h), str(hpc // 16), kvf[wl.kv_dtype], "8", "false")
             out.append((("gqa_decode_split_mfma", targs, ns * 512), (key, wl.name, kv, "bytes")))
         n_slabs = wl.B * wl.n_kv * -(-G // hpc)
-        grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
+        grid = n_slabs * -(-(min(hpc, G) * wl.d_h // 4) // 256) * 256
         targs = (str(wl.d_h), "false" if wl.q_dtype == "f32" else "true")
         out.append((("gqa_decode_combine", targs, grid), (f"decode_combine:{wl.name}", wl.name, None, None)))
     for pwl in inputs.PAGED_WORKLOADS.values():
@@ -495,7 +495,7 @@ def _workload_launches():
         out.append((("gqa_decode_split_mfma", targs, ns * 512),
                     (f"decode_split_paged_{wl.kv_dtype}:{pwl.name}", pwl.name, kv, "bytes")))
         n_slabs = wl.B * wl.n_kv * -(-G // hpc)
-        grid = n_slabs * -(-(hpc * wl.d_h // 4) // 256) * 256
+        grid = n_slabs * -(-(min(hpc, G) * wl.d_h // 4) // 256) * 256
         out.append((("gqa_decode_combine", (str(wl.d_h), "true"), grid),
                     (f"decode_combine:{pwl.name}", pwl.name, None, None)))
     for wl in inputs.MLA_WORKLOADS.values():

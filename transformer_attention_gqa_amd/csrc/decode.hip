@@ -959,7 +959,9 @@ hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int
 }
 
 hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream) {
-  const dim3 grid(c.B * c.n_kv * c.n_hchunk, (c.heads_per_chunk * D / 4 + 255) / 256);
+  // a chunk holds at most G heads: no workgroups for the chunk's unused head rows
+  const int heads = min(c.heads_per_chunk, c.h_q / c.n_kv);
+  const dim3 grid(c.B * c.n_kv * c.n_hchunk, (heads * D / 4 + 255) / 256);
   const dim3 block(256);
   switch (D) {
     case 64:
