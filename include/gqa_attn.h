@@ -34,6 +34,8 @@
  *  - Supported head dimensions: d_h = 64 or 128.
  *  - `scale` multiplies q . k before the softmax (the modules use
  *    head_dim ** -0.5); it must be finite and > 0 (GQA_ERR_VALUE otherwise).
+ *    A scale whose product with log2(e) is below the smallest normal float
+ *    is raised to it (the scores are then zero to float precision).
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -70,8 +72,18 @@ typedef enum gqa_status {
   GQA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
   GQA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
   GQA_ERR_HIP = 6,       /* a HIP launch or query failed                      */
-  GQA_ERR_VALUE = 7      /* scale is not a finite number > 0                  */
+  GQA_ERR_VALUE = 7      /* scale is not a finite number > 0, or a flags
+                            word holds unknown bits                           */
 } gqa_status;
+
+/* Decode flags (gqa_decode_desc.flags, gqa_paged_desc.flags). */
+enum {
+  /* Fixed tile order inside each workgroup, so that identical calls give
+   * bitwise-identical outputs on every path (see "Sequence split" below).
+   * Costs a few percent of decode time; without it the waves of a
+   * workgroup take tiles as they free up. */
+  GQA_DECODE_DETERMINISTIC = 1
+};
 
 /* ---------------------------------------------------------------- decode --
  * One autoregressive step over a KV cache.  The new token's K/V has already
@@ -107,28 +119,35 @@ typedef enum gqa_status {
  * leaves an unnormalised partial (O_s, m_s, l_s) per head for every
  * (sequence, kv-head) it touches, and a combine kernel merges them:
  *   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
- * On the matrix-core paths the waves of a workgroup take the tiles of its
- * range as they become free, so the float32 summation order and the point at
- * which each wave rounds its softmax weights to bf16 can change between two
- * identical calls: results agree to about 1e-3, not bit for bit.  The float32
- * path has a fixed order and is bitwise reproducible.
+ * By default, on the matrix-core paths the waves of a workgroup take the
+ * tiles of its range as they become free, so the float32 summation order and
+ * the point at which each wave rounds its softmax weights to bf16 can change
+ * between two identical calls: results agree to about 1e-3, not bit for bit.
+ * With GQA_DECODE_DETERMINISTIC in `flags` wave i of a workgroup takes tiles
+ * i, i + 8, i + 16, ... of each segment, and identical calls (same
+ * descriptor, same device) give identical bits.  The float32 path always has
+ * a fixed order.
  */
 typedef struct gqa_decode_desc {
   int32_t B, h_q, n_kv, S_max, d_h;
-  int32_t q_dtype, kv_dtype; /* GQA_F32 / GQA_BF16 / GQA_FP8_E4M3           */
-  int32_t n_split;           /* 0: one workgroup per compute unit of an MI355X
-                                (256).  > 0: number of workgroups / key ranges,
+  int32_t q_dtype, kv_dtype; /* GQA_F32 / GQA_BF16 / GQA_FP8_E4M3 / ...     */
+  int32_t n_split;           /* 0: one workgroup per compute unit of the
+                                current device (queried once per device;
+                                256 if no device can be queried).  > 0:
+                                number of workgroups / key ranges.  Either is
                                 capped at the number of tiles of a full cache
                                 and at 65536 (the effective count is
                                 attn_decode_num_splits()).                    */
+  int32_t flags;             /* 0 or GQA_DECODE_DETERMINISTIC                 */
 } gqa_decode_desc;
 
 /* Effective number of key ranges (= decode workgroups) for this descriptor,
- * or -1 if the descriptor is invalid.  Host-only, deterministic. */
+ * or -1 if the descriptor is invalid.  Host-only (with n_split = 0 it reads
+ * the current device's compute-unit count, enqueuing nothing). */
 int32_t attn_decode_num_splits(const gqa_decode_desc* d);
 
 /* Bytes of device workspace attn_decode needs for this descriptor (0 if the
- * descriptor is invalid).  Host-only, deterministic. */
+ * descriptor is invalid).  Host-only, as attn_decode_num_splits. */
 size_t attn_decode_workspace_bytes(const gqa_decode_desc* d);
 
 /* Full decode step: split kernel then combine kernel, both on `stream`.
@@ -186,6 +205,7 @@ typedef struct gqa_paged_desc {
   int32_t num_pages;         /* pages in the pool                          */
   int32_t max_pages_per_seq; /* columns of block_table                     */
   int32_t n_split;           /* as in gqa_decode_desc                      */
+  int32_t flags;             /* as in gqa_decode_desc                      */
 } gqa_paged_desc;
 
 int32_t attn_decode_paged_num_splits(const gqa_paged_desc* d);

@@ -34,8 +34,8 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
-def dd(B=2, h_q=8, n_kv=2, S=64, d=128, qt=1, kt=1, ns=0):
-    return binding.gqa_decode_desc(B, h_q, n_kv, S, d, qt, kt, ns)
+def dd(B=2, h_q=8, n_kv=2, S=64, d=128, qt=1, kt=1, ns=0, flags=0):
+    return binding.gqa_decode_desc(B, h_q, n_kv, S, d, qt, kt, ns, flags)
 
 
 def call_decode(lib, desc, q=ALIGNED, k=ALIGNED, v=ALIGNED, ks=None, vs=None, lens=ALIGNED, out=ALIGNED,
@@ -87,7 +87,9 @@ def test_split_plan_is_deterministic_and_honours_requests(lib):
     base = dd(B=16, h_q=64, n_kv=8, S=4096)
     a = lib.attn_decode_workspace_bytes(ctypes.byref(base))
     assert a == lib.attn_decode_workspace_bytes(ctypes.byref(base))
-    assert lib.attn_decode_num_splits(ctypes.byref(base)) == 256  # one workgroup per MI355X compute unit
+    # one workgroup per compute unit of the current device; with no device to
+    # query (this host), the 256 of a whole MI355X
+    assert lib.attn_decode_num_splits(ctypes.byref(base)) == 256
     n_slabs = 16 * 8  # G = 8 <= 16: one head chunk per K/V head
     max_tiles = n_slabs * (4096 // 32)
     for req in (1, 2, 7, 128, 100000):
@@ -303,3 +305,25 @@ def test_prefill_pointer_mask_and_value_errors(lib):
     assert call_prefill(lib, ad(S_k=66), mask=ALIGNED) == 2   # mask rows are read 4 keys at a time
     assert call_prefill(lib, ad(), qd=ALIGNED) == 3            # descale factors only with fp8 operands
     assert call_prefill(lib, ad(), scale=-1.0) == 7
+
+
+@pytest.mark.parametrize("flags", [2, 4, -1, 1 << 30])
+def test_unknown_decode_flags_are_rejected(lib, flags):
+    desc = dd(flags=flags)
+    assert call_decode(lib, desc) == 7
+    assert lib.attn_decode_num_splits(ctypes.byref(desc)) == -1
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(desc)) == 0
+    pdesc = binding.gqa_paged_desc(2, 8, 2, 128, 1, 1, 64, 10, 4, 0, flags)
+    assert lib.attn_decode_paged_num_splits(ctypes.byref(pdesc)) == -1
+
+
+def test_deterministic_flag_keeps_the_plan(lib):
+    """The deterministic mode changes only the order inside a workgroup: the
+    split count and the workspace are those of the default mode, and the
+    call passes validation (then fails on the first missing pointer)."""
+    a, b = dd(B=16, h_q=64, n_kv=8, S=4096), dd(B=16, h_q=64, n_kv=8, S=4096, flags=binding.GQA_DECODE_DETERMINISTIC)
+    assert lib.attn_decode_num_splits(ctypes.byref(a)) == lib.attn_decode_num_splits(ctypes.byref(b))
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(a)) == lib.attn_decode_workspace_bytes(ctypes.byref(b))
+    assert call_decode(lib, b, q=None) == 1
+    assert lib.gqa_last_hip_error().decode() == ""
+

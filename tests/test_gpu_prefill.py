@@ -126,16 +126,25 @@ def test_prefill_decode_consistency():
         assert diff <= 2 * TOL, (L, diff)
 
 
-def test_full_size_workload_sampled():
+def test_full_size_workload_every_block():
+    """c4 at full size in the benchmark's launch: one random (head, row) in
+    every workgroup block (2,048 blocks of 4 heads x 64 rows), every row of
+    one whole (sequence, head) plane, and the first and last rows of every
+    head, against the oracle row by row."""
     w = inputs.GQA_PREFILL_BF16
     inp = inputs.make_prefill_inputs(w, device=DEV)
     print(f"[prefill-full] {w}", flush=True)
     out = run(inp)
     pu.sync()
-    trip = pu.sample_rows(w.B, w.S, w.h_q, 40, seed=4)
+    trip = pu.prefill_block_samples(w.B, w.S, w.h_q, w.n_kv, seed=4)
+    trip += [(w.B - 1, r, 13) for r in range(w.S)]
+    trip += [(b, r, j) for b in range(w.B) for j in range(w.h_q) for r in (0, w.S - 1)]
+    print(f"[prefill-full] {len(trip)} rows", flush=True)
     q, k, v = pu.prefill_f64(inp)
     ref = oracle.prefill_rows(q, k, v, w.scale, trip)
-    got = torch.stack([out[b, r, j] for b, r, j in trip])
+    idx = torch.tensor(trip, device=DEV)
+    got = out[idx[:, 0], idx[:, 1], idx[:, 2]]
     err = pu.max_err(got, ref)
+    print(f"[prefill-full] max abs err {err:.3e}", flush=True)
     assert err <= TOL, f"max abs err {err}"
     assert torch.isfinite(out.float()).all()

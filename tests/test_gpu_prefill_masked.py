@@ -35,9 +35,10 @@ def _lens_mask(inp):
 
 
 def compare(inp, out, triples=None):
-    """bf16: max-abs error <= 2e-2 against the oracle.  fp8: every element
-    within the arithmetic's bound (parity_utils.fp8_prefill_bound) and the
-    relative RMS error below 0.1 (a wrong key or head mapping gives ~1)."""
+    """bf16: max-abs error <= 2e-2 against the oracle.  fp8: max-abs error
+    <= 5e-2 (the fp8 bar) element by element against the oracle on the
+    dequantised values, and relative RMS error <= 0.03 over all compared
+    elements (a wrong key or head mapping gives ~1)."""
     w = inp.wl
     q, k, v = pu.masked_prefill_values(inp)
     lens, mask = _lens_mask(inp)
@@ -45,23 +46,16 @@ def compare(inp, out, triples=None):
         ref = oracle.prefill(q, k, v, w.scale, causal=w.causal, kv_lens=lens, mask=mask)
         got = out
     else:
-        ref = omasked.prefill_rows(q, k, v, w.scale, triples, causal=w.causal, kv_lens=lens, mask=mask)
-        got = torch.stack([out[b, r, j] for b, r, j in triples])
+        ref = pu.masked_rows(q, k, v, w.scale, triples, w.causal, lens, mask)
+        idx = torch.tensor(triples, device=out.device)
+        got = out[idx[:, 0], idx[:, 1], idx[:, 2]]
     if w.dtype != "fp8":
         err = pu.max_err(got, ref)
+        print(f"[prefill_masked] max abs err {err:.3e}", flush=True)
         assert err <= TOL, f"max abs err {err}"
         return
-    g = got.detach().float().cpu().double().numpy()
-    assert np.all(np.isfinite(g)), "non-finite GPU output"
-    if triples is None:
-        triples = [(b, r, j) for b in range(w.B) for r in range(w.S_q) for j in range(w.h_q)]
-        g = g.reshape(-1, w.d_h)
-        ref = ref.reshape(-1, w.d_h)
-    bound = pu.fp8_prefill_bound(q, k, v, w.scale, triples, w.causal, lens, mask)
-    excess = np.abs(g - ref) - bound
-    assert np.all(excess <= 0), f"fp8 bound exceeded by {excess.max()} at row {triples[int(np.argmax(excess.max(1)))]}"
-    rel = np.sqrt(np.mean((g - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30)
-    assert rel <= 0.1, f"relative rms error {rel}"
+    err, rel = pu.check_fp8_prefill(got, ref)
+    print(f"[prefill_masked] fp8 max abs err {err:.3e}, relative rms {rel:.3e}", flush=True)
 
 
 def check(inp):
@@ -150,15 +144,40 @@ def test_documents_with_full_tiles(causal):
 
 
 @pytest.mark.parametrize("name", sorted(inputs.MASKED_PREFILL_WORKLOADS))
-def test_full_size_sampled(name):
-    """The benchmarked workloads in their launch configuration, on sampled
-    rows (first and last rows, rows at document and padding edges, random)."""
+def test_full_size_every_block(name):
+    """The benchmarked workloads in their launch configuration: one random
+    (head, row) in every workgroup block, plus the first and last rows of
+    every head, against the oracle row by row."""
     w = inputs.MASKED_PREFILL_WORKLOADS[name]
     inp = inputs.make_masked_prefill_inputs(w, device=DEV)
     print(f"[prefill_masked] full size {w}", flush=True)
     out = run(inp)
     pu.sync()
-    compare(inp, out, pu.sample_rows(w.B, w.S_q, w.h_q, 48, seed=460))
+    trip = pu.prefill_block_samples(w.B, w.S_q, w.h_q, w.n_kv, seed=460)
+    trip += [(b, r, j) for b in range(w.B) for j in range(w.h_q) for r in (0, w.S_q - 1)]
+    compare(inp, out, trip)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v"])
+def test_fp8_zero_descale(which):
+    """An all-zero head quantised by absmax has descale 0.  A zero Q or K
+    descale makes every visible score 0 (equal weights: the mean of the
+    visible V rows); a zero V descale makes the output 0.  Hidden keys must
+    stay hidden (no NaN from 0 * -inf)."""
+    w = wl(2, 150, 150, 8, 2, 128, True, seed=490, dtype="fp8")
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=[150, 97], poison_padding=True)
+    if which == "q":
+        inp.q[1, :, 5] = 0
+        inp.q_descale[1, 5] = 0.0
+    elif which == "k":
+        inp.k[0, :, 1] = 0
+        inp.k_descale[0, 1] = 0.0
+    else:
+        inp.v[1, :, 0] = 0
+        inp.v_descale[1, 0] = 0.0
+    out = check(inp)
+    if which == "v":
+        assert torch.count_nonzero(out[1, :, 0:4]) == 0
 
 
 @pytest.mark.parametrize("h_q,n_kv", [(8, 8), (8, 4), (8, 2), (16, 2), (6, 2)])

@@ -209,25 +209,26 @@ def test_row_helpers_match_full_forms():
 
 # ------------------------------------------------- spectrum and head repetition
 
-def _repeat_kv_pages(x, n_rep):
-    """The GQA module's K/V repetition: insert an axis after the K/V-head axis,
-    expand it n_rep times, fold it into the head axis.  x: [B, g, S, d]."""
-    B, g, S, d = x.shape
-    return x[:, :, None, :, :].expand(B, g, n_rep, S, d).reshape(B, g * n_rep, S, d)
+def _repeat_kv_heads(x, n_rep, axis):
+    """Each K/V head repeated n_rep times in place along `axis`, so head j of
+    the result is K/V head j // n_rep: the contiguous query groups of GQA
+    ("GQA Implementation" in "Evolution of AI Attention Mechanisms"), giving
+    an MHA problem with one K/V head per query head."""
+    return np.repeat(x, n_rep, axis=axis)
 
 
 @pytest.mark.parametrize("h_q,n_kv", [(8, 8), (8, 4), (8, 2), (8, 1)])
 def test_gqa_equals_mha_on_repeated_kv(h_q, n_kv):
     B, S, d = 2, 10, 8
     q, k, v = _rand(B, h_q, d), _rand(B, n_kv, S, d), _rand(B, n_kv, S, d)
-    kr = _repeat_kv_pages(torch.from_numpy(k), h_q // n_kv).numpy()
-    vr = _repeat_kv_pages(torch.from_numpy(v), h_q // n_kv).numpy()
+    kr = _repeat_kv_heads(k, h_q // n_kv, axis=1)
+    vr = _repeat_kv_heads(v, h_q // n_kv, axis=1)
     lens = [10, 7]
     np.testing.assert_allclose(oracle.decode(q, k, v, lens, 0.3), oracle.decode(q, kr, vr, lens, 0.3),
                                rtol=0, atol=1e-15)
     qp, kp, vp = _rand(B, S, h_q, d), _rand(B, S, n_kv, d), _rand(B, S, n_kv, d)
-    kpr = _repeat_kv_pages(torch.from_numpy(kp).transpose(1, 2), h_q // n_kv).transpose(1, 2).numpy()
-    vpr = _repeat_kv_pages(torch.from_numpy(vp).transpose(1, 2), h_q // n_kv).transpose(1, 2).numpy()
+    kpr = _repeat_kv_heads(kp, h_q // n_kv, axis=2)
+    vpr = _repeat_kv_heads(vp, h_q // n_kv, axis=2)
     np.testing.assert_allclose(oracle.prefill_causal(qp, kp, vp, 0.3), oracle.prefill_causal(qp, kpr, vpr, 0.3),
                                rtol=0, atol=1e-15)
 

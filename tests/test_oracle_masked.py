@@ -45,18 +45,26 @@ def test_visible_keys_hand_built():
 
 
 def _module_attention(q, k, v, scale, attention_mask):
-    """The pages' MHA/GQA module written in torch float64: K/V heads repeated
-    (expand + reshape), scores * scale, masked_fill(mask == 0, -inf), softmax,
-    times V.  q [B,S_q,h,d], k/v [B,S_k,n_kv,d] -> [B,S_q,h,d]."""
-    tq, tk, tv = (torch.from_numpy(x).transpose(1, 2) for x in (q, k, v))
-    B, n_kv, S_k, d = tk.shape
-    G = tq.shape[1] // n_kv
-    tk = tk[:, :, None].expand(B, n_kv, G, S_k, d).reshape(B, n_kv * G, S_k, d)
-    tv = tv[:, :, None].expand(B, n_kv, G, S_k, d).reshape(B, n_kv * G, S_k, d)
-    w = torch.matmul(tq, tk.transpose(-2, -1)) * scale
-    w = w.masked_fill(attention_mask[:, None] == 0, float("-inf"))
-    w = torch.softmax(w, dim=-1)
-    return torch.matmul(w, tv).transpose(1, 2).numpy()
+    """Masked grouped-query attention written from the definition, in torch
+    float64 on the CPU: query head j reads K/V head j // G (contiguous groups,
+    the head order of "GQA Implementation" in "Evolution of AI Attention
+    Mechanisms"); for every (batch, head) the scores are scale * Q K^T, a key
+    the mask hides scores -inf, each row is soft-maxed and multiplies V.
+    q [B,S_q,h,d], k/v [B,S_k,n_kv,d], attention_mask [B,S_q,S_k] bool ->
+    [B,S_q,h,d]."""
+    B, S_q, h, d = q.shape
+    G = h // k.shape[2]
+    kv_head = np.arange(h) // G
+    out = np.zeros_like(q)
+    for b in range(B):
+        hidden = ~attention_mask[b].numpy()
+        for j in range(h):
+            kk = torch.from_numpy(k[b, :, kv_head[j], :])
+            vv = torch.from_numpy(v[b, :, kv_head[j], :])
+            s = (torch.from_numpy(q[b, :, j, :]) @ kk.T) * scale
+            s[torch.from_numpy(hidden)] = float("-inf")
+            out[b, :, j, :] = (torch.softmax(s, dim=-1) @ vv).numpy()
+    return out
 
 
 CASES = [
@@ -172,3 +180,21 @@ def test_fp8_per_head_dequantisation():
         oracle.dequantize_fp8_heads(codes, np.array([[0.5]]))
     with pytest.raises(ValueError):
         oracle.dequantize_fp8_heads(codes, np.ones((1, 2), dtype=np.float32))
+
+
+def test_zero_descale_head_gives_the_mean_of_visible_values():
+    """An all-zero head quantised by absmax has descale 0: its values decode
+    to exactly 0, so every visible score of a zero query head is 0 and the
+    softmax weights are equal -- each output row is the mean of the V rows it
+    sees (closed form), never NaN."""
+    rng = np.random.default_rng(11)
+    B, S, h, n_kv, d = 1, 6, 2, 1, 8
+    codes = rng.integers(0, 0x7F, size=(B, S, h, d), dtype=np.uint8)   # finite codes only
+    qv = oracle.dequantize_fp8_heads(codes, np.array([[0.0, 0.25]], dtype=np.float32))
+    assert np.all(qv[:, :, 0] == 0.0)
+    k, v = _rand(B, S, n_kv, d, seed=5), _rand(B, S, n_kv, d, seed=6)
+    out = oracle.prefill(qv, k, v, 0.3, causal=True, kv_lens=[5])
+    for r in range(S):
+        n = min(r + 1, 5)
+        np.testing.assert_allclose(out[0, r, 0], v[0, :n, 0].mean(axis=0), rtol=0, atol=1e-15)
+    assert np.all(np.isfinite(out))

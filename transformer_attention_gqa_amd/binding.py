@@ -18,6 +18,7 @@ LIB_NAME = "libgqa_attn.so"
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_INT8, GQA_INT4 = 0, 1, 2, 3, 4
+GQA_DECODE_DETERMINISTIC = 1
 QUANTIZED_KV = (GQA_FP8_E4M3, GQA_INT8, GQA_INT4)
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE", 4: "GQA_ERR_ALIGN",
           5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE"}
@@ -36,13 +37,14 @@ class GqaError(RuntimeError):
 class gqa_decode_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
                 ("S_max", ctypes.c_int32), ("d_h", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class gqa_paged_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("h_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("n_split", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class gqa_mla_desc(ctypes.Structure):
@@ -127,6 +129,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _temp_workspace(nbytes, device, stream):
+    """A workspace the call allocates for itself, on the stream its kernels run
+    on: the caching allocator then hands the block to another tensor only
+    behind that stream's work, even when `stream` is not torch's current
+    stream and the tensor is freed as soon as the call returns."""
+    if stream is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def _dtype_code(t):
     if t.dtype == torch.float32:
         return GQA_F32
@@ -164,11 +177,12 @@ def _require(t, name, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
-def decode_desc(q, k_cache, n_split=0):
+def decode_desc(q, k_cache, n_split=0, deterministic=False):
     """Descriptor for q [B, h_q, d] and cache [B, n_kv, S_max, d]."""
     B, h_q, d = q.shape
     n_kv, s_max = k_cache.shape[1], k_cache.shape[2]
-    return gqa_decode_desc(B, h_q, n_kv, s_max, d, _dtype_code(q), _kv_code(k_cache, d), n_split)
+    return gqa_decode_desc(B, h_q, n_kv, s_max, d, _dtype_code(q), _kv_code(k_cache, d), n_split,
+                           GQA_DECODE_DETERMINISTIC if deterministic else 0)
 
 
 def attn_decode_num_splits(desc):
@@ -196,21 +210,21 @@ def _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale):
                 raise ValueError(f"{name} must be a contiguous float32 tensor of shape [B, n_kv, S_max]")
 
 
-def _workspace(desc, device, workspace):
-    need = attn_decode_workspace_bytes(desc)
+def _workspace(desc, device, workspace, stream):
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        workspace = _temp_workspace(attn_decode_workspace_bytes(desc), device, stream)
     return workspace, workspace.numel() * workspace.element_size()
 
 
 def attn_decode(q, k_cache, v_cache, seq_lens, scale, out=None, k_scale=None, v_scale=None, workspace=None,
-                n_split=0, stream=None):
-    """out[B, h_q, d] = GQA decode step (split + combine kernels)."""
+                n_split=0, stream=None, deterministic=False):
+    """out[B, h_q, d] = GQA decode step (split + combine kernels).  With
+    deterministic=True identical calls give identical bits."""
     _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
-    desc = decode_desc(q, k_cache, n_split)
+    desc = decode_desc(q, k_cache, n_split, deterministic)
     if out is None:
         out = torch.empty_like(q)
-    workspace, ws_bytes = _workspace(desc, q.device, workspace)
+    workspace, ws_bytes = _workspace(desc, q.device, workspace, stream)
     _check(load_library().attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                       _ptr(v_scale), _ptr(seq_lens), float(scale), _ptr(out), _ptr(workspace),
                                       ws_bytes, _stream(stream)))
@@ -238,10 +252,10 @@ class PreparedCall:
 
 
 def prepare_decode(q, k_cache, v_cache, seq_lens, scale, out, workspace, k_scale=None, v_scale=None, n_split=0,
-                   stream=None):
+                   stream=None, deterministic=False):
     """PreparedCall of attn_decode (see attn_decode for the arguments)."""
     _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
-    desc = decode_desc(q, k_cache, n_split)
+    desc = decode_desc(q, k_cache, n_split, deterministic)
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < attn_decode_workspace_bytes(desc):
         raise ValueError("workspace smaller than attn_decode_workspace_bytes")
@@ -256,10 +270,10 @@ def prepare_decode(q, k_cache, v_cache, seq_lens, scale, out, workspace, k_scale
 
 
 def prepare_decode_partials(q, k_cache, v_cache, seq_lens, scale, workspace, k_scale=None, v_scale=None, n_split=0,
-                            stream=None):
+                            stream=None, deterministic=False):
     """PreparedCall of attn_decode_partials."""
     _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
-    desc = decode_desc(q, k_cache, n_split)
+    desc = decode_desc(q, k_cache, n_split, deterministic)
     ws_bytes = workspace.numel() * workspace.element_size()
     lib = load_library()
     args = (ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens),
@@ -270,10 +284,10 @@ def prepare_decode_partials(q, k_cache, v_cache, seq_lens, scale, workspace, k_s
 
 
 def attn_decode_partials(q, k_cache, v_cache, seq_lens, scale, workspace, k_scale=None, v_scale=None, n_split=0,
-                         stream=None):
+                         stream=None, deterministic=False):
     """Split kernel only: per-chunk partials into `workspace`."""
     _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
-    desc = decode_desc(q, k_cache, n_split)
+    desc = decode_desc(q, k_cache, n_split, deterministic)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().attn_decode_partials(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                                _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens), float(scale),
@@ -289,12 +303,12 @@ def attn_decode_combine(q, k_cache, seq_lens, workspace, out, n_split=0, stream=
     return out
 
 
-def paged_desc(q, k_pages, block_table, n_split=0):
+def paged_desc(q, k_pages, block_table, n_split=0, deterministic=False):
     """Descriptor for q [B, h_q, d], pages [num_pages, n_kv, page_size, d] and block_table [B, max_pages]."""
     B, h_q, d = q.shape
     num_pages, n_kv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     return gqa_paged_desc(B, h_q, n_kv, d, _dtype_code(q), _kv_code(k_pages, d), page_size, num_pages,
-                          block_table.shape[1], n_split)
+                          block_table.shape[1], n_split, GQA_DECODE_DETERMINISTIC if deterministic else 0)
 
 
 def attn_decode_paged_num_splits(desc):
@@ -326,15 +340,14 @@ def _paged_checks(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale):
 
 
 def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out=None, k_scale=None, v_scale=None,
-                      workspace=None, n_split=0, stream=None):
+                      workspace=None, n_split=0, stream=None, deterministic=False):
     """out[B, h_q, d] = GQA decode step over a paged cache (see attn_decode_paged in gqa_attn.h)."""
     _paged_checks(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale)
-    desc = paged_desc(q, k_pages, block_table, n_split)
+    desc = paged_desc(q, k_pages, block_table, n_split, deterministic)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = torch.empty(max(attn_decode_paged_workspace_bytes(desc), 16), dtype=torch.uint8,
-                                device=q.device)
+        workspace = _temp_workspace(attn_decode_paged_workspace_bytes(desc), q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().attn_decode_paged(ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                             _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
@@ -391,8 +404,7 @@ def attn_decode_mla(q_abs, c_kv, seq_lens, scale, out=None, workspace=None, n_sp
     _mla_checks(q_abs, c_kv, seq_lens, out)
     desc = mla_desc(q_abs, c_kv, n_split)
     if workspace is None:
-        workspace = torch.empty(max(attn_decode_mla_workspace_bytes(desc), 16), dtype=torch.uint8,
-                                device=q_abs.device)
+        workspace = _temp_workspace(attn_decode_mla_workspace_bytes(desc), q_abs.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().attn_decode_mla(ctypes.byref(desc), _ptr(q_abs), _ptr(c_kv), _ptr(seq_lens),
                                           float(scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -3,6 +3,8 @@
 // allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cfloat>
 #include <cstdint>
 #include <cstring>
 
@@ -16,10 +18,12 @@ namespace {
 constexpr double kLog2e = 1.4426950408889634;
 constexpr int kTileMfma = 32;
 constexpr int kTileF32 = 64;
-// Default number of decode workgroups: one per compute unit of an MI355X
-// (256 CUs); each runs 8 wavefronts and owns 1/256 of all key tiles.
-constexpr long kDefaultWorkgroups = 256;
+// Default number of decode workgroups: one per compute unit of the current
+// device (each runs 8 wavefronts and owns an equal share of all key tiles);
+// 256, a whole MI355X, when no device can be queried.
+constexpr int kFallbackComputeUnits = 256;
 constexpr long kMaxWorkgroups = 65536;
+constexpr int kMaxDevices = 64;
 
 thread_local char g_last_hip_error[256] = "";
 
@@ -30,6 +34,37 @@ void record_hip_error(hipError_t e) {
 }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Compute units of the current device, queried once per device and cached
+// (a device partitioned into fewer CUs gets a persistent grid of its own
+// size).  The query enqueues nothing; if it fails (no device), the count of a
+// whole MI355X is used and the error is cleared so that it cannot be taken
+// for a launch failure later.
+int device_compute_units() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return kFallbackComputeUnits;
+  }
+  if (dev < kMaxDevices) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return kFallbackComputeUnits;
+  }
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// scale * log2(e) as the kernels take it.  A scale so small that the product
+// is not a normal float is raised to the smallest normal: the scores are then
+// effectively zero either way, and a zero factor would turn the -inf of a
+// hidden key into NaN.
+float qk_scale_log2(float scale) { return fmaxf((float)((double)scale * kLog2e), FLT_MIN); }
 
 // K/V element types that come with per-row scales
 bool is_quantized(int32_t t) { return t == GQA_FP8_E4M3 || t == GQA_INT8 || t == GQA_INT4; }
@@ -45,12 +80,14 @@ struct DecodePlan {
   int n_hchunk;         // head chunks per K/V group
   long n_slabs;         // B * n_kv * n_hchunk
   int W;                // workgroups launched (balanced key ranges)
+  int deterministic;    // static tile order inside a workgroup
 };
 
 gqa_status validate_decode_desc(const gqa_decode_desc* d) {
   if (!d) return GQA_ERR_NULL;
   if (d->B <= 0 || d->h_q <= 0 || d->n_kv <= 0 || d->S_max <= 0 || d->d_h <= 0 || d->n_split < 0)
     return GQA_ERR_SHAPE;
+  if ((d->flags & ~GQA_DECODE_DETERMINISTIC) != 0) return GQA_ERR_VALUE;
   if (d->h_q % d->n_kv != 0) return GQA_ERR_SHAPE;
   if (d->d_h != 64 && d->d_h != 128) return GQA_ERR_SHAPE;
   const bool ok = (d->q_dtype == GQA_F32 && d->kv_dtype == GQA_F32) ||
@@ -87,11 +124,12 @@ DecodePlan plan_decode(const gqa_decode_desc* d) {
   p.n_hchunk = (G + p.heads_per_chunk - 1) / p.heads_per_chunk;
   p.n_slabs = (long)d->B * d->n_kv * p.n_hchunk;
   const long max_tiles = p.n_slabs * ((d->S_max + p.tile - 1) / p.tile);
-  long W = d->n_split > 0 ? (long)d->n_split : kDefaultWorkgroups;
+  long W = d->n_split > 0 ? (long)d->n_split : device_compute_units();
   if (W > max_tiles) W = max_tiles;
   if (W > kMaxWorkgroups) W = kMaxWorkgroups;
   if (W < 1) W = 1;
   p.W = (int)W;
+  p.deterministic = (d->flags & GQA_DECODE_DETERMINISTIC) != 0;
   return p;
 }
 
@@ -144,13 +182,14 @@ gqa_status do_partials(const gqa_decode_desc* d, const DecodePlan& p, const void
   a.seq_lens = seq_lens;
   a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
-  a.qk_scale_log2 = (float)((double)scale * kLog2e);
+  a.qk_scale_log2 = qk_scale_log2(scale);
   a.B = d->B;
   a.h_q = d->h_q;
   a.n_kv = d->n_kv;
   a.S_max = d->S_max;
   a.n_hchunk = p.n_hchunk;
   a.heads_per_chunk = p.heads_per_chunk;
+  a.deterministic = p.deterministic;
   hipError_t e = launch_decode_split(a, d->d_h, p.hb, p.kind, p.W, stream);
   if (e != hipSuccess) {
     record_hip_error(e);
@@ -194,7 +233,7 @@ gqa_status paged_to_decode_desc(const gqa_paged_desc* pd, gqa_decode_desc* d, in
   if ((int64_t)pd->B * pd->max_pages_per_seq > (int64_t)1 << 31) return GQA_ERR_SHAPE;
   if ((int64_t)pd->num_pages * pd->n_kv * ps > (int64_t)1 << 40) return GQA_ERR_SHAPE;
   *d = gqa_decode_desc{pd->B, pd->h_q, pd->n_kv, pd->max_pages_per_seq * ps, pd->d_h, pd->q_dtype, pd->kv_dtype,
-                       pd->n_split};
+                       pd->n_split, pd->flags};
   int sh = 0;
   while ((1 << sh) < ps) ++sh;
   *page_shift = sh;
@@ -228,7 +267,7 @@ MlaPlan plan_mla(const gqa_mla_desc* d) {
   p.n_hchunk = (d->h_q + p.heads_per_chunk - 1) / p.heads_per_chunk;
   p.n_slabs = (long)d->B * p.n_hchunk;
   const long max_tiles = p.n_slabs * ((d->S_max + kTileMfma - 1) / kTileMfma);
-  long W = d->n_split > 0 ? (long)d->n_split : kDefaultWorkgroups;
+  long W = d->n_split > 0 ? (long)d->n_split : device_compute_units();
   if (W > max_tiles) W = max_tiles;
   if (W > kMaxWorkgroups) W = kMaxWorkgroups;
   if (W < 1) W = 1;
@@ -359,8 +398,8 @@ gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const v
   if (!q || !k || !v || !out) return GQA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return GQA_ERR_ALIGN;
   if (bad_scale(scale)) return GQA_ERR_VALUE;
-  hipError_t e = launch_prefill_causal(q, k, v, out, (float)((double)scale * kLog2e), d->B, d->S, d->h_q, d->n_kv,
-                                       d->d_h, stream);
+  hipError_t e = launch_prefill_causal(q, k, v, out, qk_scale_log2(scale), d->B, d->S, d->h_q, d->n_kv, d->d_h,
+                                       stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;
@@ -397,7 +436,7 @@ gqa_status attn_decode_mla_partials(const gqa_mla_desc* d, const void* q_abs, co
   a.seq_lens = seq_lens;
   a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
-  a.qk_scale_log2 = (float)((double)scale * kLog2e);
+  a.qk_scale_log2 = qk_scale_log2(scale);
   a.B = d->B;
   a.h_q = d->h_q;
   a.S_max = d->S_max;
@@ -480,7 +519,7 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
         reinterpret_cast<uintptr_t>(v_descale)) & 3u) != 0)
     return GQA_ERR_ALIGN;
   if (bad_scale(scale)) return GQA_ERR_VALUE;
-  const float sl2 = (float)((double)scale * kLog2e);
+  const float sl2 = qk_scale_log2(scale);
   const hipError_t e =
       fp8 ? launch_prefill_fp8(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->causal, kv_lens, mask,
                                q_descale, k_descale, v_descale, stream)
@@ -502,7 +541,7 @@ const char* gqa_status_string(gqa_status s) {
     case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer not 16-byte aligned";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch failed";
-    case GQA_ERR_VALUE: return "GQA_ERR_VALUE: scale must be finite and > 0";
+    case GQA_ERR_VALUE: return "GQA_ERR_VALUE: scale not finite and > 0, or unknown flag bits";
   }
   return "unknown gqa_status";
 }

@@ -258,8 +258,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 
   // Further tiles of a segment (after each wave's first two) are claimed
   // from an LDS counter, so waves whose loads are served faster take more
-  // tiles and all reach the segment's merge at about the same time.
-  auto claim_tile = [&]() {
+  // tiles and all reach the segment's merge at about the same time.  In the
+  // deterministic mode wave i keeps the static order i, i + NW, i + 2 NW, ...,
+  // which fixes every wave's summation order and rounding points.
+  const bool det = a.deterministic != 0;
+  auto claim_tile = [&](int cur_tile) {
+    if (det) return cur_tile + NW;
     int v = 0;
     if (lane == 0) v = atomicAdd(&s_next_tile, 1);
     return uniform(__shfl(v, 0, 64));
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       tile = next_tile;
       if (tile >= cur.ntile) break;
       stage(0);
-      next_tile = claim_tile();
+      next_tile = claim_tile(tile);
       issue_next(next_tile, 0);
     }
 

@@ -35,6 +35,7 @@ struct DecodeArgs {
   float* part_ml;  // [W + n_slabs][heads_per_chunk][2]: running max (log2 domain), running sum
   float qk_scale_log2;
   int B, h_q, n_kv, S_max, n_hchunk, heads_per_chunk;
+  int deterministic;  // nonzero: wave i takes tiles i, i + NW, ... of a segment (no tile claims)
 };
 
 struct CombineArgs {

@@ -63,8 +63,12 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // then have no visible key at all (zero output).
 // F8: q, k, v are OCP e4m3 codes with one descale factor per (batch, head)
 // (the FP8 mode of FlashAttention-3, "Flash Attention 3 Features"); both
-// products run on v_mfma_f32_32x32x64_f8f6f4, P rounded to e4m3 (kept <= 256
-// by the reference max, below the format's 448), d = 128 only.
+// products run on v_mfma_f32_32x32x64_f8f6f4, d = 128 only.  The softmax
+// weights enter the second product as two e4m3 terms, p = hi + lo with hi =
+// e4m3(p) and lo = e4m3(p - hi) (two products per d tile), so each weight
+// carries a relative error of at most 2^-8 (2^-10 absolute for the smallest)
+// instead of the 2^-4 of a single e4m3 value; the reference max keeps every
+// p <= 256, below the format's 448.
 // MASK (with GEN): a dense mask is given; without it the mask machinery
 // (tile bitmaps, mask tiles, per-element masking) is compiled out.
 template <int D, int HC, bool GEN, bool F8 = false, bool MASK = false>
@@ -154,7 +158,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       }
       qf8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
-    qk_log2 *= a.q_descale[(size_t)b * a.h_q + head] * a.k_descale[(size_t)b * a.n_kv + g];
+    // a zero descale (an all-zero head quantised by absmax) would make the
+    // score factor 0 and turn the -inf of a hidden key into NaN; the smallest
+    // normal float keeps hidden keys at -inf and every visible score at zero
+    // to float precision, which is the exact result (equal weights)
+    qk_log2 = fmaxf(qk_log2 * (a.q_descale[(size_t)b * a.h_q + head] * a.k_descale[(size_t)b * a.n_kv + g]),
+                    __FLT_MIN__);
     out_scale = a.v_descale[(size_t)b * a.n_kv + g];
   }
 
@@ -539,15 +548,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       }
       l += psum;
       if constexpr (F8) {
-        // ---- O^T += V^T P^T on one 64-key product per 32-wide d tile.  P
-        // byte b = 16kh + r of a lane is the score register sacc[kh][r], key
+        // ---- O^T += V^T P^T on two 64-key products (hi and lo weights) per
+        // 32-wide d tile.  P byte b = 16kh + r of a lane is the score register sacc[kh][r], key
         // 32kh + 8(r/4) + 4h2 + r%4.  ds_read_b64_tr_b8 hands output lane
         // 16gg + 8u + c byte j of source lane 16gg + 2j + u (byte c of its 8):
         // source lane (gg, j, u) therefore reads, for read t (bytes 8t..8t+7),
         // key 32(t/2) + 16(t%2) + 8(j/4) + 4(gg/2) + j%4 at d columns
         // 32dt + 16(gg%2) + 8u .. +7, so that output lane l holds d = 32dt +
         // l%32 for exactly the keys of its P bytes.
-        i32x8 pf8;
+        i32x8 pf8, pl8;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           const f32x16& sp = sacc[w >> 2];
@@ -555,6 +564,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
           int x = __builtin_amdgcn_cvt_pk_fp8_f32(sp[r0], sp[r0 + 1], 0, false);
           x = __builtin_amdgcn_cvt_pk_fp8_f32(sp[r0 + 2], sp[r0 + 3], x, true);
           pf8[w] = x;
+          // the rounding remainders, exact in float32, rounded to e4m3 again
+          const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+          const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+          int y = __builtin_amdgcn_cvt_pk_fp8_f32(sp[r0] - h01[0], sp[r0 + 1] - h01[1], 0, false);
+          y = __builtin_amdgcn_cvt_pk_fp8_f32(sp[r0 + 2] - h23[0], sp[r0 + 3] - h23[1], y, true);
+          pl8[w] = y;
         }
         const int gg = lane >> 4, jj = (lane & 15) >> 1, uu = lane & 1;
         const int vkey = 8 * (jj >> 2) + 4 * (gg >> 1) + (jj & 3);  // plus 16t: same swizzle for every t
@@ -571,6 +586,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
             vf8[2 * t + 1] = r[1];
           }
           o[nt] = mfma32_fp8(vf8, pf8, o[nt]);
+          o[nt] = mfma32_fp8(vf8, pl8, o[nt]);
         }
       } else {
       // ---- O^T += V^T P^T, 4 k-steps of 16 keys
