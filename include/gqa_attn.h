@@ -72,8 +72,10 @@ typedef enum gqa_status {
   GQA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
   GQA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
   GQA_ERR_HIP = 6,       /* a HIP launch or query failed                      */
-  GQA_ERR_VALUE = 7      /* scale is not a finite number > 0, or a flags
+  GQA_ERR_VALUE = 7,     /* scale is not a finite number > 0, or a flags
                             word holds unknown bits                           */
+  GQA_ERR_SCRATCH = 8    /* attn_decode_noalloc: the call's partials need
+                            more than attn_decode_noalloc_max_scratch_bytes() */
 } gqa_status;
 
 /* Decode flags (gqa_decode_desc.flags, gqa_paged_desc.flags). */
@@ -168,6 +170,28 @@ gqa_status attn_decode_partials(const gqa_decode_desc* d, const void* q, const v
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 gqa_status attn_decode_combine(const gqa_decode_desc* d, const int32_t* seq_lens, const void* workspace,
                                size_t workspace_bytes, void* out, hipStream_t stream);
+
+/* ------------------------------------------- decode without allocation --
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * step of attn_decode with the same arguments except the workspace.  The
+ * partials live in a static device array of the library, 16 MiB per GPU,
+ * which each GPU the library runs on holds until the process ends; its
+ * device address is looked up once per device on the first call there.
+ * The call allocates and frees nothing (no hipMalloc, no hipFree).
+ * A descriptor whose workspace (attn_decode_workspace_bytes) exceeds
+ * attn_decode_noalloc_max_scratch_bytes() returns GQA_ERR_SCRATCH and
+ * enqueues nothing; the ragged GQA, long MQA and fp8 / int8 / int4 cache
+ * workloads of this library's benchmark need at most 5.3 MiB.  All calls on
+ * one GPU share its array: two calls whose work can overlap on that GPU
+ * (different streams without ordering between them) race and give wrong
+ * results; calls ordered on one stream are safe.  No contents need to carry
+ * over between calls.  Results equal those of attn_decode with the same
+ * descriptor (bit for bit with GQA_DECODE_DETERMINISTIC). */
+size_t attn_decode_noalloc_max_scratch_bytes(void);
+gqa_status attn_decode_noalloc(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                               void* out, hipStream_t stream);
 
 /* ------------------------------------------------------ paged decode --
  * The decode step of attn_decode over a paged cache ("Multi-Query Attention

@@ -327,3 +327,20 @@ def test_deterministic_flag_keeps_the_plan(lib):
     assert call_decode(lib, b, q=None) == 1
     assert lib.gqa_last_hip_error().decode() == ""
 
+
+
+def test_noalloc_scratch_limit_is_checked_on_the_host(lib):
+    """attn_decode_noalloc rejects, before any HIP call, a descriptor whose
+    partials need more than the static scratch holds (here 64 x 64 slabs)."""
+    assert lib.attn_decode_noalloc_max_scratch_bytes() == 16 << 20
+    big = dd(B=64, h_q=64, n_kv=64, S=4096)
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(big)) > lib.attn_decode_noalloc_max_scratch_bytes()
+    assert lib.attn_decode_noalloc(ctypes.byref(big), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
+                                   ALIGNED, None) == 8
+    assert lib.attn_decode_noalloc(ctypes.byref(dd()), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
+                                   None, None) == 1
+    assert lib.attn_decode_noalloc(ctypes.byref(dd()), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 0.0,
+                                   ALIGNED, None) == 7
+    assert lib.attn_decode_noalloc(ctypes.byref(dd(flags=2)), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
+                                   ALIGNED, None) == 7
+    assert lib.gqa_last_hip_error().decode() == ""

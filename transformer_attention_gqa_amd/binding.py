@@ -21,11 +21,12 @@ GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_INT8, GQA_INT4 = 0, 1, 2, 3, 4
 GQA_DECODE_DETERMINISTIC = 1
 QUANTIZED_KV = (GQA_FP8_E4M3, GQA_INT8, GQA_INT4)
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE", 4: "GQA_ERR_ALIGN",
-          5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE"}
+          5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_HIP", 7: "GQA_ERR_VALUE", 8: "GQA_ERR_SCRATCH"}
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
             "attn_decode_combine", "attn_decode_paged_num_splits", "attn_decode_paged_workspace_bytes",
             "attn_decode_paged", "attn_decode_mla_num_splits", "attn_decode_mla_workspace_bytes",
-            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "attn_prefill", "gqa_status_string", "gqa_last_hip_error")
+            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "attn_prefill", "gqa_status_string", "gqa_last_hip_error",
+            "attn_decode_noalloc", "attn_decode_noalloc_max_scratch_bytes")
 
 
 class GqaError(RuntimeError):
@@ -81,6 +82,9 @@ def load_library(path=LIB_PATH):
     lib.attn_decode_workspace_bytes.argtypes, lib.attn_decode_workspace_bytes.restype = [dd], sz
     lib.attn_decode.argtypes = [dd, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = [dd, vp, vp, vp, vp, vp, vp, f32, vp, vp]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
+    lib.attn_decode_noalloc_max_scratch_bytes.argtypes, lib.attn_decode_noalloc_max_scratch_bytes.restype = [], sz
     lib.attn_decode_partials.argtypes = [dd, vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
     lib.attn_decode_partials.restype = ctypes.c_int
     lib.attn_decode_combine.argtypes = [dd, vp, vp, sz, vp, vp]
@@ -228,6 +232,25 @@ def attn_decode(q, k_cache, v_cache, seq_lens, scale, out=None, k_scale=None, v_
     _check(load_library().attn_decode(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                       _ptr(v_scale), _ptr(seq_lens), float(scale), _ptr(out), _ptr(workspace),
                                       ws_bytes, _stream(stream)))
+    return out
+
+
+def attn_decode_noalloc_max_scratch_bytes():
+    return load_library().attn_decode_noalloc_max_scratch_bytes()
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seq_lens, scale, out, k_scale=None, v_scale=None, n_split=0,
+                        stream=None, deterministic=False):
+    """attn_decode with its partials in the library's static device scratch:
+    allocates nothing (the caller passes `out`).  Calls that can overlap on
+    one GPU race (see attn_decode_noalloc in gqa_attn.h)."""
+    _decode_checks(q, k_cache, v_cache, seq_lens, k_scale, v_scale)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    desc = decode_desc(q, k_cache, n_split, deterministic)
+    _check(load_library().attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(k_scale), _ptr(v_scale), _ptr(seq_lens), float(scale), _ptr(out),
+                                              _stream(stream)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cfloat>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "gqa_attn.h"
 #include "gqa_launch.h"
@@ -285,6 +286,42 @@ WorkspaceLayout mla_workspace_layout(const gqa_mla_desc* d, const MlaPlan& p) {
   return l;
 }
 
+// ---- scratch of attn_decode_noalloc: the split kernel's partial rows live in
+// one file-scope device array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy for the life of the process.  In host
+// code `scratch` names a host-side stand-in, not device memory: kernels and
+// copies take the device address that hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (null + status on
+// failure).
+gqa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    const hipError_t e = hipGetLastError();
+    record_hip_error(e != hipSuccess ? e : hipErrorInvalidDevice);
+    return GQA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      record_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      (void)hipGetLastError();
+      return GQA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
 }  // namespace
 }  // namespace gqa
 
@@ -345,6 +382,30 @@ gqa_status attn_decode(const gqa_decode_desc* d, const void* q, const void* k_ca
   st = do_partials(d, p, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, workspace, stream);
   if (st != GQA_OK) return st;
   return do_combine(d, p, seq_lens, workspace, out, stream);
+}
+
+size_t attn_decode_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+gqa_status attn_decode_noalloc(const gqa_decode_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale, const int32_t* seq_lens, float scale,
+                               void* out, hipStream_t stream) {
+  gqa_status st = validate_decode_desc(d);
+  if (st != GQA_OK) return st;
+  st = check_decode_ptrs(d, q, k_cache, v_cache, k_scale, v_scale, seq_lens);
+  if (st != GQA_OK) return st;
+  if (!out) return GQA_ERR_NULL;
+  if (misaligned(out)) return GQA_ERR_ALIGN;
+  if (bad_scale(scale)) return GQA_ERR_VALUE;
+  const DecodePlan p = plan_decode(d);
+  if (workspace_layout(d, p).total > kScratchBytes) return GQA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != GQA_OK) return st;
+  // the split kernel writes every partial the combine kernel reads, so the
+  // scratch needs no clearing between calls
+  st = do_partials(d, p, q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, ws, stream);
+  if (st != GQA_OK) return st;
+  return do_combine(d, p, seq_lens, ws, out, stream);
 }
 
 int32_t attn_decode_paged_num_splits(const gqa_paged_desc* pd) {
@@ -542,6 +603,8 @@ const char* gqa_status_string(gqa_status s) {
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch failed";
     case GQA_ERR_VALUE: return "GQA_ERR_VALUE: scale not finite and > 0, or unknown flag bits";
+    case GQA_ERR_SCRATCH:
+      return "GQA_ERR_SCRATCH: the call needs more partial rows than the library's static scratch holds";
   }
   return "unknown gqa_status";
 }
