@@ -66,6 +66,21 @@ def measured_traffic(kernel_key):
     return ent.get("hbm_bytes_per_launch")
 
 
+def measured_mfma(kernel_key):
+    """Matrix-core counters of a prefill kernel from the committed counter run
+    (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE), or
+    nulls if absent or taken on a different kernel source."""
+    none = {"mfma_busy": None, "clock_GHz": None}
+    try:
+        data = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return none
+    ent = data.get("kernels", {}).get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest() or ent.get("mfma_busy") is None:
+        return none
+    return {"mfma_busy": ent["mfma_busy"], "clock_GHz": ent.get("clock_GHz")}
+
+
 def precondition_gpu(seconds=0.3):
     """Run dense bf16 matrix products for about `seconds` so the GPU has left
     its idle clock state before the first warmup step (a few warmup steps of
@@ -81,33 +96,54 @@ def precondition_gpu(seconds=0.3):
 
 def measure_ceilings():
     """Reference rates measured on this GPU in the same run (context for the
-    roofline fractions, which are taken against the vendor peaks): a 2 GiB
-    device-to-device copy (bytes read + written per second) and an
-    8192^3 bf16 matrix product through the vendor BLAS."""
+    roofline fractions, which are taken against the vendor peaks): the
+    library's read-only stream over 2 GiB (gqa_stream_read: every byte read
+    once with the decode kernels' 128-bit non-temporal loads, nothing
+    written), median of 10 timed passes, and an 8192^3 bf16 matrix product
+    through the vendor BLAS."""
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
             fn()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e-3
-    n = 1 << 30  # bf16 elements: 2 GiB
-    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
-    dst = torch.empty_like(src)
-    src.fill_(1.0)
-    t_copy = timed(lambda: dst.copy_(src), 10)
-    del src, dst
+        ts = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps))
+        return ts[len(ts) // 2], ts[0]
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t_read, t_read_min = timed(lambda: binding.gqa_stream_read(buf, sink), 10)
+    del buf
     a = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
     bm = torch.randn(8192, 8192, dtype=torch.bfloat16, device="cuda")
-    t_mm = timed(lambda: torch.mm(a, bm), 20)
+    t_mm, _ = timed(lambda: torch.mm(a, bm), 20)
     del a, bm
     torch.cuda.empty_cache()
-    return {"copy_GBps": 2 * 2 * n / t_copy / 1e9,
+    return {"stream_read_GBps": nbytes / t_read / 1e9,
+            "stream_read_GBps_best": nbytes / t_read_min / 1e9,
             "bf16_gemm_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
-            "note": "2 GiB device copy (read + write bytes) and an 8192^3 bf16 torch.mm, same run"}
+            "note": "gqa_stream_read over 2 GiB (read-only, median and best of 10) and an 8192^3 bf16 "
+                    "torch.mm (median of 20), same run"}
+
+
+def step_distribution(step_fn, steps):
+    """Per-step device times (ms) of `steps` back-to-back steps: HIP events
+    recorded on the launch stream between consecutive steps, in a region of
+    its own after the timed one.  Returns median, min and max."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        step_fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ts = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return {"median": ts[len(ts) // 2] if len(ts) % 2 else 0.5 * (ts[len(ts) // 2 - 1] + ts[len(ts) // 2]),
+            "min": ts[0], "max": ts[-1], "n": steps}
 
 
 def time_steps(step_fn, steps, warmup, use_graph=False):
@@ -179,6 +215,7 @@ def bench_decode(wl, steps, warmup, use_graph=False, n_split=0):
         part_calls[i % ncopies]()
 
     ms_step, ev_ms = time_steps(step, steps, warmup, use_graph)
+    dist = step_distribution(step, steps)
     # the split kernel (the one that reads the cache) over a region of its own
     _, kernel_ms = time_steps(partials, steps, 2, use_graph)
 
@@ -197,6 +234,7 @@ def bench_decode(wl, steps, warmup, use_graph=False, n_split=0):
         "n_split": n_split,
         "kv_copies_rotated": ncopies,
         "event_ms_per_step": ev_ms,
+        "step_ms": dist,
         "split_kernel_ms": kernel_ms,
         "combine_ms_approx": ev_ms - kernel_ms,
         "roofline": {"bound": "hbm", "kernel": "gqa_decode_split_mfma" if wl.kv_dtype != "f32"
@@ -237,6 +275,7 @@ def bench_decode_paged(pwl, steps, warmup, use_graph=False):
         calls[i % ncopies]()
 
     ms_step, ev_ms = time_steps(step, steps, warmup, use_graph)
+    dist = step_distribution(step, steps)
     key = f"decode_split_paged_{wl.kv_dtype}:{pwl.name}"
     # a step is split + combine; the combine's share is taken from the
     # contiguous workload's launches of the same grid in the kernel trace
@@ -254,6 +293,7 @@ def bench_decode_paged(pwl, steps, warmup, use_graph=False):
         "n_split": n_split,
         "kv_copies_rotated": ncopies,
         "event_ms_per_step": ev_ms,
+        "step_ms": dist,
         "roofline": {"bound": "hbm", "kernel": "gqa_decode_split_mfma (paged) + gqa_decode_combine",
                      "achieved": achieved_step, "peak": roofline.HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved_step / roofline.HBM_PEAK_GBPS, "traffic": measured_traffic(key)},
@@ -287,6 +327,7 @@ def bench_decode_mla(wl, steps, warmup, use_graph=False):
         part_calls[i % ncopies]()
 
     ms_step, ev_ms = time_steps(step, steps, warmup, use_graph)
+    dist = step_distribution(step, steps)
     _, kernel_ms = time_steps(partials, steps, 2, use_graph)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     flops = roofline.mla_flops(wl.h_q, wl.d_c, lens)
@@ -301,6 +342,7 @@ def bench_decode_mla(wl, steps, warmup, use_graph=False):
         "n_split": binding.attn_decode_mla_num_splits(desc),
         "kv_copies_rotated": ncopies,
         "event_ms_per_step": ev_ms,
+        "step_ms": dist,
         "split_kernel_ms": kernel_ms,
         "combine_ms_approx": ev_ms - kernel_ms,
         "split_kernel_tflops": flops / (kernel_ms * 1e-3) / 1e12,
@@ -325,8 +367,10 @@ def bench_prefill(wl, steps, warmup, use_graph=False):
         call()
 
     ms_step, k_ms = time_steps(step, steps, warmup, use_graph)  # one launch per step
+    dist = step_distribution(step, steps)
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = roofline.MFMA_PEAK_TFLOPS["bf16"]
+    ckey = f"prefill_causal:{wl.name}"
     return {
         "workload": wl.name,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -336,9 +380,10 @@ def bench_prefill(wl, steps, warmup, use_graph=False):
         "causal_flops": flops,
         "io_bytes": roofline.prefill_io_bytes(wl.B, wl.S, wl.h_q, wl.n_kv, wl.d_h),
         "kernel_ms": k_ms,
+        "step_ms": dist,
         "roofline": {"bound": "mfma", "kernel": "gqa_prefill_causal_kernel", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(f"prefill_causal:{wl.name}")},
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(ckey),
+                     **measured_mfma(ckey)},
         "dtype": "bf16",
         "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "h_q": wl.h_q, "n_kv": wl.n_kv, "d_h": wl.d_h,
                    "seed": wl.seed},
@@ -361,8 +406,10 @@ def bench_prefill_masked(wl, steps, warmup, use_graph=False):
         call()
 
     ms_step, k_ms = time_steps(step, steps, warmup, use_graph)
+    dist = step_distribution(step, steps)
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = roofline.MFMA_PEAK_TFLOPS[wl.dtype]  # a contraction takes its own dtype's peak
+    ckey = f"prefill_masked:{wl.name}"
     return {
         "workload": wl.name,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -372,10 +419,11 @@ def bench_prefill_masked(wl, steps, warmup, use_graph=False):
         "visible_pairs": pairs,
         "visible_flops": flops,
         "kernel_ms": k_ms,
+        "step_ms": dist,
         "roofline": {"bound": "mfma", "kernel": "gqa_prefill_fp8_kernel" if wl.dtype == "fp8"
                      else "gqa_prefill_masked_kernel", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": measured_traffic(f"prefill_masked:{wl.name}")},
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(ckey),
+                     **measured_mfma(ckey)},
         "dtype": wl.dtype,
         "config": {"workload": wl.name, "B": wl.B, "S_q": wl.S_q, "S_k": wl.S_k, "h_q": wl.h_q, "n_kv": wl.n_kv,
                    "d_h": wl.d_h, "causal": wl.causal, "kv_lens": wl.kv_lens, "mask": wl.mask, "dtype": wl.dtype,
@@ -434,7 +482,11 @@ PROFILE_COMMANDS = {
              "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <out>/prof_write -o run --output-format csv -- "
              "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --kernel-trace "
+            "-d <out>/prof_mfma -o run --output-format csv -- python3 bench.py --steps 5 --warmup 1 "
+            "--no-cpu-baseline",
 }
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 CALIB_GRID = (1 << 30) // 16  # threads of the calibration kernel (4 floats per thread)
 
 
@@ -537,7 +589,30 @@ def _workload_launches():
     return out
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
+def mfma_utilisation(busy, gui_active, duration_ns, n_cu):
+    """Matrix-core busy fraction and clock of one dispatch from rocprofv3
+    counters.  GRBM_GUI_ACTIVE counts the GPU's busy cycles once per XCD
+    (8 on MI355X), so per-XCD cycles are GRBM_GUI_ACTIVE / 8 and the clock is
+    that over the kernel's duration; SQ_VALU_MFMA_BUSY_CYCLES sums the busy
+    cycles of every SIMD's matrix core (4 per compute unit), so the busy
+    fraction is it over 4 * n_cu * per-XCD cycles."""
+    cycles = gui_active / 8.0
+    return busy / (4.0 * n_cu * cycles), cycles / duration_ns
+
+
+def _counter_rows(d):
+    """rocprofv3 counter rows of a run -> {dispatch id: (kernel name, grid size, {counter: value})}."""
+    import csv
+    out = {}
+    for f in os.listdir(d):
+        if f.endswith("counter_collection.csv"):
+            for r in csv.DictReader(open(os.path.join(d, f))):
+                ent = out.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], int(r["Grid_Size"]), {}))
+                ent[2][r["Counter_Name"]] = ent[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, dest, mfma_dir=None, n_cu=256):
     import csv
     import statistics
 
@@ -595,9 +670,38 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
         for ckey, r in resolve(((*kernel_identity(r["Kernel_Name"]), int(r["Grid_Size"])), r) for r in crow):
             counters.setdefault((kind, ckey), []).append(float(r["Counter_Value"]))
         counters[(kind, "scale")] = (1 << 20) / statistics.median(calib)  # KiB expected / KiB counted
+    # matrix-core counters: per dispatch, joined with the same run's kernel trace for the duration
+    mfma = {}
+    gemm_check = None
+    if mfma_dir:
+        crows = _counter_rows(mfma_dir)
+        trows = {int(r["Dispatch_Id"]): r for r in rows(mfma_dir, "kernel_trace.csv")}
+        stream = []
+        for did in sorted(crows):
+            kname, grid, vals = crows[did]
+            if did not in trows or any(c not in vals for c in MFMA_COUNTERS):
+                continue
+            t = trows[did]
+            dur = int(t["End_Timestamp"]) - int(t["Start_Timestamp"])
+            stream.append(((*kernel_identity(kname), grid), (vals, dur, kname)))
+        for ckey, (vals, dur, _) in resolve(stream):
+            mfma.setdefault(ckey, []).append((vals, dur))
+        # the warm-up products (torch.mm of two 4096 x 4096 bf16 matrices) are a kernel of known
+        # work: their counter-derived busy fraction against their timed flop rate checks the formula
+        g = [(vals, dur) for (_, (vals, dur, kname)) in stream if kname.startswith("Cijk_") and dur > 0]
+        if g:
+            busy = statistics.median(mfma_utilisation(v["SQ_VALU_MFMA_BUSY_CYCLES"], v["GRBM_GUI_ACTIVE"], d,
+                                                      n_cu)[0] for v, d in g)
+            clk = statistics.median(mfma_utilisation(v["SQ_VALU_MFMA_BUSY_CYCLES"], v["GRBM_GUI_ACTIVE"], d,
+                                                     n_cu)[1] for v, d in g)
+            tfl = statistics.median(2 * 4096 ** 3 / (d * 1e-9) / 1e12 for v, d in g)
+            gemm_check = {"kernel": "torch.mm 4096^3 bf16 (warm-up)", "dispatches": len(g), "mfma_busy": busy,
+                          "clock_GHz": clk, "TFLOPs": tfl,
+                          "TFLOPs_implied_by_busy": busy * roofline.MFMA_PEAK_TFLOPS["bf16"] * clk / 2.4}
     digest = source_digest()
     summary = {"source_digest": digest, "fetch_scale": counters[("FETCH_SIZE", "scale")],
-               "write_scale": counters[("WRITE_SIZE", "scale")], "kernels": {}}
+               "write_scale": counters[("WRITE_SIZE", "scale")], "n_cu": n_cu, "mfma_counter_check": gemm_check,
+               "kernels": {}}
     os.makedirs(dest, exist_ok=True)
     for ckey in sorted(info):
         key, (_, wname, algo, algo_unit) = info[ckey]
@@ -622,6 +726,13 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
         elif algo_unit == "flops":
             ent["algorithmic_flops"] = algo
             ent["achieved_TFLOPs_at_mean"] = algo / (ent["mean_us"] * 1e-6) / 1e12
+        ent["mfma_busy"] = ent["clock_GHz"] = None
+        if mfma.get(ckey):
+            util = [mfma_utilisation(v["SQ_VALU_MFMA_BUSY_CYCLES"], v["GRBM_GUI_ACTIVE"], d, n_cu) for v, d in mfma[ckey]]
+            ent["mfma_busy"] = statistics.median(u[0] for u in util)
+            ent["clock_GHz"] = statistics.median(u[1] for u in util)
+            ent["mfma_counters_median"] = {c: statistics.median(v[c] for v, _ in mfma[ckey]) for c in MFMA_COUNTERS}
+            ent["mfma_run_duration_us_median"] = statistics.median(d for _, d in mfma[ckey]) * 1e-3
         summary["kernels"][ckey] = ent
         fname = os.path.join(dest, f"{key[0]}__{wname}.txt")
         with open(fname, "w") as f:
@@ -629,6 +740,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
             f.write("commands (run from the repository root on one MI355X; <out> = output directory):\n")
             for k in ("trace", "fetch", "write"):
                 f.write(f"  {PROFILE_COMMANDS[k]}\n")
+            if mfma_dir:
+                f.write(f"  {PROFILE_COMMANDS['mfma']}\n")
             f.write(f"kernel source digest: {digest}\n\n")
             f.write(f"kernel-trace: {len(d)} launches, mean {ent['mean_us']:.2f} us, median {ent['median_us']:.2f} us, "
                     f"min {ent['min_us']:.2f} us, max {ent['max_us']:.2f} us\n")
@@ -649,6 +762,17 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest):
                 pk, pname = (5000.0, "5.0 PFLOP/s fp8") if "fp8" in key[0] else (2500.0, "2.5 PFLOP/s bf16")
                 f.write(f"flops of the visible pairs: {algo:.4e} -> {ent['achieved_TFLOPs_at_mean']:.0f} TFLOP/s at "
                         f"the mean duration ({ent['achieved_TFLOPs_at_mean'] / pk * 100:.1f}% of {pname})\n")
+            if ent["mfma_busy"] is not None:
+                mc = ent["mfma_counters_median"]
+                f.write(f"matrix cores busy: {ent['mfma_busy'] * 100:.1f}% of SIMD cycles at {ent['clock_GHz']:.2f} GHz "
+                        f"(median over {len(mfma[ckey])} dispatches: SQ_VALU_MFMA_BUSY_CYCLES {mc['SQ_VALU_MFMA_BUSY_CYCLES']:.4g}"
+                        f", GRBM_GUI_ACTIVE {mc['GRBM_GUI_ACTIVE']:.4g}, SQ_BUSY_CYCLES {mc['SQ_BUSY_CYCLES']:.4g}, "
+                        f"{ent['mfma_run_duration_us_median']:.1f} us in that run; busy = MFMA cycles / "
+                        f"(4 SIMDs x {n_cu} CUs x GRBM_GUI_ACTIVE / 8 XCDs))\n")
+                if gemm_check:
+                    f.write(f"counter check on the same run's torch.mm 4096^3 bf16: busy {gemm_check['mfma_busy'] * 100:.1f}% "
+                            f"at {gemm_check['clock_GHz']:.2f} GHz implies {gemm_check['TFLOPs_implied_by_busy']:.0f} "
+                            f"TFLOP/s; timed {gemm_check['TFLOPs']:.0f} TFLOP/s\n")
     json.dump(summary, open(os.path.join(dest, "counters.json"), "w"), indent=1)
     with open(os.path.join(dest, "all_kernels__bench_default_run.txt"), "w") as f:
         f.write(f"rocprofv3 --stats kernel summary of: {PROFILE_COMMANDS['trace']}\n")
@@ -690,11 +814,15 @@ def main(argv=None):
                     "K eager launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB read + 1 GiB write elementwise kernel (counter calibration)")
-    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="turn rocprofv3 output directories into profiles/ summaries and exit")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="TRACE_DIR FETCH_DIR WRITE_DIR [MFMA_DIR]: turn rocprofv3 output directories into "
+                         "profiles/ summaries and exit")
     args = ap.parse_args(argv)
     if args.summarize:
-        s = summarize_profiles(*args.summarize, dest=os.path.join(ROOT, "profiles"))
+        if len(args.summarize) not in (3, 4):
+            ap.error("--summarize takes 3 or 4 directories")
+        s = summarize_profiles(*args.summarize[:3], dest=os.path.join(ROOT, "profiles"),
+                               mfma_dir=args.summarize[3] if len(args.summarize) == 4 else None)
         print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk in ("mean_us", "hbm_bytes_per_launch")}
                           for k, v in s["kernels"].items()}, indent=1))
         return 0
@@ -726,11 +854,26 @@ def main(argv=None):
         wl = {**inputs.DECODE_WORKLOADS, **inputs.QUANT_DECODE_WORKLOADS}[name]
         return bench_decode(wl, steps, warmup, use_graph, args.n_split)
 
-    main_res = run(args.workload, args.steps, args.warmup)
+    ceilings = None
+    if not args.no_ceilings:
+        print("[bench] measured ceilings", file=sys.stderr, flush=True)
+        ceilings = measure_ceilings()
+
+    def vs_ceiling(res):
+        # decode: the step's and the split kernel's bytes/s as a share of the read-only stream in this run
+        if ceilings and res.get("unit") == "GB/s":
+            res["pct_of_measured_read_ceiling"] = 100.0 * res["value"] / ceilings["stream_read_GBps"]
+            res["roofline"]["frac_of_measured_read_ceiling"] = res["roofline"]["achieved"] / ceilings[
+                "stream_read_GBps"]
+        if ceilings and res.get("unit") == "TFLOP/s" and res.get("dtype") == "bf16":
+            res["pct_of_measured_gemm"] = 100.0 * res["value"] / ceilings["bf16_gemm_TFLOPs"]
+        return res
+
+    main_res = vs_ceiling(run(args.workload, args.steps, args.warmup))
     others = {}
     if not args.only_main:
         for name in run_order(args.workload)[1:]:
-            others[name] = run(name, max(5, min(args.steps, 20)), 2)
+            others[name] = vs_ceiling(run(name, max(5, min(args.steps, 20)), 2))
             torch.cuda.empty_cache()
 
     line = {
@@ -754,9 +897,8 @@ def main(argv=None):
         "main": {k: v for k, v in main_res.items() if k not in ("config", "roofline")},
         "workloads": others,
     }
-    if not args.no_ceilings:
-        print("[bench] measured ceilings", file=sys.stderr, flush=True)
-        line["measured_ceilings"] = measure_ceilings()
+    if ceilings:
+        line["measured_ceilings"] = ceilings
     if not args.no_cpu_baseline and args.workload in inputs.DECODE_WORKLOADS:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inputs.DECODE_WORKLOADS[args.workload])

@@ -348,6 +348,17 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
                         const float* q_descale, const float* k_descale, const float* v_descale,
                         const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, hipStream_t stream);
 
+/* -------------------------------------------------------- measurement --
+ * Read-only HBM stream: reads every byte of `buf` once (128-bit non-temporal
+ * loads, the decode kernels' loads) and writes nothing but, in a practically
+ * impossible case, one word to `sink`.  Its rate is the measured read
+ * ceiling that decode's achieved bandwidth (KV bytes per step, the
+ * "bandwidth argument" of "Multi-query attention") is compared with beside
+ * the vendor peak.  bytes: a nonzero multiple of 16; buf 16-byte aligned;
+ * sink: one caller-owned uint32 of device memory (contents unspecified
+ * afterwards). */
+gqa_status gqa_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* ------------------------------------------------------------- errors --- */
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status s);

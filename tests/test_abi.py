@@ -344,3 +344,12 @@ def test_noalloc_scratch_limit_is_checked_on_the_host(lib):
     assert lib.attn_decode_noalloc(ctypes.byref(dd(flags=2)), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
                                    ALIGNED, None) == 7
     assert lib.gqa_last_hip_error().decode() == ""
+
+
+def test_stream_read_argument_errors(lib):
+    assert lib.gqa_stream_read(None, 1024, ALIGNED, None) == 1
+    assert lib.gqa_stream_read(ALIGNED, 1024, None, None) == 1
+    assert lib.gqa_stream_read(ALIGNED, 0, ALIGNED, None) == 2
+    assert lib.gqa_stream_read(ALIGNED, 1000, ALIGNED, None) == 2
+    assert lib.gqa_stream_read(MISALIGNED, 1024, ALIGNED, None) == 4
+    assert lib.gqa_stream_read(ALIGNED, 1024, ALIGNED + 2, None) == 4

@@ -310,3 +310,16 @@ def test_runs_on_a_side_stream():
     s.synchronize()
     pu.sync()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 3 * (1 << 20) + 48, 1 << 28])
+def test_stream_read_runs_and_writes_nothing_else(nbytes):
+    """The read-only stream (the measured HBM ceiling) reads any multiple of
+    16 bytes, leaves the buffer unchanged and touches nothing but its sink."""
+    buf = torch.arange(nbytes // 4, dtype=torch.int32, device=DEV)
+    before = buf.clone()
+    sink = torch.zeros(2, dtype=torch.int32, device=DEV)
+    binding.gqa_stream_read(buf, sink[:1])
+    pu.sync()
+    assert torch.equal(buf, before)
+    assert int(sink[1]) == 0

@@ -26,7 +26,7 @@ EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decod
             "attn_decode_combine", "attn_decode_paged_num_splits", "attn_decode_paged_workspace_bytes",
             "attn_decode_paged", "attn_decode_mla_num_splits", "attn_decode_mla_workspace_bytes",
             "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "attn_prefill", "gqa_status_string", "gqa_last_hip_error",
-            "attn_decode_noalloc", "attn_decode_noalloc_max_scratch_bytes")
+            "attn_decode_noalloc", "attn_decode_noalloc_max_scratch_bytes", "gqa_stream_read")
 
 
 class GqaError(RuntimeError):
@@ -108,6 +108,7 @@ def load_library(path=LIB_PATH):
     lib.attn_prefill.argtypes = [ad, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_prefill_causal.restype = ctypes.c_int
+    lib.gqa_stream_read.argtypes, lib.gqa_stream_read.restype = [vp, sz, vp, vp], ctypes.c_int
     lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [ctypes.c_int], cp
     lib.gqa_last_hip_error.argtypes, lib.gqa_last_hip_error.restype = [], cp
     _lib = lib
@@ -549,3 +550,10 @@ def prepare_prefill(q, k, v, scale, out, causal=True, kv_lens=None, mask=None, q
                                            ctypes.c_float(scale), _ptr(out)), stream, out)
     call._keep = (desc,)
     return call
+
+
+def gqa_stream_read(buf, sink, stream=None):
+    """Read every byte of `buf` once on the GPU (the measured HBM read
+    ceiling); `sink` is a one-element int32/uint32 device tensor."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().gqa_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))

@@ -593,6 +593,18 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
   return GQA_OK;
 }
 
+gqa_status gqa_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return GQA_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return GQA_ERR_SHAPE;
+  if (misaligned(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return GQA_ERR_ALIGN;
+  const hipError_t e = launch_stream_read(buf, bytes, sink, device_compute_units(), stream);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return GQA_ERR_HIP;
+  }
+  return GQA_OK;
+}
+
 const char* gqa_status_string(gqa_status s) {
   switch (s) {
     case GQA_OK: return "GQA_OK";

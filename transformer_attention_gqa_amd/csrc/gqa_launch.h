@@ -81,4 +81,8 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void*
                               const uint8_t* mask, const float* q_descale, const float* k_descale,
                               const float* v_descale, hipStream_t stream);
 
+// Read-only stream over `bytes` (a multiple of 16) at `buf`: the measured HBM
+// read ceiling.  One workgroup of 512 threads per compute unit.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int n_cu, hipStream_t stream);
+
 }  // namespace gqa
