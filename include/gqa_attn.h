@@ -329,12 +329,15 @@ gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const v
  * dtype GQA_FP8_E4M3 (the FP8 mode listed for FlashAttention-3 in "Flash
  * Attention 3 Features"): q/k/v hold OCP E4M3 codes (same shapes, one byte
  * per element) and the values are code * descale with float32 factors
- *   q_descale [B, h_q], k_descale [B, n_kv], v_descale [B, n_kv] (device);
- * d_h must be 128.  Both products run on fp8 matrix cores: the scores from
+ *   q_descale [B, h_q], k_descale [B, n_kv], v_descale [B, n_kv] (device),
+ *   finite and >= 0 (an all-zero head quantised by absmax has descale 0;
+ *   its scores are then 0, i.e. equal weights);
+ * d_h = 64 or 128.  Both products run on fp8 matrix cores: the scores from
  * the codes (the descale factors fold into the score scale and the output),
- * and the weighted sum with the softmax weights rounded to E4M3 (relative
- * error up to 2^-4 per weight, normal range), float32 accumulation, out
- * bf16.
+ * and the weighted sum with each softmax weight split into two E4M3 terms,
+ * hi = e4m3(p) and lo = e4m3(p - hi), two products per d tile (relative
+ * error at most 2^-8 per weight, 2^-10 absolute for the smallest), float32
+ * accumulation, out bf16.
  * Key tiles past every row's visible prefix are skipped, and a wave skips
  * the products of a tile the dense mask hides from all of its rows.
  */

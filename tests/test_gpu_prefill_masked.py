@@ -180,23 +180,33 @@ def test_fp8_zero_descale(which):
         assert torch.count_nonzero(out[1, :, 0:4]) == 0
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("h_q,n_kv", [(8, 8), (8, 4), (8, 2), (16, 2), (6, 2)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_head_chunks_and_lengths(h_q, n_kv, causal):
-    """fp8 operands over every head-chunk size, key lengths 200, 1, 0 and 77
-    (NaN codes past each length)."""
-    inp = inputs.make_masked_prefill_inputs(wl(4, 200, 200, h_q, n_kv, 128, causal, seed=470 + h_q + n_kv,
+def test_fp8_head_chunks_and_lengths(h_q, n_kv, causal, d):
+    """fp8 operands over every head-chunk size and both head dims, key
+    lengths 200, 1, 0 and 77 (NaN codes past each length)."""
+    inp = inputs.make_masked_prefill_inputs(wl(4, 200, 200, h_q, n_kv, d, causal, seed=470 + h_q + n_kv + d,
                                                dtype="fp8"), device=DEV, kv_lens=[200, 1, 0, 77],
                                             poison_padding=True)
     out = check(inp)
     assert torch.count_nonzero(out[2]) == 0
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("kind", ["random", "docs"])
-def test_fp8_masks_and_key_counts(kind):
-    w = wl(2, 150, 300, 8, 2, 128, True, seed=480, mask=kind, doc_lens=(16, 80), dtype="fp8")
+def test_fp8_masks_and_key_counts(kind, d):
+    w = wl(2, 150, 300, 8, 2, d, True, seed=480 + d, mask=kind, doc_lens=(16, 80), dtype="fp8")
     m = inputs.draw_mask(kind, 2, 150, 300, 480, (16, 80)) if kind == "random" else None
     if kind == "docs":  # documents over the keys; the queries are the last 150 positions
         full = inputs.draw_mask("docs", 2, 300, 300, 480, (16, 80))
         m = full[:, 150:, :].contiguous()
     check(inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=[300, 222], mask=m))
+
+
+def test_fp8_head_dim_64_long_causal():
+    """fp8 at d = 64 over several row blocks and key tiles per workgroup (a
+    1,000-token causal prompt, GQA with 4 query heads per K/V head), every
+    output element against the oracle."""
+    w = wl(1, 1000, 1000, 8, 2, 64, True, seed=495, dtype="fp8")
+    check(inputs.make_masked_prefill_inputs(w, device=DEV))

@@ -571,7 +571,6 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
   const bool fp8 = d->dtype == GQA_FP8_E4M3;
   if (d->dtype != GQA_BF16 && !fp8) return GQA_ERR_DTYPE;
   if (!fp8 && (q_descale || k_descale || v_descale)) return GQA_ERR_DTYPE;
-  if (fp8 && d->d_h != 128) return GQA_ERR_SHAPE;
   if (!q || !k || !v || !out) return GQA_ERR_NULL;
   if (fp8 && (!q_descale || !k_descale || !v_descale)) return GQA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(mask)) return GQA_ERR_ALIGN;
@@ -582,7 +581,7 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
   if (bad_scale(scale)) return GQA_ERR_VALUE;
   const float sl2 = qk_scale_log2(scale);
   const hipError_t e =
-      fp8 ? launch_prefill_fp8(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->causal, kv_lens, mask,
+      fp8 ? launch_prefill_fp8(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal, kv_lens, mask,
                                q_descale, k_descale, v_descale, stream)
           : launch_prefill_masked(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal,
                                   kv_lens, mask, stream);

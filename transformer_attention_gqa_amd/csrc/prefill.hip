@@ -70,7 +70,7 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // then have no visible key at all (zero output).
 // F8: q, k, v are OCP e4m3 codes with one descale factor per (batch, head)
 // (the FP8 mode of FlashAttention-3, "Flash Attention 3 Features"); both
-// products run on v_mfma_f32_32x32x64_f8f6f4, d = 128 only.  The softmax
+// products run on v_mfma_f32_32x32x64_f8f6f4, d = 64 or 128.  The softmax
 // weights enter the second product as two e4m3 terms, p = hi + lo with hi =
 // e4m3(p) and lo = e4m3(p - hi) (two products per d tile), so each weight
 // carries a relative error of at most 2^-8 (2^-10 absolute for the smallest)
@@ -80,7 +80,7 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // (tile bitmaps, mask tiles, per-element masking) is compiled out.
 template <int D, int HC, bool GEN, bool F8 = false, bool MASK = false>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
-  static_assert(!F8 || (D == 128 && GEN), "the fp8 body serves d = 128 with general masks");
+  static_assert(!F8 || GEN, "the fp8 body serves general masks");
   constexpr int RB = kWaves / HC;  // 32-row blocks per head in one workgroup
   constexpr int BM = 32 * RB;    // query rows per workgroup
   constexpr int EB = F8 ? 1 : 2; // bytes per element
@@ -94,8 +94,13 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // two per 256-byte bank window, and rows r, r + 2 of a 4-row group go to
   // different row halves, so the score reads (16 rows, one chunk) and the
   // transposed V reads (16 rows x 2 chunks) hit 16 chunk positions
+  // (fp8 rows of 64 bytes, d = 64, four to a bank window: chunk position
+  // c ^ ((r >> 2) & 3) keeps the 16 rows of a score read and the row pairs of
+  // a transposed V read on distinct banks)
   auto sw = [](int r) {
-    if constexpr (F8) {
+    if constexpr (F8 && D == 64) {
+      return (r >> 2) & 3;
+    } else if constexpr (F8) {
       const int j = (r >> 1) & 7;
       return ((j & 1) << 2) | (j >> 1);
     } else {
@@ -221,8 +226,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // masked for valid query rows, so they contribute nothing.  With key
   // lengths the same holds at the length: rows at or past it are never read.
   constexpr int RPI = 64 / CH;                  // tile rows per wave instruction
-  constexpr int NINS = kBN / (RPI * kWaves);    // instructions per wave per tensor
-  static_assert(NINS * RPI * kWaves == kBN, "tile rows must split evenly over the waves");
+  // A tile of fewer than kWaves instructions per tensor (fp8 at d = 64: four
+  // of 16 rows) is loaded by half the waves for K and the other half for V.
+  constexpr bool SPLIT_KV = kBN / RPI < kWaves;
+  constexpr int NINS = SPLIT_KV ? 1 : kBN / (RPI * kWaves);  // instructions per wave per tensor
+  static_assert(SPLIT_KV ? 2 * kBN == RPI * kWaves : NINS * RPI * kWaves == kBN,
+                "tile rows must split evenly over the waves");
   const int dma_r = lane / CH;                  // row within an instruction's rows
   const int dma_c = (lane % CH);                // physical chunk of this lane's LDS slot
   // Per-lane element offsets inside a tile, computed once; a full tile then
@@ -231,14 +240,34 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // (a vector, not an array: a local array captured by the lambdas below
   // makes hipcc's host pass drop this kernel's launch stub)
   static_assert(NINS <= 4, "per-lane DMA offsets are kept in a u32x4");
+  // first tile row of instruction u of this wave (split: the wave's row
+  // block of its tensor)
+  auto ins_row0 = [&](int u) { return SPLIT_KV ? (wave % (kWaves / 2)) * RPI : (u * kWaves + wave) * RPI; };
   u32x4 dma_off = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < NINS; ++u) {
-    const int r = (u * kWaves + wave) * RPI + dma_r;
+    const int r = ins_row0(u) + dma_r;
     dma_off[u] = (uint32_t)(r * kv_row_bytes + (dma_c ^ sw(r)) * 16);
   }
   auto dma_tile = [&](int j, char* kdst, char* vdst) {
     const int key0 = j * kBN;
+    if constexpr (SPLIT_KV) {
+      // waves 0 .. kWaves/2 - 1 load K, the others V
+      const bool is_k = wave < kWaves / 2;
+      const char* base = is_k ? kbase : vbase;
+      char* dst = is_k ? kdst : vdst;
+      const int r0 = ins_row0(0);
+      if (key0 + kBN <= kv_n) {
+        __builtin_amdgcn_global_load_lds(base + (size_t)key0 * kv_row_bytes + dma_off[0], (lds_void*)(dst + r0 * ROWB),
+                                         16, 0, 0);
+      } else {
+        const int r = r0 + dma_r;
+        const int key = min(key0 + r, kv_n - 1);
+        const size_t off = (size_t)key * kv_row_bytes + (dma_c ^ sw(r)) * 16;
+        __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + r0 * ROWB), 16, 0, 0);
+      }
+      return;
+    }
     if (key0 + kBN <= kv_n) {
       const char* kt = kbase + (size_t)key0 * kv_row_bytes;
       const char* vt = vbase + (size_t)key0 * kv_row_bytes;
@@ -673,9 +702,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_masked_kernel(Pref
   prefill_body<D, HC, true, false, MASK>(a);
 }
 
-template <int HC, bool MASK>
+template <int D, int HC, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_fp8_kernel(PrefillArgs a) {
-  prefill_body<128, HC, true, true, MASK>(a);
+  prefill_body<D, HC, true, true, MASK>(a);
 }
 
 static int gcd_int(int x, int y) {
@@ -769,7 +798,7 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
 }
 
 hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
-                              int S_q, int S_k, int h_q, int n_kv, int causal, const int32_t* kv_lens,
+                              int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                               const uint8_t* mask, const float* q_descale, const float* k_descale,
                               const float* v_descale, hipStream_t stream) {
   const int HC = gcd_int(h_q / n_kv, kWaves);
@@ -783,15 +812,22 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void*
   a.v_descale = v_descale;
   if (mask) a.grp_block = kMaskGroupBlock;
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
-#define GQA_LAUNCH_FP8(HH)                                                                              \
+#define GQA_LAUNCH_FP8(DD, HH)                                                                          \
   do {                                                                                                  \
-    if (mask) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<HH, true>), grid, block, 0, stream, a);        \
-    else hipLaunchKernelGGL((gqa_prefill_fp8_kernel<HH, false>), grid, block, 0, stream, a);            \
+    if (mask) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<DD, HH, true>), grid, block, 0, stream, a);    \
+    else hipLaunchKernelGGL((gqa_prefill_fp8_kernel<DD, HH, false>), grid, block, 0, stream, a);        \
   } while (0)
-  if (HC == 8) GQA_LAUNCH_FP8(8);
-  else if (HC == 4) GQA_LAUNCH_FP8(4);
-  else if (HC == 2) GQA_LAUNCH_FP8(2);
-  else GQA_LAUNCH_FP8(1);
+  if (D == 128) {
+    if (HC == 8) GQA_LAUNCH_FP8(128, 8);
+    else if (HC == 4) GQA_LAUNCH_FP8(128, 4);
+    else if (HC == 2) GQA_LAUNCH_FP8(128, 2);
+    else GQA_LAUNCH_FP8(128, 1);
+  } else {
+    if (HC == 8) GQA_LAUNCH_FP8(64, 8);
+    else if (HC == 4) GQA_LAUNCH_FP8(64, 4);
+    else if (HC == 2) GQA_LAUNCH_FP8(64, 2);
+    else GQA_LAUNCH_FP8(64, 1);
+  }
 #undef GQA_LAUNCH_FP8
   return hipGetLastError();
 }
