@@ -272,6 +272,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // Stage the tile whose loads were issued last into the wave's LDS slab as
   // bf16 (quantized codes are converted exactly) and take over its scales.
   float kscur[2][4], vscur[2][4];
+  // int4 codes staged as 136 + code, the offset removed in the products (one
+  // 16-head block only: with two the extra registers spill)
+  constexpr bool BIAS4 = KVF == kKvInt4 && HB == 1;
   auto stage = [&](int half = 0) {
     if constexpr (QUANT) {
 #pragma unroll
@@ -321,8 +324,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         const int sw = swz<CH>(r);
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[half][u][h]));
-          lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(vreg[half][u][h]));
+          if constexpr (BIAS4) {
+            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased(kreg[half][u][h]));
+            lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased(vreg[half][u][h]));
+          } else {
+            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[half][u][h]));
+            lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(vreg[half][u][h]));
+          }
         }
       } else {
         const int pc = ld_chunk ^ swz<CH>(r);
@@ -370,6 +378,31 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     store_q(qc);
     if (threadIdx.x == 0) s_next_tile = 2 * NW;
     __syncthreads();  // sq and the tile counter ready
+
+    // int4 caches are staged as 136 + code (see i4x8_to_bf16x8_biased).  For
+    // the scores, q . (k + 136) - 136 sum(q) = q . k: every score
+    // accumulator starts at -136 sum(q) of its head, formed by one product of
+    // the head's query row with a row of ones (lane: head r16 of block hb).
+    // For the weighted sum, sum_t p_t (v_t + 136) - 136 sum_t p_t = sum_t
+    // p_t v_t: one extra product with a ones row carries sum_t p_t (the bf16
+    // weights the products use) next to O, and the segment's end removes it.
+    float kbias[BIAS4 ? HB : 1];
+    f32x4 osum[BIAS4 ? HB : 1];  // row 0 (lane r16, register 0): sum of the weights of head r16
+    u32x4 ones_row0 = {0u, 0u, 0u, 0u};
+    if constexpr (BIAS4) {
+      const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+      if (r16 == 0) ones_row0 = ones;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int qrow = 16 * hb + r16;
+        f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          qs = mfma16(ones, lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ swz<CH>(qrow)) << 4)), qs);
+        kbias[hb] = -kInt4Bias * qs[0];
+        osum[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
 
     // ---- running state (per lane: head r16 of every head block; head l32 in the 32x32 shape)
     f32x4 o[M32 ? 1 : HB][M32 ? 1 : NT];
@@ -467,6 +500,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             // B operand of S^T = K Q^T: lane holds Q[head 16hb + r16][32kk + 8q4 .. +7]
             const int qrow = 16 * hb + r16;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BIAS4) acc = f32x4{kbias[hb], kbias[hb], kbias[hb], kbias[hb]};
   #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
               acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ swz<CH>(qrow)) << 4)), acc);
@@ -532,9 +566,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         }
         if (__builtin_amdgcn_ballot_w64(any_grow)) {
   #pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
+          for (int hb = 0; hb < HB; ++hb) {
   #pragma unroll
             for (int n = 0; n < NT; ++n) o[hb][n] *= alpha[hb];
+            if constexpr (BIAS4) osum[hb] *= alpha[hb];
+          }
         }
         // ---- O^T += V^T P^T: one 16-wide d tile of V at a time, shared by all head blocks
   #pragma unroll
@@ -548,6 +584,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           const u32x4 vf = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
+        }
+        if constexpr (BIAS4) {
+  #pragma unroll
+          for (int hb = 0; hb < HB; ++hb) osum[hb] = mfma16(ones_row0, pf[hb], osum[hb]);
         }
       }
       if constexpr (SPLIT2) {
@@ -588,6 +628,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         float lt = wave_sum_xor(l[hb], 16);
         lt = wave_sum_xor(lt, 32);
         l[hb] = lt;
+      }
+      if constexpr (BIAS4) {
+        // remove 136 sum_t p_t (held by lane r16 of each head block)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const float c = kInt4Bias * __shfl(osum[hb][0], r16, 64);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) o[hb][n] -= c;
+        }
       }
       // O^T[d = 16n + 4q4 + i][head r16] -> ow[head][d] (float32), reusing the wave slab
 #pragma unroll

@@ -114,6 +114,27 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
   return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 
+// Eight signed int4 codes (one dword, code i in bits 4i .. 4i+3, two's
+// complement) -> eight bf16 values 136 + code, exact, formed from the bit
+// patterns alone: code ^ 8 is the offset-binary nibble u = code + 8 in
+// 0..15, and a bf16 whose exponent field is that of 128 with u in its low
+// mantissa bits is 128 + u (the mantissa step at 128 is 1).  Codes 2k and
+// 2k+1 are byte k; or-ing the byte with a copy shifted up by 12 puts code
+// 2k+1 in bits 16..19, the low mantissa bits of the upper bf16, so each pair
+// costs a bit-field extract, a shift-or and an and-or.  The caller removes
+// the 136.
+constexpr float kInt4Bias = 136.0f;
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8_biased(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = (u >> (8 * k)) & 0xFFu;
+    r[k] = ((x | (x << 12)) & 0x000F000Fu) | 0x43004300u;
+  }
+  return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
