@@ -153,6 +153,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char sq[HPC * D * 2];  // the segment's query rows, bf16, swizzled
   __shared__ float sm_ml[NW][HPC][2];
   __shared__ int s_next_tile;  // next unclaimed tile of the current segment
+  // quantized caches: the staged tile's K scales (entries 0..31) and V scales
+  // (32..63), one per row, in each wave's own slot
+  __shared__ __attribute__((aligned(16))) float ssc[QUANT ? NW : 1][64];
 
   const int W = gridDim.x;
   const int w = blockIdx.x;
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // staged and computed, the next tile's same half is already loading, so
   // two halves are always in flight.  The LDS slab still holds 32 tokens.
   u32x4 kreg[NH][NLD], vreg[NH][NLD];
-  float ksc[NH][2][4], vsc[NH][2][4];
+  float ksl[NH], vsl[NH];  // K and V scale of row lane % 32 of the tile in flight
 
   // loads of tile `tile` of segment s into kreg/vreg (and its K/V scales).
   // The tile's first row is wave-uniform: it becomes the base of a buffer
@@ -218,19 +221,22 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       vreg[half][u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
     }
     if constexpr (QUANT) {
-      // lane (q4, .) needs the scales of rows 16h + 4q4 + i; rows past the end
+      // one K and one V scale per lane (row lane % 32); rows past the end
       // read zero, and their scores are masked anyway
       const auto rks = make_rsrc(a.k_scale + row0, nvalid * 4);
       const auto rvs = make_rsrc(a.v_scale + row0, nvalid * 4);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ksc[half][h][i] = buffer_load_f32(rks, 16 * q4 + 4 * (16 * h + i));
-          vsc[half][h][i] = buffer_load_f32(rvs, 16 * q4 + 4 * (16 * h + i));
-        }
+      ksl[half] = buffer_load_f32(rks, 4 * (lane & 31));
+      vsl[half] = buffer_load_f32(rvs, 4 * (lane & 31));
     }
   };
+  // int4 caches with one 16-head block are staged as 136 + code, the offset
+  // removed in the products, and with the codes of each 8-element chunk in
+  // the order 0 2 4 6 1 3 5 7 (each bf16 pair then comes from one byte
+  // permute, see i4x8_to_bf16x8_biased_eo).  Q is staged in the same order,
+  // which leaves every score unchanged, and the rows of O come out in it and
+  // are put back in order at the segment end.  (With two head blocks the
+  // extra registers spill, so that kernel converts through float.)
+  constexpr bool BIAS4 = KVF == kKvInt4 && HB == 1;
   struct QRows {
     u32x4 v[QCH];
   };
@@ -252,7 +258,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     for (int i = 0; i < QCH; ++i) {
       const int e = threadIdx.x + i * NW * 64;
       const int hl = e / CH, c = e % CH;
-      if (e < HPC * CH) lds_store(sq + hl * (2 * D) + ((c ^ swz<CH>(hl)) << 4), r.v[i]);
+      u32x4 x = r.v[i];
+      if constexpr (BIAS4) x = bf16x8_even_odd(x);
+      if (e < HPC * CH) lds_store(sq + hl * (2 * D) + ((c ^ swz<CH>(hl)) << 4), x);
     }
   };
 
@@ -270,22 +278,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   };
 
   // Stage the tile whose loads were issued last into the wave's LDS slab as
-  // bf16 (quantized codes are converted exactly) and take over its scales.
-  float kscur[2][4], vscur[2][4];
-  // int4 codes staged as 136 + code, the offset removed in the products (one
-  // 16-head block only: with two the extra registers spill)
-  constexpr bool BIAS4 = KVF == kKvInt4 && HB == 1;
+  // bf16 (quantized codes are converted exactly) and its scales into the
+  // wave's scale slot.
   auto stage = [&](int half = 0) {
-    if constexpr (QUANT) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kscur[h][i] = ksc[half][h][i];
-          vscur[h][i] = vsc[half][h][i];
-        }
-    }
     wave_lds_fence();
+    if constexpr (QUANT) ssc[wave][lane] = lane < 32 ? ksl[half] : vsl[half];
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int r = u * RPL + ld_row;
@@ -325,8 +322,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           if constexpr (BIAS4) {
-            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased(kreg[half][u][h]));
-            lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased(vreg[half][u][h]));
+            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(kreg[half][u][h]));
+            lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(vreg[half][u][h]));
           } else {
             lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[half][u][h]));
             lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(vreg[half][u][h]));
@@ -516,6 +513,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         u32x4 pf[HB];
         bool any_grow = false;
         float alpha[HB];
+        f32x4 kscur[2], vscur[2];  // scales of rows 16h + 4q4 + i (unused for bf16)
+        if constexpr (QUANT) {
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            kscur[h] = lds_load<f32x4>(&ssc[wave][16 * h + 4 * q4]);
+            vscur[h] = lds_load<f32x4>(&ssc[wave][32 + 16 * h + 4 * q4]);
+          }
+        }
   #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
           float sv[2][4];
@@ -642,7 +647,16 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) lds_store(ow + ow_idx(hb * 16 + r16, 16 * n + 4 * q4), o[hb][n]);
+        for (int n = 0; n < NT; ++n) {
+          if constexpr (BIAS4) {
+            // staged column 16n + 4q4 + i holds d = 16n + 8(q4/2) + 2i + q4%2
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              ow[ow_idx(hb * 16 + r16, 16 * n + 8 * (q4 >> 1) + 2 * i + (q4 & 1))] = o[hb][n][i];
+          } else {
+            lds_store(ow + ow_idx(hb * 16 + r16, 16 * n + 4 * q4), o[hb][n]);
+          }
+        }
         if (q4 == 0) {
           sm_ml[wave][hb * 16 + r16][0] = m[hb];
           sm_ml[wave][hb * 16 + r16][1] = l[hb];

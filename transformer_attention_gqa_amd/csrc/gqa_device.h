@@ -135,6 +135,29 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8_biased(uint32_t w) {
   return r;
 }
 
+// The same values in the order 0 2 4 6 1 3 5 7 (bf16 position j holds code
+// pi(j)): with the even codes' nibbles in the bytes of one word and the odd
+// ones' in another, each output dword is a byte permute of one of them with
+// the bytes 0x43, so eight codes cost two masks, a shift, an xor and four
+// permutes.  v_perm_b32 picks result byte k by selector byte k from the
+// eight bytes of {first operand : second operand}, 0..3 being the second.
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8_biased_eo(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t ev = u & 0x0F0F0F0Fu;         // offset nibbles of codes 0 2 4 6
+  const uint32_t od = (u >> 4) & 0x0F0F0F0Fu;  // codes 1 3 5 7
+  constexpr uint32_t k43 = 0x43434343u;
+  return u32x4{__builtin_amdgcn_perm(k43, ev, 0x04010400u), __builtin_amdgcn_perm(k43, ev, 0x04030402u),
+               __builtin_amdgcn_perm(k43, od, 0x04010400u), __builtin_amdgcn_perm(k43, od, 0x04030402u)};
+}
+
+// Eight bf16 values (one 16-byte chunk, element j in the low half of dword
+// j/2 when j is even, the high half when odd) put in the order 0 2 4 6 1 3 5
+// 7 used by i4x8_to_bf16x8_biased_eo.
+__device__ __forceinline__ u32x4 bf16x8_even_odd(const u32x4& x) {
+  return u32x4{__builtin_amdgcn_perm(x[1], x[0], 0x05040100u), __builtin_amdgcn_perm(x[3], x[2], 0x05040100u),
+               __builtin_amdgcn_perm(x[1], x[0], 0x07060302u), __builtin_amdgcn_perm(x[3], x[2], 0x07060302u)};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
