@@ -141,6 +141,20 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   constexpr bool SPLIT2 = KVF == kKvInt4 && HB == 1;
   constexpr int NH = SPLIT2 ? 2 : 1;  // register halves
   constexpr int TT = NH * kTile;      // tokens per scheduled tile
+  // int4 caches with one 16-head block are converted to bf16 136 + code, the
+  // offset removed in the products, with the codes of each 8-element chunk
+  // in the order 0 2 4 6 1 3 5 7 (each bf16 pair then comes from one byte
+  // permute, see i4x8_to_bf16x8_biased_eo).  Q is staged in the same order,
+  // which leaves every score unchanged, and the rows of O come out in it and
+  // are put back in order at the segment end.  (With two head blocks the
+  // extra registers spill, so that kernel converts through float.)
+  constexpr bool BIAS4 = KVF == kKvInt4 && HB == 1;
+  // With d = 128 such a kernel also skips the LDS for K: lane (q4, r16)
+  // loads the 16 bytes (32 codes) q4 of token row r16 of each 16-token half,
+  // exactly the codes of its score-product operand when k-slot (q4, j) of
+  // k-step kk stands for d = 32 q4 + 8 kk + j (and Q is read to match), so
+  // K goes from the load registers through the conversion into the product.
+  constexpr bool KDIR = BIAS4 && D == 128;
   // 32 heads of a bf16 cache: one 32x32 score tile per 32 tokens on
   // v_mfma_f32_32x32x16_bf16 (the same shape as the prefill kernel with heads
   // in place of query rows); otherwise HB blocks of 16 heads on 16x16x32.
@@ -207,6 +221,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // the end read as zero without a memory access (a cache tail may hold NaN)
   // and each load needs only a 32-bit lane offset.
   const unsigned lane_off = ld_row * ROWB + ld_chunk * 16;
+  const unsigned k_lane_off = KDIR ? r16 * ROWB + q4 * 16 : lane_off;  // (RPL = 16 rows per load then)
+  static_assert(!KDIR || (RPL == 16 && NLD == 2), "direct K assumes 16 rows of 64 bytes per load");
   // (a half past the segment's end gets an empty range: its loads return
   // zeros without a memory access, so every path issues the same loads)
   auto issue_loads = [&](Segment& s, int tile, int half = 0) {
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + row0 * ROWB, nvalid * ROWB);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      kreg[half][u] = buffer_load_x4_nt(rk, lane_off + u * RPL * ROWB);
+      kreg[half][u] = buffer_load_x4_nt(rk, k_lane_off + u * RPL * ROWB);
       vreg[half][u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
     }
     if constexpr (QUANT) {
@@ -229,14 +245,6 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       vsl[half] = buffer_load_f32(rvs, 4 * (lane & 31));
     }
   };
-  // int4 caches with one 16-head block are staged as 136 + code, the offset
-  // removed in the products, and with the codes of each 8-element chunk in
-  // the order 0 2 4 6 1 3 5 7 (each bf16 pair then comes from one byte
-  // permute, see i4x8_to_bf16x8_biased_eo).  Q is staged in the same order,
-  // which leaves every score unchanged, and the rows of O come out in it and
-  // are put back in order at the segment end.  (With two head blocks the
-  // extra registers spill, so that kernel converts through float.)
-  constexpr bool BIAS4 = KVF == kKvInt4 && HB == 1;
   struct QRows {
     u32x4 v[QCH];
   };
@@ -280,9 +288,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // Stage the tile whose loads were issued last into the wave's LDS slab as
   // bf16 (quantized codes are converted exactly) and its scales into the
   // wave's scale slot.
+  u32x4 kcur[KDIR ? NLD : 1];  // direct K: the staged half's codes, 16-token half u in kcur[u]
   auto stage = [&](int half = 0) {
     wave_lds_fence();
     if constexpr (QUANT) ssc[wave][lane] = lane < 32 ? ksl[half] : vsl[half];
+    if constexpr (KDIR) {
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) kcur[u] = kreg[half][u];
+    }
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int r = u * RPL + ld_row;
@@ -322,7 +335,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           if constexpr (BIAS4) {
-            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(kreg[half][u][h]));
+            if constexpr (!KDIR)
+              lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(kreg[half][u][h]));
             lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(vreg[half][u][h]));
           } else {
             lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[half][u][h]));
@@ -399,6 +413,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         kbias[hb] = -kInt4Bias * qs[0];
         osum[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+    // direct K: the B operands of the score product for k-step kk, Q[head
+    // r16][32 q4 + 8 kk + pi(j)] = staged chunk 4 q4 + kk, held for the segment
+    u32x4 qreg[KDIR ? KK : 1];
+    if constexpr (KDIR) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qreg[kk] = lds_load<u32x4>(sq + r16 * (2 * D) + (((4 * q4 + kk) ^ swz<CH>(r16)) << 4));
     }
 
     // ---- running state (per lane: head r16 of every head block; head l32 in the 32x32 shape)
@@ -489,9 +510,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         for (int h = 0; h < 2; ++h) {
           const int row = 16 * h + r16;
           u32x4 kf[KK];
+          if constexpr (KDIR) {
   #pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ swz<CH>(row)) << 4));
+            for (int kk = 0; kk < KK; ++kk) kf[kk] = i4x8_to_bf16x8_biased_eo(kcur[h][kk]);
+          } else {
+  #pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+              kf[kk] = lds_load<u32x4>(kt + row * (2 * D) + (((4 * kk + q4) ^ swz<CH>(row)) << 4));
+          }
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
             // B operand of S^T = K Q^T: lane holds Q[head 16hb + r16][32kk + 8q4 .. +7]
@@ -500,7 +526,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             if constexpr (BIAS4) acc = f32x4{kbias[hb], kbias[hb], kbias[hb], kbias[hb]};
   #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-              acc = mfma16(kf[kk], lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ swz<CH>(qrow)) << 4)), acc);
+              acc = mfma16(kf[kk],
+                           KDIR ? qreg[kk]
+                                : lds_load<u32x4>(sq + qrow * (2 * D) + (((4 * kk + q4) ^ swz<CH>(qrow)) << 4)),
+                           acc);
             sc[h][hb] = acc;
           }
         }
