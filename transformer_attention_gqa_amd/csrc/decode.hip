@@ -155,6 +155,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // k-step kk stands for d = 32 q4 + 8 kk + j (and Q is read to match), so
   // K goes from the load registers through the conversion into the product.
   constexpr bool KDIR = BIAS4 && D == 128;
+  // V^T fragments of the weighted sum read ahead of the softmax (registers allowing)
+  constexpr int NPRE = HB == 1 ? 4 : 0;
   // 32 heads of a bf16 cache: one 32x32 score tile per 32 tokens on
   // v_mfma_f32_32x32x16_bf16 (the same shape as the prefill kernel with heads
   // in place of query rows); otherwise HB blocks of 16 heads on 16x16x32.
@@ -533,6 +535,20 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             sc[h][hb] = acc;
           }
         }
+        // V^T fragment n of the staged tile: lane holds V[token k-slot 8 q4 + j][d = 16 n + r16]
+        auto v_frag = [&](int n) {
+          const int col = 16 * n + 4 * (r16 & 3);  // bf16 column
+          const int c = col >> 3, wsub = col & 7;
+          const int row_lo = 4 * q4 + (r16 >> 2);
+          const int row_hi = 16 + row_lo;
+          const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ swz<CH>(row_lo)) << 4) + 2 * wsub);
+          const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ swz<CH>(row_hi)) << 4) + 2 * wsub);
+          return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        };
+        // the first fragments are read now, so their latency hides under the softmax
+        u32x4 vpre[NPRE > 0 ? NPRE : 1];
+  #pragma unroll
+        for (int n = 0; n < NPRE; ++n) vpre[n] = v_frag(n);
         // ---- online softmax per head block -> bf16 probabilities (B operand of PV).
         // The reference max moves only when a tile's max exceeds it by more than
         // kRescaleSlack (log2 units): O and l always share the same reference, so
@@ -607,15 +623,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           }
         }
         // ---- O^T += V^T P^T: one 16-wide d tile of V at a time, shared by all head blocks
+        // (the first NPRE fragments were read before the softmax)
   #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const int col = 16 * n + 4 * (r16 & 3);  // bf16 column
-          const int c = col >> 3, wsub = col & 7;
-          const int row_lo = 4 * q4 + (r16 >> 2);
-          const int row_hi = 16 + row_lo;
-          const u32x2 lo2 = lds_read_tr16(vt + row_lo * (2 * D) + ((c ^ swz<CH>(row_lo)) << 4) + 2 * wsub);
-          const u32x2 hi2 = lds_read_tr16(vt + row_hi * (2 * D) + ((c ^ swz<CH>(row_hi)) << 4) + 2 * wsub);
-          const u32x4 vf = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+          const u32x4 vf = n < NPRE ? vpre[n < NPRE ? n : 0] : v_frag(n);
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
         }
