@@ -581,7 +581,7 @@ def _workload_launches():
         mask = inputs.draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, wl.seed, wl.doc_lens) if wl.mask else None
         pairs = roofline.visible_pairs(wl.B, wl.S_q, wl.S_k, wl.causal, lens, mask)
         has_mask = "true" if wl.mask else "false"  # dense-mask instantiation of the kernel
-        kname, targs = (("gqa_prefill_fp8_kernel", (str(hc), has_mask)) if wl.dtype == "fp8"
+        kname, targs = (("gqa_prefill_fp8_kernel", (str(wl.d_h), str(hc), has_mask)) if wl.dtype == "fp8"
                         else ("gqa_prefill_masked_kernel", (str(wl.d_h), str(hc), has_mask)))
         out.append(((kname, targs, grid),
                     (f"prefill_masked:{wl.name}", wl.name, roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs),
@@ -682,10 +682,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, dest, mfma_dir=None, n_c
             if did not in trows or any(c not in vals for c in MFMA_COUNTERS):
                 continue
             t = trows[did]
-            dur = int(t["End_Timestamp"]) - int(t["Start_Timestamp"])
-            stream.append(((*kernel_identity(kname), grid), (vals, dur, kname)))
-        for ckey, (vals, dur, _) in resolve(stream):
-            mfma.setdefault(ckey, []).append((vals, dur))
+            dt = int(t["End_Timestamp"]) - int(t["Start_Timestamp"])
+            stream.append(((*kernel_identity(kname), grid), (vals, dt, kname)))
+        for ckey, (vals, dt, _) in resolve(stream):
+            mfma.setdefault(ckey, []).append((vals, dt))
         # the warm-up products (torch.mm of two 4096 x 4096 bf16 matrices) are a kernel of known
         # work: their counter-derived busy fraction against their timed flop rate checks the formula
         g = [(vals, dur) for (_, (vals, dur, kname)) in stream if kname.startswith("Cijk_") and dur > 0]
