@@ -357,7 +357,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     }
     __syncthreads();
     const int nrows = min(BM, S - blk0);
-    constexpr int TPI = 4;  // tiles per wave and pass: their loads are in flight together
+    // four lanes cover one row's 64 bytes of a tile, so a load instruction
+    // reads 16 rows x 64 consecutive bytes (16 cache-line requests, not 64);
+    // a pass loads TPI tiles of all BM rows, about 16 loads in flight
+    static_assert(kBN == 64, "the scan assumes 64-key tiles");
+    constexpr int NRG = BM / 16;                    // 16-row groups of the block
+    constexpr int TPI = NRG >= 16 ? 1 : 16 / NRG;  // tiles per wave and pass
     for (int j0 = wave; j0 < n_tiles; j0 += TPI * kWaves) {
       uint32_t any[TPI], zero[TPI];
 #pragma unroll
@@ -365,13 +370,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
         any[u] = 0u;
         zero[u] = 0u;
       }
-      for (int r = lane; r < nrows; r += 64) {
 #pragma unroll
-        for (int u = 0; u < TPI; ++u) {
-          const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((j0 + u * kWaves) * kBN);
+      for (int g = 0; g < NRG; ++g) {
+        const int r = 16 * g + (lane >> 2);
+        if (r < nrows) {
 #pragma unroll
-          for (int i = 0; i < kBN / 16; ++i) {
-            const u32x4 mv = buffer_load_x4(mrsrc, off + 16 * i);
+          for (int u = 0; u < TPI; ++u) {
+            const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((j0 + u * kWaves) * kBN + 16 * (lane & 3));
+            const u32x4 mv = buffer_load_x4(mrsrc, off);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               any[u] |= mv[e];
