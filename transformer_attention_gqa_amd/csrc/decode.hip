@@ -145,8 +145,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // offset removed in the products, with the codes of each 8-element chunk
   // in the order 0 2 4 6 1 3 5 7 (each bf16 pair then comes from one byte
   // permute, see i4x8_to_bf16x8_biased_eo).  Q is staged in the same order,
-  // which leaves every score unchanged, and the rows of O come out in it and
-  // are put back in order at the segment end.  (With two head blocks the
+  // which leaves every score unchanged; with V staged the same way the rows
+  // of O come out in that order and are put back at the segment end.  (With two head blocks the
   // extra registers spill, so that kernel converts through float.)
   constexpr bool BIAS4 = KVF == kKvInt4 && HB == 1;
   // With d = 128 such a kernel also skips the LDS for K: lane (q4, r16)
@@ -155,6 +155,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // k-step kk stands for d = 32 q4 + 8 kk + j (and Q is read to match), so
   // K goes from the load registers through the conversion into the product.
   constexpr bool KDIR = BIAS4 && D == 128;
+  // Such a kernel keeps V as raw codes in LDS too (2 KiB per 32 tokens instead
+  // of 8 KiB of bf16) and reads it with the 4-bit transposing LDS read: within
+  // each 16-lane group, output lane i receives nibble i of the 8 bytes each of
+  // the 16 lanes points at (nibble j from lane j).  Lane (q4, L) points at the
+  // token of k-slot 8 q4 + (L % 8) and at the 8 bytes of d-tile 2p + L / 8,
+  // so one read gives lane (q4, r16) the codes of d = 32p + r16 (first dword)
+  // and 32p + 16 + r16 (second) over its 8 k-slots: the A operands of two
+  // products, in natural d order.  8-byte chunk c of token row r sits at chunk
+  // position c ^ vsw(r); vsw keeps both the 16-byte staging writes and the
+  // transposed reads (8 rows x 2 chunks per 16 lanes) on distinct banks.
+  auto vsw = [](int r) { return (((r >> 4) & 1) << 1) | (((r >> 2) & 1) << 2); };
   // V^T fragments of the weighted sum read ahead of the softmax (registers allowing)
   constexpr int NPRE = HB == 1 ? 4 : 0;
   // 32 heads of a bf16 cache: one 32x32 score tile per 32 tokens on
@@ -330,6 +341,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{k0[0], k0[1], k1[0], k1[1]});
           lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{v0[0], v0[1], v1[0], v1[1]});
         }
+      } else if constexpr (KDIR) {
+        // V as raw codes: 8-byte chunks 2c and 2c+1 of row r, adjacent under
+        // vsw (which leaves bit 0 of the chunk index alone)
+        lds_store(vt + r * ROWB + 8 * ((2 * ld_chunk) ^ vsw(r)), vreg[half][u]);
       } else if constexpr (KVF == kKvInt4) {
         // 32 codes -> logical bf16 chunks 4c .. 4c+3 of row r (one per dword)
         const int c0 = 4 * ld_chunk;
@@ -337,8 +352,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           if constexpr (BIAS4) {
-            if constexpr (!KDIR)
-              lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(kreg[half][u][h]));
+            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(kreg[half][u][h]));
             lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8_biased_eo(vreg[half][u][h]));
           } else {
             lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), i4x8_to_bf16x8(kreg[half][u][h]));
@@ -535,6 +549,21 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             sc[h][hb] = acc;
           }
         }
+        // direct K (raw V): codes of d-tiles 2p and 2p + 1 over the lane's k-slots
+        auto v_raw = [&](int pp) {
+          const int L = r16 & 7;
+          const int row = 16 * (L >> 2) + 4 * q4 + (L & 3);  // token of k-slot 8 q4 + L
+          const int c = 2 * pp + (r16 >> 3);
+          const auto v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2*)(vt + row * ROWB + 8 * (c ^ vsw(row))));
+          return __builtin_bit_cast(u32x2, v);
+        };
+        constexpr int NRAW = KDIR ? NT / 2 : 1;
+        u32x2 vraw[NRAW];
+        if constexpr (KDIR) {
+  #pragma unroll
+          for (int pp = 0; pp < NRAW; ++pp) vraw[pp] = v_raw(pp);  // latency hidden by the softmax
+        }
         // V^T fragment n of the staged tile: lane holds V[token k-slot 8 q4 + j][d = 16 n + r16]
         auto v_frag = [&](int n) {
           const int col = 16 * n + 4 * (r16 & 3);  // bf16 column
@@ -546,9 +575,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         };
         // the first fragments are read now, so their latency hides under the softmax
-        u32x4 vpre[NPRE > 0 ? NPRE : 1];
+        constexpr int NPRE_ = KDIR ? 0 : NPRE;
+        u32x4 vpre[NPRE_ > 0 ? NPRE_ : 1];
   #pragma unroll
-        for (int n = 0; n < NPRE; ++n) vpre[n] = v_frag(n);
+        for (int n = 0; n < NPRE_; ++n) vpre[n] = v_frag(n);
         // ---- online softmax per head block -> bf16 probabilities (B operand of PV).
         // The reference max moves only when a tile's max exceeds it by more than
         // kRescaleSlack (log2 units): O and l always share the same reference, so
@@ -611,6 +641,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   #pragma unroll
               for (int i = 0; i < 4; ++i) p[h][i] *= vscur[h][i];
           }
+          if constexpr (KDIR)  // k-slots in the order 0 2 4 6 1 3 5 7 of the converted V codes
+            pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][2]), pack_bf16x2(p[1][0], p[1][2]), pack_bf16x2(p[0][1], p[0][3]),
+                           pack_bf16x2(p[1][1], p[1][3])};
+          else
           pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
                          pack_bf16x2(p[1][2], p[1][3])};
         }
@@ -626,7 +660,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         // (the first NPRE fragments were read before the softmax)
   #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const u32x4 vf = n < NPRE ? vpre[n < NPRE ? n : 0] : v_frag(n);
+          u32x4 vf;
+          if constexpr (KDIR) vf = i4x8_to_bf16x8_biased_eo(vraw[n >> 1][n & 1]);
+          else vf = n < NPRE_ ? vpre[n < NPRE_ ? n : 0] : v_frag(n);
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
         }
@@ -688,7 +724,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          if constexpr (BIAS4) {
+          if constexpr (BIAS4 && !KDIR) {
             // staged column 16n + 4q4 + i holds d = 16n + 8(q4/2) + 2i + q4%2
 #pragma unroll
             for (int i = 0; i < 4; ++i)
