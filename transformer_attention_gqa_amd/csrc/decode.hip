@@ -484,14 +484,21 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           for (int r = 0; r < 16; ++r)
             sacc[r] = tt0 + 8 * (r >> 2) + 4 * h2 + (r & 3) < t_end ? sacc[r] : kNegInf;
         }
+        // lane-local check first; the exchange only when a score exceeds the
+        // reference by more than the slack (as in the 16 x 16 path below)
         float mt = kNegInf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-        mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
-        const bool grow = mt > m[0] + kRescaleSlack;
-        const float m_new = grow ? mt : m[0];
-        const float alpha = grow ? fast_exp2(m[0] - m_new) : 1.0f;
-        m[0] = m_new;
+        bool grow = false;
+        float alpha = 1.0f;
+        if (__builtin_amdgcn_ballot_w64(mt * a.qk_scale_log2 > m[0] + kRescaleSlack)) {
+          mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
+          grow = mt > m[0] + kRescaleSlack;
+          const float m_new = grow ? mt : m[0];
+          alpha = grow ? fast_exp2(m[0] - m_new) : 1.0f;
+          m[0] = m_new;
+        }
+        const float m_new = m[0];
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -596,42 +603,59 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             vscur[h] = lds_load<f32x4>(&ssc[wave][32 + 16 * h + 4 * q4]);
           }
         }
+        // Each lane first checks its own scores against the reference: only
+        // if one of them exceeds it by more than the slack (a head's first
+        // tile of the segment, as a rule) does the wave form the per-head
+        // tile maxima with the cross-lane exchanges and move the reference.
+        // The head-wide test is the same one, so the result is unchanged.
+        float sv[HB][2][4];
+        float lmax[HB];
+        bool need = false;
   #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-          float sv[2][4];
-          float mt = kNegInf;
+          lmax[hb] = kNegInf;
   #pragma unroll
           for (int h = 0; h < 2; ++h)
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
               float x = sc[h][hb][i];
               if constexpr (QUANT) x *= kscur[h][i];  // the per-token K scale (> 0)
-              sv[h][i] = x;
+              sv[hb][h][i] = x;
             }
           if (tail) {
   #pragma unroll
             for (int h = 0; h < 2; ++h)
   #pragma unroll
-              for (int i = 0; i < 4; ++i) sv[h][i] = tt0 + 16 * h + 4 * q4 + i < t_end ? sv[h][i] : kNegInf;
+              for (int i = 0; i < 4; ++i) sv[hb][h][i] = tt0 + 16 * h + 4 * q4 + i < t_end ? sv[hb][h][i] : kNegInf;
           }
   #pragma unroll
           for (int h = 0; h < 2; ++h)
   #pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sv[h][i]);
-          mt = wave_max_xor(mt, 16);
-          mt = wave_max_xor(mt, 32) * a.qk_scale_log2;  // scale > 0 keeps the order
-          const bool grow = mt > m[hb] + kRescaleSlack;
-          const float m_new = grow ? mt : m[hb];
-          alpha[hb] = grow ? fast_exp2(m[hb] - m_new) : 1.0f;
-          any_grow = any_grow || grow;
-          m[hb] = m_new;
+            for (int i = 0; i < 4; ++i) lmax[hb] = fmaxf(lmax[hb], sv[hb][h][i]);
+          need = need || lmax[hb] * a.qk_scale_log2 > m[hb] + kRescaleSlack;  // scale > 0 keeps the order
+          alpha[hb] = 1.0f;
+        }
+        if (__builtin_amdgcn_ballot_w64(need)) {
+  #pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            float mt = wave_max_xor(lmax[hb], 16);
+            mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
+            const bool grow = mt > m[hb] + kRescaleSlack;
+            const float m_new = grow ? mt : m[hb];
+            alpha[hb] = grow ? fast_exp2(m[hb] - m_new) : 1.0f;
+            any_grow = any_grow || grow;
+            m[hb] = m_new;
+          }
+        }
+  #pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
           float psum = 0.f;
           float p[2][4];
   #pragma unroll
           for (int h = 0; h < 2; ++h)
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              p[h][i] = fast_exp2(__builtin_fmaf(sv[h][i], a.qk_scale_log2, -m_new));
+              p[h][i] = fast_exp2(__builtin_fmaf(sv[hb][h][i], a.qk_scale_log2, -m[hb]));
               psum += p[h][i];
             }
           l[hb] = l[hb] * alpha[hb] + psum;
@@ -645,8 +669,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
             pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][2]), pack_bf16x2(p[1][0], p[1][2]), pack_bf16x2(p[0][1], p[0][3]),
                            pack_bf16x2(p[1][1], p[1][3])};
           else
-          pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
-                         pack_bf16x2(p[1][2], p[1][3])};
+            pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]), pack_bf16x2(p[1][0], p[1][1]),
+                           pack_bf16x2(p[1][2], p[1][3])};
         }
         if (__builtin_amdgcn_ballot_w64(any_grow)) {
   #pragma unroll

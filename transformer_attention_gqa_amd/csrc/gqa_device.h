@@ -138,13 +138,13 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8_biased(uint32_t w) {
 // The same values in the order 0 2 4 6 1 3 5 7 (bf16 position j holds code
 // pi(j)): with the even codes' nibbles in the bytes of one word and the odd
 // ones' in another, each output dword is a byte permute of one of them with
-// the bytes 0x43, so eight codes cost two masks, a shift, an xor and four
-// permutes.  v_perm_b32 picks result byte k by selector byte k from the
+// the bytes 0x43, so eight codes cost a shift, two masks and four permutes.  v_perm_b32 picks result byte k by selector byte k from the
 // eight bytes of {first operand : second operand}, 0..3 being the second.
 __device__ __forceinline__ u32x4 i4x8_to_bf16x8_biased_eo(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t ev = u & 0x0F0F0F0Fu;         // offset nibbles of codes 0 2 4 6
-  const uint32_t od = (u >> 4) & 0x0F0F0F0Fu;  // codes 1 3 5 7
+  // offset nibbles (code ^ 8) of codes 0 2 4 6 and of codes 1 3 5 7, one per byte
+  // (written mask-then-flip so each is one three-input bit operation)
+  const uint32_t ev = (w & 0x0F0F0F0Fu) ^ 0x08080808u;
+  const uint32_t od = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
   constexpr uint32_t k43 = 0x43434343u;
   return u32x4{__builtin_amdgcn_perm(k43, ev, 0x04010400u), __builtin_amdgcn_perm(k43, ev, 0x04030402u),
                __builtin_amdgcn_perm(k43, od, 0x04010400u), __builtin_amdgcn_perm(k43, od, 0x04030402u)};
