@@ -154,7 +154,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // exactly the codes of its score-product operand when k-slot (q4, j) of
   // k-step kk stands for d = 32 q4 + 8 kk + j (and Q is read to match), so
   // K goes from the load registers through the conversion into the product.
-  constexpr bool KDIR = BIAS4 && D == 128;
+  // The fp8 and int8 kernels with one head block (d = 128) do the same with
+  // their 128-byte rows: lane (q4, r16) loads bytes 32 q4 .. 32 q4 + 31 of
+  // token row r16 of each 16-token half (two 16-byte loads) and converts them
+  // exactly to the bf16 operands of its four k-steps.
+  constexpr bool KDIR = (BIAS4 || ((KVF == kKvFp8 || KVF == kKvInt8) && HB == 1)) && D == 128;
+  constexpr bool V4RAW = KDIR && KVF == kKvInt4;  // V as raw int4 codes (below)
   // Such a kernel keeps V as raw codes in LDS too (2 KiB per 32 tokens instead
   // of 8 KiB of bf16) and reads it with the 4-bit transposing LDS read: within
   // each 16-lane group, output lane i receives nibble i of the 8 bytes each of
@@ -234,8 +239,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // the end read as zero without a memory access (a cache tail may hold NaN)
   // and each load needs only a 32-bit lane offset.
   const unsigned lane_off = ld_row * ROWB + ld_chunk * 16;
-  const unsigned k_lane_off = KDIR ? r16 * ROWB + q4 * 16 : lane_off;  // (RPL = 16 rows per load then)
-  static_assert(!KDIR || (RPL == 16 && NLD == 2), "direct K assumes 16 rows of 64 bytes per load");
+  // byte offset of K load u from the tile's first row
+  auto k_off = [&](int u) -> unsigned {
+    if constexpr (!KDIR) return lane_off + u * RPL * ROWB;
+    else if constexpr (KVF == kKvInt4) return (16 * u + r16) * ROWB + 16 * q4;  // half u
+    else return (16 * (u >> 1) + r16) * ROWB + 32 * q4 + 16 * (u & 1);         // half u / 2, part u % 2
+  };
+  static_assert(!KDIR || (KVF == kKvInt4 ? NLD == 2 : NLD == 4), "direct K: two 16-token halves per tile");
   // (a half past the segment's end gets an empty range: its loads return
   // zeros without a memory access, so every path issues the same loads)
   auto issue_loads = [&](Segment& s, int tile, int half = 0) {
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
     const auto rv = make_rsrc(static_cast<const char*>(a.v) + row0 * ROWB, nvalid * ROWB);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      kreg[half][u] = buffer_load_x4_nt(rk, k_lane_off + u * RPL * ROWB);
+      kreg[half][u] = buffer_load_x4_nt(rk, k_off(u));
       vreg[half][u] = buffer_load_x4_nt(rv, lane_off + u * RPL * ROWB);
     }
     if constexpr (QUANT) {
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   // Stage the tile whose loads were issued last into the wave's LDS slab as
   // bf16 (quantized codes are converted exactly) and its scales into the
   // wave's scale slot.
-  u32x4 kcur[KDIR ? NLD : 1];  // direct K: the staged half's codes, 16-token half u in kcur[u]
+  u32x4 kcur[KDIR ? NLD : 1];  // direct K: the staged tile's codes, as loaded
   auto stage = [&](int half = 0) {
     wave_lds_fence();
     if constexpr (QUANT) ssc[wave][lane] = lane < 32 ? ksl[half] : vsl[half];
@@ -315,19 +325,22 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       if constexpr (KVF == kKvFp8) {
         // 16 codes -> 16 bf16 = logical bf16 chunks 2c, 2c+1 of row r
         const int c0 = 2 * ld_chunk;
-        u32x2 t0 = e4m3x4_to_bf16x4(kreg[half][u][0]), t1 = e4m3x4_to_bf16x4(kreg[half][u][1]);
-        u32x2 t2 = e4m3x4_to_bf16x4(kreg[half][u][2]), t3 = e4m3x4_to_bf16x4(kreg[half][u][3]);
-        const u32x4 klo = u32x4{t0[0], t0[1], t1[0], t1[1]};
-        const u32x4 khi = u32x4{t2[0], t2[1], t3[0], t3[1]};
+        u32x2 t0, t1, t2, t3;
+        const int sw = swz<CH>(r);
+        if constexpr (!KDIR) {
+          t0 = e4m3x4_to_bf16x4(kreg[half][u][0]);
+          t1 = e4m3x4_to_bf16x4(kreg[half][u][1]);
+          t2 = e4m3x4_to_bf16x4(kreg[half][u][2]);
+          t3 = e4m3x4_to_bf16x4(kreg[half][u][3]);
+          lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), u32x4{t0[0], t0[1], t1[0], t1[1]});
+          lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), u32x4{t2[0], t2[1], t3[0], t3[1]});
+        }
         t0 = e4m3x4_to_bf16x4(vreg[half][u][0]);
         t1 = e4m3x4_to_bf16x4(vreg[half][u][1]);
         t2 = e4m3x4_to_bf16x4(vreg[half][u][2]);
         t3 = e4m3x4_to_bf16x4(vreg[half][u][3]);
         const u32x4 vlo = u32x4{t0[0], t0[1], t1[0], t1[1]};
         const u32x4 vhi = u32x4{t2[0], t2[1], t3[0], t3[1]};
-        const int sw = swz<CH>(r);
-        lds_store(kt + r * (2 * D) + ((c0 ^ sw) << 4), klo);
-        lds_store(kt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), khi);
         lds_store(vt + r * (2 * D) + ((c0 ^ sw) << 4), vlo);
         lds_store(vt + r * (2 * D) + (((c0 + 1) ^ sw) << 4), vhi);
       } else if constexpr (KVF == kKvInt8) {
@@ -336,12 +349,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         const int sw = swz<CH>(r);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const u32x2 k0 = i8x4_to_bf16x4(kreg[half][u][2 * h]), k1 = i8x4_to_bf16x4(kreg[half][u][2 * h + 1]);
+          if constexpr (!KDIR) {
+            const u32x2 k0 = i8x4_to_bf16x4(kreg[half][u][2 * h]), k1 = i8x4_to_bf16x4(kreg[half][u][2 * h + 1]);
+            lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{k0[0], k0[1], k1[0], k1[1]});
+          }
           const u32x2 v0 = i8x4_to_bf16x4(vreg[half][u][2 * h]), v1 = i8x4_to_bf16x4(vreg[half][u][2 * h + 1]);
-          lds_store(kt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{k0[0], k0[1], k1[0], k1[1]});
           lds_store(vt + r * (2 * D) + (((c0 + h) ^ sw) << 4), u32x4{v0[0], v0[1], v1[0], v1[1]});
         }
-      } else if constexpr (KDIR) {
+      } else if constexpr (V4RAW) {
         // V as raw codes: 8-byte chunks 2c and 2c+1 of row r, adjacent under
         // vsw (which leaves bit 0 of the chunk index alone)
         lds_store(vt + r * ROWB + 8 * ((2 * ld_chunk) ^ vsw(r)), vreg[half][u]);
@@ -533,9 +548,23 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
         for (int h = 0; h < 2; ++h) {
           const int row = 16 * h + r16;
           u32x4 kf[KK];
-          if constexpr (KDIR) {
+          if constexpr (KDIR && KVF == kKvInt4) {
   #pragma unroll
             for (int kk = 0; kk < KK; ++kk) kf[kk] = i4x8_to_bf16x8_biased_eo(kcur[h][kk]);
+          } else if constexpr (KDIR) {  // 8-bit codes d = 32 q4 + 8 kk .. +7: bytes 8 kk .. of the lane's 32
+  #pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+              const u32x4& w = kcur[2 * h + (kk >> 1)];
+              u32x2 lo4, hi4;
+              if constexpr (KVF == kKvFp8) {
+                lo4 = e4m3x4_to_bf16x4(w[2 * (kk & 1)]);
+                hi4 = e4m3x4_to_bf16x4(w[2 * (kk & 1) + 1]);
+              } else {
+                lo4 = i8x4_to_bf16x4(w[2 * (kk & 1)]);
+                hi4 = i8x4_to_bf16x4(w[2 * (kk & 1) + 1]);
+              }
+              kf[kk] = u32x4{lo4[0], lo4[1], hi4[0], hi4[1]};
+            }
           } else {
   #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
@@ -565,9 +594,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
               (__attribute__((address_space(3))) i32x2*)(vt + row * ROWB + 8 * (c ^ vsw(row))));
           return __builtin_bit_cast(u32x2, v);
         };
-        constexpr int NRAW = KDIR ? NT / 2 : 1;
+        constexpr int NRAW = V4RAW ? NT / 2 : 1;
         u32x2 vraw[NRAW];
-        if constexpr (KDIR) {
+        if constexpr (V4RAW) {
   #pragma unroll
           for (int pp = 0; pp < NRAW; ++pp) vraw[pp] = v_raw(pp);  // latency hidden by the softmax
         }
@@ -582,7 +611,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         };
         // the first fragments are read now, so their latency hides under the softmax
-        constexpr int NPRE_ = KDIR ? 0 : NPRE;
+        constexpr int NPRE_ = V4RAW ? 0 : NPRE;
         u32x4 vpre[NPRE_ > 0 ? NPRE_ : 1];
   #pragma unroll
         for (int n = 0; n < NPRE_; ++n) vpre[n] = v_frag(n);
@@ -665,7 +694,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   #pragma unroll
               for (int i = 0; i < 4; ++i) p[h][i] *= vscur[h][i];
           }
-          if constexpr (KDIR)  // k-slots in the order 0 2 4 6 1 3 5 7 of the converted V codes
+          if constexpr (V4RAW)  // k-slots in the order 0 2 4 6 1 3 5 7 of the converted V codes
             pf[hb] = u32x4{pack_bf16x2(p[0][0], p[0][2]), pack_bf16x2(p[1][0], p[1][2]), pack_bf16x2(p[0][1], p[0][3]),
                            pack_bf16x2(p[1][1], p[1][3])};
           else
@@ -685,7 +714,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
   #pragma unroll
         for (int n = 0; n < NT; ++n) {
           u32x4 vf;
-          if constexpr (KDIR) vf = i4x8_to_bf16x8_biased_eo(vraw[n >> 1][n & 1]);
+          if constexpr (V4RAW) vf = i4x8_to_bf16x8_biased_eo(vraw[n >> 1][n & 1]);
           else vf = n < NPRE_ ? vpre[n < NPRE_ ? n : 0] : v_frag(n);
   #pragma unroll
           for (int hb = 0; hb < HB; ++hb) o[hb][n] = mfma16(vf, pf[hb], o[hb][n]);
@@ -748,7 +777,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_split_mfma(DecodeArgs a) {
       for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          if constexpr (BIAS4 && !KDIR) {
+          if constexpr (BIAS4 && !V4RAW) {
             // staged column 16n + 4q4 + i holds d = 16n + 8(q4/2) + 2i + q4%2
 #pragma unroll
             for (int i = 0; i < 4; ++i)
