@@ -33,7 +33,8 @@
  *  - `out` must not overlap any input or the workspace.
  *  - Supported head dimensions: d_h = 64 or 128.
  *  - `scale` multiplies q . k before the softmax (the modules use
- *    head_dim ** -0.5); it must be finite and > 0 (GQA_ERR_VALUE otherwise).
+ *    head_dim ** -0.5); it must be finite and >= 0 (GQA_ERR_VALUE otherwise).
+ *    0 gives every visible key the same weight (the mean of their values).
  *    A scale whose product with log2(e) is below the smallest normal float
  *    is raised to it (the scores are then zero to float precision).
  */
@@ -72,7 +73,7 @@ typedef enum gqa_status {
   GQA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                  */
   GQA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
   GQA_ERR_HIP = 6,       /* a HIP launch or query failed                      */
-  GQA_ERR_VALUE = 7,     /* scale is not a finite number > 0, or a flags
+  GQA_ERR_VALUE = 7,     /* scale is not a finite number >= 0, or a flags
                             word holds unknown bits                           */
   GQA_ERR_SCRATCH = 8    /* attn_decode_noalloc: the call's partials need
                             more than attn_decode_noalloc_max_scratch_bytes() */

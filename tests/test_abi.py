@@ -123,8 +123,8 @@ def test_prefill_errors(lib):
     assert call(pd(), out=MISALIGNED) == 4
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
-def test_scale_must_be_finite_positive(lib, scale):
+@pytest.mark.parametrize("scale", [-0.125, -1e-30, float("inf"), float("-inf"), float("nan")])
+def test_scale_must_be_finite_and_non_negative(lib, scale):
     desc = dd()
     need = lib.attn_decode_workspace_bytes(ctypes.byref(desc))
     assert lib.attn_decode(ctypes.byref(desc), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, scale, ALIGNED,
@@ -200,7 +200,7 @@ def test_paged_pointer_and_value_errors(lib):
     assert call_paged(lib, desc, table=ALIGNED + 2) == 4
     assert call_paged(lib, desc, vp=MISALIGNED) == 4
     assert call_paged(lib, desc, ws_bytes=16) == 5
-    assert call_paged(lib, desc, scale=0.0) == 7
+    assert call_paged(lib, desc, scale=-1.0) == 7
 
 
 @pytest.mark.parametrize("kt", [3, 4])
@@ -340,7 +340,7 @@ def test_noalloc_scratch_limit_is_checked_on_the_host(lib):
                                    ALIGNED, None) == 8
     assert lib.attn_decode_noalloc(ctypes.byref(dd()), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
                                    None, None) == 1
-    assert lib.attn_decode_noalloc(ctypes.byref(dd()), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 0.0,
+    assert lib.attn_decode_noalloc(ctypes.byref(dd()), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, -1.0,
                                    ALIGNED, None) == 7
     assert lib.attn_decode_noalloc(ctypes.byref(dd(flags=2)), ALIGNED, ALIGNED, ALIGNED, None, None, ALIGNED, 1.0,
                                    ALIGNED, None) == 7

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from transformer_attention_gqa_amd import binding, inputs
 import parity_utils as pu
 
@@ -133,6 +134,27 @@ def test_single_key_returns_value_row():
     pu.sync()
     for j in range(8):
         assert torch.equal(out[:, j], inp.v[:, j // 4, 0])  # p = 1 exactly; bf16 value passes through
+
+
+@pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_zero_scale_gives_the_mean_of_visible_values(kd, h_q):
+    """scale = 0: every visible key has the same weight, so each output row is
+    the mean of the sequence's visible V rows (the oracle at scale 0)."""
+    qd = "f32" if kd == "f32" else "bf16"
+    w = wl("zero", B=3, h_q=h_q, n_kv=2, d=128, S=300, qd=qd, kd=kd, seed=61)
+    inp = inputs.make_decode_inputs(w, device=DEV, seq_lens=[1, 300, 77])
+    out = binding.attn_decode(inp.q, inp.k, inp.v, inp.seq_lens, 0.0, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    pu.sync()
+    q = pu.to_f64(inp.q)
+    lens = inp.seq_lens.cpu().tolist()
+    ref = np.zeros(tuple(out.shape))
+    for b in range(w.B):
+        for g in range(w.n_kv):
+            k, v = pu.cache_f64(inp, b, g)
+            for j in range(g * w.G, (g + 1) * w.G):
+                ref[b, j] = oracle.attend_one_row(q[b, j], k[:lens[b]], v[:lens[b]], 0.0)
+    assert pu.max_err(out, ref) <= pu.TOL[kd]
 
 
 @pytest.mark.parametrize("kd", ["f32", "bf16", "fp8", "int8", "int4"])

@@ -115,3 +115,15 @@ def test_mla_full_size_sampled():
     bs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, w.B - 1, *rng.integers(0, w.B, 3).tolist()})
     err = pu.max_err(out[bs], oracle_rows(inp, bs))
     assert err <= TOL, f"max abs err {err}"
+
+
+def test_mla_zero_scale_gives_the_mean_of_visible_rows():
+    """scale = 0: every head returns the mean of the sequence's visible latent
+    rows (the oracle at scale 0); a sequence of length 0 gives zeros."""
+    inp = inputs.make_mla_inputs(wl(B=3, h_q=32, d_c=512, S=300, seed=330), device=DEV, seq_lens=[300, 1, 0],
+                                 poison_tail=True)
+    out = binding.attn_decode_mla(inp.q, inp.c_kv, inp.seq_lens, 0.0)
+    pu.sync()
+    ref = oracle.mla_decode(pu.to_f64(inp.q), pu.to_f64(inp.c_kv), inp.seq_lens.cpu().numpy(), 0.0)
+    assert pu.max_err(out, ref) <= TOL
+

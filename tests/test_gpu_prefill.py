@@ -74,6 +74,18 @@ def test_prefill_first_row_is_first_value_row():
         assert torch.equal(out[:, 0, j], inp.v[:, 0, j // 4])
 
 
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_prefill_zero_scale_gives_running_means(G):
+    """scale = 0: query row r weighs keys 0..r equally, so it returns the mean
+    of V rows 0..r (the oracle at scale 0)."""
+    w = pwl(2, 200, 2 * G, 2, 128, seed=11 + G)
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    out = binding.attn_prefill_causal(inp.q, inp.k, inp.v, 0.0)
+    pu.sync()
+    ref = oracle.prefill_causal(pu.to_f64(inp.q), pu.to_f64(inp.k), pu.to_f64(inp.v), 0.0)
+    assert pu.max_err(out, ref) <= TOL
+
+
 def test_prefill_causal_perturbation_bitwise():
     w = pwl(1, 260, 8, 2, 128, seed=5)
     inp = inputs.make_prefill_inputs(w, device=DEV)

@@ -210,3 +210,23 @@ def test_fp8_head_dim_64_long_causal():
     output element against the oracle."""
     w = wl(1, 1000, 1000, 8, 2, 64, True, seed=495, dtype="fp8")
     check(inputs.make_masked_prefill_inputs(w, device=DEV))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_zero_scale_gives_the_mean_of_visible_values(dtype):
+    """scale = 0: each row weighs its visible keys equally (key lengths, the
+    end-aligned causal rule and a dense mask combined), so it returns the
+    mean of their V rows; rows that see no key are zero."""
+    w = wl(2, 150, 232, 8, 2, 128, True, seed=77, mask="random", dtype=dtype)
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=[232, 101])
+    out = binding.attn_prefill(inp.q, inp.k, inp.v, 0.0, causal=True, kv_lens=inp.kv_lens, mask=inp.mask,
+                               q_descale=inp.q_descale, k_descale=inp.k_descale, v_descale=inp.v_descale)
+    pu.sync()
+    q, k, v = pu.masked_prefill_values(inp)
+    lens, mask = _lens_mask(inp)
+    ref = oracle.prefill(q, k, v, 0.0, causal=True, kv_lens=lens, mask=mask)
+    if dtype == "fp8":
+        pu.check_fp8_prefill(out, ref)
+    else:
+        assert pu.max_err(out, ref) <= TOL
+

@@ -71,7 +71,9 @@ float qk_scale_log2(float scale) { return fmaxf((float)((double)scale * kLog2e),
 bool is_quantized(int32_t t) { return t == GQA_FP8_E4M3 || t == GQA_INT8 || t == GQA_INT4; }
 
 // The kernels take the running max on unscaled scores, which needs scale > 0.
-bool bad_scale(float s) { return !(s > 0.0f) || !(s < __builtin_huge_valf()); }
+// A scale must be finite and >= 0: the kernels take the maximum of the
+// unscaled scores, which needs scale >= 0 to be the maximum of the scaled ones.
+bool bad_scale(float s) { return !(s >= 0.0f) || !(s < __builtin_huge_valf()); }
 
 struct DecodePlan {
   int kind;             // 0 f32, 1 bf16 K/V, 2 fp8, 3 int8, 4 int4 K/V
