@@ -26,6 +26,8 @@
 //    latent slice (v_mfma_f32_32x32x16_bf16), so a wave's accumulator holds
 //    d_c / 8 latent values of every head and the partials need no merge
 //    across waves.
+#include <type_traits>
+
 #include "decode_sched.h"
 #include "gqa_device.h"
 #include "gqa_launch.h"
@@ -182,8 +184,9 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
     }
   };
 
-  // ---- prologue: tiles 0 and 1 in LDS, the next NSET in flight (tile t in
-  // register set t % NSET)
+  // ---- prologue: tile 0 in LDS, the next NSET in flight (tile t in register
+  // set t % NSET); tile 1 is staged by step 0 once its scores are issued, so
+  // the first products do not wait for the second tile to land
   MlaSegment cur = mla_segment(a, ll, lo, hi, w, lane);
   MlaSegment ld = cur;  // segment of the tile issued last
   int cur0 = 0, ld0 = 0;  // local index of each segment's first tile
@@ -213,15 +216,13 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
   if constexpr (NSET == 3) prefetch(cr2, 2);
   stage(cr0, tiles[0]);
   prefetch(cr0, NSET);
-  stage(set_of(1), tiles[1]);
-  prefetch(set_of(1), 1 + NSET);
   reset();
   __syncthreads();  // every wave's slice of tile 0 written before its scores are read
 
   // one tile: its scores (score waves), one barrier, softmax and weighted sum
   // (every wave), then stage tile k + 2 from `next` (which takes tile k + 2 +
   // NSET) and close the segment at its end
-  auto step = [&](int k, u32x4* next) {
+  auto step = [&](int k, u32x4* next, auto first) {
     const char* ts = tiles[k % 3];
     float (*sk)[HPC * SROW] = sc[k & 1];
     const int tl = k - cur0;
@@ -234,6 +235,10 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
         acc = mfma16(lds_load<u32x4>(tile_at(ts, row, kq0 / 8 + 4 * ks + gi)), qf[ks], acc);
       // lane holds the share's S^T[token 16 tb + 4 gi + i][head 16 hq + s16]
       lds_store(sk[ksh] + (16 * hq + s16) * SROW + 16 * tb + 4 * gi, acc);
+    }
+    if constexpr (decltype(first)::value) {  // step 0: tile 1, read by step 1 after this barrier
+      stage(set_of(1), tiles[1]);
+      prefetch(set_of(1), 1 + NSET);
     }
     __syncthreads();
     // ---- online softmax (the same on every wave) and the weighted sum of
@@ -257,14 +262,22 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = tt0 + 8 * (r >> 2) + 4 * h2 + (r & 3) < cur.t_end ? s[r] : kNegInf;
       }
+      // lane-local test first; the exchange with lane ^ 32 only when one of
+      // the lane's scores exceeds the reference by more than the slack (the
+      // same head-wide test, so the result does not change)
       float mt = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
-      mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
-      const bool grow = mt > m[hb] + kMlaSlack;
-      const float m_new = grow ? mt : m[hb];
-      const float alpha = grow ? fast_exp2(m[hb] - m_new) : 1.0f;
-      m[hb] = m_new;
+      bool grow = false;
+      float alpha = 1.0f;
+      if (__builtin_amdgcn_ballot_w64(mt * a.qk_scale_log2 > m[hb] + kMlaSlack)) {
+        mt = wave_max_xor(mt, 32) * a.qk_scale_log2;
+        grow = mt > m[hb] + kMlaSlack;
+        const float m_up = grow ? mt : m[hb];
+        alpha = grow ? fast_exp2(m[hb] - m_up) : 1.0f;
+        m[hb] = m_up;
+      }
+      const float m_new = m[hb];
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -314,23 +327,27 @@ __global__ __launch_bounds__(kMlaWaves * 64) void gqa_mla_decode_split(MlaArgs a
   // steps in a loop without early exits (each set then has the same loads
   // issued after it on every path, so a stage waits only for its own set),
   // the remainder after it
-  int k = 0;
+  // (step 0 is peeled off: it alone stages tile 1)
+  using first_step = std::integral_constant<bool, true>;
+  using later_step = std::integral_constant<bool, false>;
+  step(0, set_of(2), first_step{});
+  int k = 1;
   if constexpr (NSET == 1) {
-    for (; k < n_local; ++k) step(k, cr0);
+    for (; k < n_local; ++k) step(k, cr0, later_step{});
   } else if constexpr (NSET == 2) {
     for (; k + 2 <= n_local; k += 2) {
-      step(k, cr0);
-      step(k + 1, cr1);
+      step(k, cr1, later_step{});
+      step(k + 1, cr0, later_step{});
     }
-    if (k < n_local) step(k, cr0);
+    if (k < n_local) step(k, cr1, later_step{});
   } else {
     for (; k + 3 <= n_local; k += 3) {
-      step(k, cr2);
-      step(k + 1, cr0);
-      step(k + 2, cr1);
+      step(k, cr0, later_step{});
+      step(k + 1, cr1, later_step{});
+      step(k + 2, cr2, later_step{});
     }
-    if (k < n_local) step(k, cr2);
-    if (k + 1 < n_local) step(k + 1, cr0);
+    if (k < n_local) step(k, cr0, later_step{});
+    if (k + 1 < n_local) step(k + 1, cr1, later_step{});
   }
 }
 
