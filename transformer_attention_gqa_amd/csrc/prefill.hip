@@ -221,10 +221,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // One wave instruction fills 1 KiB of LDS at (wave-uniform base + lane*16),
   // i.e. 64/CH consecutive tile rows; each lane picks the global 16-byte chunk
   // that belongs at its LDS slot under the XOR chunk swizzle, so the 16 (or 8)
-  // lanes of a row still read one contiguous cache row.  Rows past the
-  // sequence end re-read its last row (in bounds); their keys are always
-  // masked for valid query rows, so they contribute nothing.  With key
-  // lengths the same holds at the length: rows at or past it are never read.
+  // lanes of a row still read one contiguous cache row.  Rows at or past the
+  // sequence end (or the key length) are never read (see dma_tile).
   constexpr int RPI = 64 / CH;                  // tile rows per wave instruction
   // A tile of fewer than kWaves instructions per tensor (fp8 at d = 64: four
   // of 16 rows) is loaded by half the waves for K and the other half for V.
@@ -249,45 +247,35 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     const int r = ins_row0(u) + dma_r;
     dma_off[u] = (uint32_t)(r * kv_row_bytes + (dma_c ^ sw(r)) * 16);
   }
+  // The copies go through buffer resources whose base is the tile's first
+  // row and whose range ends at the last valid row (the sequence end, or the
+  // key length): rows past it read as zero without a memory access (their
+  // keys are hidden for every valid query row, so they contribute nothing).
+  // Raw buffer loads to LDS count only on the vector-memory counter, which
+  // leaves the LDS counter to the LDS reads: the compiler can then wait for
+  // the reads a product needs instead of all of them.
+  auto tile_rsrc = [&](const char* base, int key0) {
+    const int nvalid = min(kBN, kv_n - key0);  // >= 1 for a visited tile
+    return make_rsrc(base + (size_t)key0 * kv_row_bytes,
+                     (int)((unsigned)(nvalid - 1) * (unsigned)kv_row_bytes + ROWB));
+  };
   auto dma_tile = [&](int j, char* kdst, char* vdst) {
     const int key0 = j * kBN;
     if constexpr (SPLIT_KV) {
       // waves 0 .. kWaves/2 - 1 load K, the others V
       const bool is_k = wave < kWaves / 2;
-      const char* base = is_k ? kbase : vbase;
+      const auto rs = tile_rsrc(is_k ? kbase : vbase, key0);
       char* dst = is_k ? kdst : vdst;
-      const int r0 = ins_row0(0);
-      if (key0 + kBN <= kv_n) {
-        __builtin_amdgcn_global_load_lds(base + (size_t)key0 * kv_row_bytes + dma_off[0], (lds_void*)(dst + r0 * ROWB),
-                                         16, 0, 0);
-      } else {
-        const int r = r0 + dma_r;
-        const int key = min(key0 + r, kv_n - 1);
-        const size_t off = (size_t)key * kv_row_bytes + (dma_c ^ sw(r)) * 16;
-        __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + r0 * ROWB), 16, 0, 0);
-      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + ins_row0(0) * ROWB), 16, dma_off[0], 0, 0, 0);
       return;
     }
-    if (key0 + kBN <= kv_n) {
-      const char* kt = kbase + (size_t)key0 * kv_row_bytes;
-      const char* vt = vbase + (size_t)key0 * kv_row_bytes;
+    const auto rk = tile_rsrc(kbase, key0);
+    const auto rv = tile_rsrc(vbase, key0);
 #pragma unroll
-      for (int u = 0; u < NINS; ++u) {
-        const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
-        __builtin_amdgcn_global_load_lds(kt + dma_off[u], (lds_void*)(kdst + r0 * ROWB), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + dma_off[u], (lds_void*)(vdst + r0 * ROWB), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NINS; ++u) {
-        const int r0 = (u * kWaves + wave) * RPI;
-        const int r = r0 + dma_r;
-        const int key = min(key0 + r, kv_n - 1);
-        const int c = dma_c ^ sw(r);              // logical chunk stored at this slot
-        const size_t off = (size_t)key * kv_row_bytes + c * 16;
-        __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(kdst + r0 * ROWB), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(vdst + r0 * ROWB), 16, 0, 0);
-      }
+    for (int u = 0; u < NINS; ++u) {
+      const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + r0 * ROWB), 16, dma_off[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + r0 * ROWB), 16, dma_off[u], 0, 0, 0);
     }
   };
   auto dma_wait = [&]() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -648,25 +636,42 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
           o[nt] = mfma32_fp8(vf8, pl8, o[nt]);
         }
       } else {
-      // ---- O^T += V^T P^T, 4 k-steps of 16 keys
+      // ---- O^T += V^T P^T, 4 k-steps of 16 keys, products in (k-step, d tile)
+      // order; the V^T fragment of product i + 2 is read while product i runs
+      // (three fragments in flight), so no product waits for the latency of
+      // its own LDS reads
+      u32x4 pf[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const f32x16& sp = sacc[p >> 1];
         const int rb = 8 * (p & 1);
-        const u32x4 pf = {pack_bf16x2(sp[rb + 0], sp[rb + 1]), pack_bf16x2(sp[rb + 2], sp[rb + 3]),
-                          pack_bf16x2(sp[rb + 4], sp[rb + 5]), pack_bf16x2(sp[rb + 6], sp[rb + 7])};
-        const int gi = lane >> 4, s16 = lane & 15;
+        pf[p] = u32x4{pack_bf16x2(sp[rb + 0], sp[rb + 1]), pack_bf16x2(sp[rb + 2], sp[rb + 3]),
+                      pack_bf16x2(sp[rb + 4], sp[rb + 5]), pack_bf16x2(sp[rb + 6], sp[rb + 7])};
+      }
+      const int gi = lane >> 4, s16 = lane & 15;
+      auto vfrag = [&](int i) {
+        const int p = i / NT, nt = i % NT;
+        const int col = 32 * nt + 16 * (gi & 1) + 4 * (s16 & 3);
+        const int c = col >> 3, w = col & 7;
+        const int ra = 16 * p + 4 * h2 + (s16 >> 2);
+        const int rbw = ra + 8;
+        const u32x2 va = lds_read_tr16(vt + ra * ROWB + ((c ^ sw(ra)) << 4) + 2 * w);
+        const u32x2 vb = lds_read_tr16(vt + rbw * ROWB + ((c ^ sw(rbw)) << 4) + 2 * w);
+        return u32x4{va[0], va[1], vb[0], vb[1]};
+      };
+      constexpr int NPV = 4 * NT;
+      u32x4 vq[3];
+      vq[0] = vfrag(0);
+      vq[1] = vfrag(1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = 32 * nt + 16 * (gi & 1) + 4 * (s16 & 3);
-          const int c = col >> 3, w = col & 7;
-          const int ra = 16 * p + 4 * h2 + (s16 >> 2);
-          const int rbw = ra + 8;
-          const u32x2 va = lds_read_tr16(vt + ra * ROWB + ((c ^ sw(ra)) << 4) + 2 * w);
-          const u32x2 vb = lds_read_tr16(vt + rbw * ROWB + ((c ^ sw(rbw)) << 4) + 2 * w);
-          const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
-          o[nt] = mfma32(vf, pf, o[nt]);
+      for (int i = 0; i < NPV; ++i) {
+        if (i + 2 < NPV) {
+          vq[(i + 2) % 3] = vfrag(i + 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads for product i + 2,
         }
+        o[i % NT] = mfma32(vq[i % 3], pf[i / NT], o[i % NT]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // then product i
       }
       }
     }
