@@ -399,8 +399,13 @@ def bench_prefill_masked(wl, steps, warmup, use_graph=False):
                                    None if x.mask is None else x.mask.cpu())
     flops = roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs)
     out = torch.empty(x.q.shape, dtype=torch.bfloat16, device=dev)
+    ws = None
+    if x.mask is not None:  # the key-tile bitmaps of the pass over the mask
+        desc = binding._attn_desc(x.q, x.k, x.v, out, wl.causal, x.kv_lens, x.mask)
+        ws = torch.empty(max(binding.attn_prefill_workspace_bytes(desc), 16), dtype=torch.uint8, device=dev)
     call = binding.prepare_prefill(x.q, x.k, x.v, wl.scale, out, causal=wl.causal, kv_lens=x.kv_lens, mask=x.mask,
-                                   q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale)
+                                   q_descale=x.q_descale, k_descale=x.k_descale, v_descale=x.v_descale,
+                                   workspace=ws)
 
     def step(i):
         call()
@@ -420,8 +425,9 @@ def bench_prefill_masked(wl, steps, warmup, use_graph=False):
         "visible_flops": flops,
         "kernel_ms": k_ms,
         "step_ms": dist,
-        "roofline": {"bound": "mfma", "kernel": "gqa_prefill_fp8_kernel" if wl.dtype == "fp8"
-                     else "gqa_prefill_masked_kernel", "achieved": achieved, "peak": peak,
+        "roofline": {"bound": "mfma", "kernel": ("gqa_prefill_fp8_kernel" if wl.dtype == "fp8"
+                                                 else "gqa_prefill_masked_kernel")
+                     + (" + gqa_mask_tiles_kernel" if x.mask is not None else ""), "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": measured_traffic(ckey),
                      **measured_mfma(ckey)},
         "dtype": wl.dtype,
@@ -586,6 +592,9 @@ def _workload_launches():
         out.append(((kname, targs, grid),
                     (f"prefill_masked:{wl.name}", wl.name, roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs),
                      "flops")))
+        if wl.mask:  # the pass over the mask: one workgroup of 512 per (row block, batch entry)
+            out.append((("gqa_mask_tiles_kernel", (str(bm),), -(-wl.S_q // bm) * wl.B * 512),
+                        (f"mask_tiles:{wl.name}", wl.name, None, None)))
     return out
 
 

@@ -352,6 +352,26 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
                         const float* q_descale, const float* k_descale, const float* v_descale,
                         const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, hipStream_t stream);
 
+/* attn_prefill with a caller-owned workspace for the dense mask's key-tile
+ * bitmaps.  Without a workspace (attn_prefill) every workgroup scans the mask
+ * rows of its row block to find the key tiles any row sees and those every
+ * row sees, once per K/V-head workgroup; with one, a pass over the mask forms
+ * them once per (batch entry, row block) before the attention kernel, on the
+ * same stream.  The results are the same bits either way.
+ *   workspace        device, 16-byte aligned, attn_prefill_workspace_bytes(d)
+ *                    bytes or more (GQA_ERR_WORKSPACE otherwise); ignored and
+ *                    may be NULL when mask is NULL
+ * The workspace holds no state between calls; calls that may run
+ * concurrently need their own. */
+gqa_status attn_prefill_ws(const gqa_attn_desc* d, const void* q, const void* k, const void* v,
+                           const float* q_descale, const float* k_descale, const float* v_descale,
+                           const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes attn_prefill_ws needs for a dense mask (host only): 2 bits
+ * per (row block, key tile); 0 for an invalid descriptor. */
+size_t attn_prefill_workspace_bytes(const gqa_attn_desc* d);
+
 /* -------------------------------------------------------- measurement --
  * Read-only HBM stream: reads every byte of `buf` once (128-bit non-temporal
  * loads, the decode kernels' loads) and writes nothing but, in a practically

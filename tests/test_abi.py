@@ -308,6 +308,50 @@ def test_prefill_pointer_mask_and_value_errors(lib):
     assert call_prefill(lib, ad(), scale=-1.0) == 7
 
 
+def call_prefill_ws(lib, desc, mask=ALIGNED, ws=ALIGNED, ws_bytes=None, **kw):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_prefill_workspace_bytes(ctypes.byref(desc))
+    a = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, qd=None, kd=None, vd=None, lens=None, out=ALIGNED, scale=1.0)
+    a.update(kw)
+    return lib.attn_prefill_ws(ctypes.byref(desc), a["q"], a["k"], a["v"], a["qd"], a["kd"], a["vd"], a["lens"],
+                               mask, a["scale"], a["out"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("B,S_q,S_k,h_q,n_kv", [(2, 64, 64, 8, 2), (4, 4096, 4096, 32, 8), (3, 1000, 70000, 8, 8),
+                                              (1, 33, 600000, 16, 2), (2, 300, 300, 12, 4)])
+def test_prefill_workspace_size(lib, B, S_q, S_k, h_q, n_kv):
+    """Two bitmaps per (batch entry, row block), one bit per 64-key tile,
+    at most 256 words each; a row block holds 32 rows for every wave of 8
+    that a head chunk leaves over (chunk = gcd(group size, 8))."""
+    G = h_q // n_kv
+    hc = next(c for c in (8, 4, 2, 1) if G % c == 0)
+    BM = 32 * (8 // hc)
+    words = min(-(-S_k // (64 * 32)), 256)
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(ad(B, S_q, S_k, h_q, n_kv))) == \
+        B * -(-S_q // BM) * 2 * words * 4
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(ad(B=0))) == 0
+    assert lib.attn_prefill_workspace_bytes(None) == 0
+
+
+def test_prefill_workspace_errors(lib):
+    """attn_prefill_ws checks what attn_prefill checks, and with a mask a
+    workspace of attn_prefill_workspace_bytes, 16-byte aligned."""
+    desc = ad()
+    need = lib.attn_prefill_workspace_bytes(ctypes.byref(desc))
+    assert need > 0
+    assert call_prefill_ws(lib, desc, ws=None) == 5
+    assert call_prefill_ws(lib, desc, ws_bytes=need - 1) == 5
+    assert call_prefill_ws(lib, desc, ws=MISALIGNED) == 4
+    assert call_prefill_ws(lib, ad(S_k=66)) == 2
+    assert call_prefill_ws(lib, desc, q=None) == 1
+    assert call_prefill_ws(lib, desc, mask=MISALIGNED) == 4
+    assert call_prefill_ws(lib, desc, scale=-1.0) == 7
+    assert call_prefill_ws(lib, desc, scale=float("nan")) == 7
+    assert call_prefill_ws(lib, ad(dt=2)) == 1
+    # the workspace is checked before the scale: both are host checks
+    assert call_prefill_ws(lib, desc, ws=None, scale=-1.0) == 5
+
+
 @pytest.mark.parametrize("flags", [2, 4, -1, 1 << 30])
 def test_unknown_decode_flags_are_rejected(lib, flags):
     desc = dd(flags=flags)

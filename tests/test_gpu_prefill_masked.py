@@ -230,3 +230,46 @@ def test_zero_scale_gives_the_mean_of_visible_values(dtype):
     else:
         assert pu.max_err(out, ref) <= TOL
 
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("h_q,n_kv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("kind", ["random", "docs"])
+def test_mask_prepass_equals_in_kernel_scan(dtype, h_q, n_kv, kind):
+    """The pass that forms every row block's key-tile bitmaps once
+    (attn_prefill_ws) and the workgroups' own scans (attn_prefill) classify
+    the same tiles, so the outputs agree bit for bit; row blocks of 256, 128,
+    64 and 32 rows, key lengths, more keys than queries, and a workspace that
+    starts full of stale words (every word the kernel reads is rewritten)."""
+    w = wl(3, 300, 520, h_q, n_kv, 128, True, seed=500 + h_q + n_kv, mask=kind, doc_lens=(16, 120), dtype=dtype)
+    if kind == "docs":  # documents over the keys; the queries are the last 300 positions
+        m = inputs.draw_mask("docs", 3, 520, 520, w.seed, (16, 120))[:, 220:, :].contiguous()
+    else:
+        m = inputs.draw_mask("random", 3, 300, 520, w.seed)
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=[520, 333, 0], mask=m)
+    args = dict(causal=True, kv_lens=inp.kv_lens, mask=inp.mask, q_descale=inp.q_descale,
+                k_descale=inp.k_descale, v_descale=inp.v_descale)
+    desc = binding._attn_desc(inp.q, inp.k, inp.v, torch.empty(inp.q.shape, dtype=torch.bfloat16, device=DEV),
+                              True, inp.kv_lens, inp.mask)
+    nbytes = binding.attn_prefill_workspace_bytes(desc)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+    a = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, workspace=ws, **args)
+    b = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, mask_prepass=False, **args)
+    pu.sync()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    compare(inp, a)
+
+
+@pytest.mark.parametrize("name", sorted(inputs.MASKED_PREFILL_WORKLOADS))
+def test_full_size_mask_prepass_equals_in_kernel_scan(name):
+    """The benchmarked masked workloads: both ways of classifying key tiles
+    give the same bits over the whole output."""
+    w = inputs.MASKED_PREFILL_WORKLOADS[name]
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV)
+    if inp.mask is None:
+        pytest.skip("no dense mask in this workload")
+    args = dict(causal=w.causal, kv_lens=inp.kv_lens, mask=inp.mask, q_descale=inp.q_descale,
+                k_descale=inp.k_descale, v_descale=inp.v_descale)
+    a = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, **args)
+    b = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, mask_prepass=False, **args)
+    pu.sync()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -25,7 +25,8 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_NULL", 2: "GQA_ERR_SHAPE", 3: "GQA_ERR_DTYPE"
 EXPORTED = ("attn_decode_num_splits", "attn_decode_workspace_bytes", "attn_decode", "attn_decode_partials",
             "attn_decode_combine", "attn_decode_paged_num_splits", "attn_decode_paged_workspace_bytes",
             "attn_decode_paged", "attn_decode_mla_num_splits", "attn_decode_mla_workspace_bytes",
-            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "attn_prefill", "gqa_status_string", "gqa_last_hip_error",
+            "attn_decode_mla", "attn_decode_mla_partials", "attn_decode_mla_combine", "attn_prefill_causal", "attn_prefill", "attn_prefill_ws", "attn_prefill_workspace_bytes",
+            "gqa_status_string", "gqa_last_hip_error",
             "attn_decode_noalloc", "attn_decode_noalloc_max_scratch_bytes", "gqa_stream_read")
 
 
@@ -107,6 +108,9 @@ def load_library(path=LIB_PATH):
     ad = ctypes.POINTER(gqa_attn_desc)
     lib.attn_prefill.argtypes = [ad, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp]
     lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_prefill_ws.argtypes = [ad, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, sz, vp]
+    lib.attn_prefill_ws.restype = ctypes.c_int
+    lib.attn_prefill_workspace_bytes.argtypes, lib.attn_prefill_workspace_bytes.restype = [ad], sz
     lib.attn_prefill_causal.restype = ctypes.c_int
     lib.gqa_stream_read.argtypes, lib.gqa_stream_read.restype = [vp, sz, vp, vp], ctypes.c_int
     lib.gqa_status_string.argtypes, lib.gqa_status_string.restype = [ctypes.c_int], cp
@@ -524,30 +528,61 @@ def _descale_checks(q, k, descales):
             raise ValueError(f"{name} must be a contiguous float32 tensor of shape [B, {H}]")
 
 
+def attn_prefill_workspace_bytes(desc):
+    """Bytes of workspace attn_prefill_ws needs for a masked call (the
+    per-row-block key-tile bitmaps)."""
+    return load_library().attn_prefill_workspace_bytes(ctypes.byref(desc))
+
+
 def attn_prefill(q, k, v, scale, causal=True, kv_lens=None, mask=None, out=None, q_descale=None, k_descale=None,
-                 v_descale=None, stream=None):
+                 v_descale=None, stream=None, workspace=None, mask_prepass=True):
     """out[B, S_q, h_q, d] (bf16) = attention of q [B,S_q,h_q,d] over k/v [B,S_k,n_kv,d] with the causal rule
     (end-aligned), key lengths and a dense [B, S_q, S_k] mask.  Operands are bf16, or uint8 e4m3 codes with
-    per-(batch, head) descale factors (see attn_prefill in gqa_attn.h)."""
+    per-(batch, head) descale factors (see attn_prefill in gqa_attn.h).
+
+    With a mask and `mask_prepass` (the default) the call goes through
+    attn_prefill_ws: one pass classifies every row block's key tiles into
+    `workspace` (allocated on the call's stream when None) and the attention
+    kernel reads those bitmaps.  `mask_prepass=False` calls attn_prefill,
+    whose workgroups each scan their own mask rows; both give the same bits."""
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     desc = _attn_desc(q, k, v, out, causal, kv_lens, mask)
     _descale_checks(q, k, (q_descale, k_descale, v_descale))
-    _check(load_library().attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale),
-                                       _ptr(k_descale), _ptr(v_descale), _ptr(kv_lens), _ptr(mask), float(scale),
-                                       _ptr(out), _stream(stream)))
+    lib = load_library()
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+            _ptr(kv_lens), _ptr(mask), float(scale), _ptr(out))
+    if mask is None or not mask_prepass:
+        if workspace is not None:
+            raise ValueError("a workspace goes with a masked call through the pre-pass only")
+        _check(lib.attn_prefill(*head, _stream(stream)))
+        return out
+    if workspace is None:
+        workspace = _temp_workspace(attn_prefill_workspace_bytes(desc), q.device, stream)
+    _check(lib.attn_prefill_ws(*head, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)))
     return out
 
 
 def prepare_prefill(q, k, v, scale, out, causal=True, kv_lens=None, mask=None, q_descale=None, k_descale=None,
-                    v_descale=None, stream=None):
-    """PreparedCall of attn_prefill."""
+                    v_descale=None, stream=None, workspace=None):
+    """PreparedCall of attn_prefill, or of attn_prefill_ws when a workspace
+    (at least attn_prefill_workspace_bytes) is given with a mask."""
     desc = _attn_desc(q, k, v, out, causal, kv_lens, mask)
     _descale_checks(q, k, (q_descale, k_descale, v_descale))
     lib = load_library()
-    call = PreparedCall(lib.attn_prefill, (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale),
-                                           _ptr(k_descale), _ptr(v_descale), _ptr(kv_lens), _ptr(mask),
-                                           ctypes.c_float(scale), _ptr(out)), stream, out)
+    head = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+            _ptr(kv_lens), _ptr(mask), ctypes.c_float(scale), _ptr(out))
+    if workspace is None:
+        call = PreparedCall(lib.attn_prefill, head, stream, out)
+    else:
+        if mask is None:
+            raise ValueError("a workspace goes with a masked call only")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        if ws_bytes < attn_prefill_workspace_bytes(desc):
+            raise ValueError("workspace smaller than attn_prefill_workspace_bytes")
+        call = PreparedCall(lib.attn_prefill_ws, head + (_ptr(workspace), ctypes.c_size_t(ws_bytes)), stream, out)
+        call._keep_ws = workspace
     call._keep = (desc,)
     return call
 

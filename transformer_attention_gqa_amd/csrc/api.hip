@@ -558,9 +558,10 @@ gqa_status attn_decode_mla(const gqa_mla_desc* d, const void* q_abs, const void*
   return attn_decode_mla_combine(d, seq_lens, workspace, workspace_bytes, out, stream);
 }
 
-gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, const void* v, const float* q_descale,
-                        const float* k_descale, const float* v_descale, const int32_t* kv_lens, const uint8_t* mask,
-                        float scale, void* out, hipStream_t stream) {
+namespace {
+
+// Shape checks of a general-mask prefill descriptor (host only).
+gqa_status check_attn_desc(const gqa_attn_desc* d, bool has_mask) {
   if (!d) return GQA_ERR_NULL;
   if (d->B <= 0 || d->S_q <= 0 || d->S_k <= 0 || d->h_q <= 0 || d->n_kv <= 0 || d->d_h <= 0) return GQA_ERR_SHAPE;
   if (d->h_q % d->n_kv != 0) return GQA_ERR_SHAPE;
@@ -569,9 +570,18 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
   if ((int64_t)d->B * d->S_q * d->h_q > (int64_t)1 << 31) return GQA_ERR_SHAPE;
   if ((int64_t)d->B * d->S_k * d->n_kv > (int64_t)1 << 31) return GQA_ERR_SHAPE;
   // 4-key mask words; a workgroup's mask rows (up to 256) within a 31-bit buffer range
-  if (mask && (d->S_k % 4 != 0 || d->S_k > (1 << 23))) return GQA_ERR_SHAPE;
+  if (has_mask && (d->S_k % 4 != 0 || d->S_k > (1 << 23))) return GQA_ERR_SHAPE;
+  if (d->dtype != GQA_BF16 && d->dtype != GQA_FP8_E4M3) return GQA_ERR_DTYPE;
+  return GQA_OK;
+}
+
+gqa_status prefill_general(const gqa_attn_desc* d, const void* q, const void* k, const void* v,
+                           const float* q_descale, const float* k_descale, const float* v_descale,
+                           const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, bool with_workspace, hipStream_t stream) {
+  gqa_status st = check_attn_desc(d, mask != nullptr);
+  if (st != GQA_OK) return st;
   const bool fp8 = d->dtype == GQA_FP8_E4M3;
-  if (d->dtype != GQA_BF16 && !fp8) return GQA_ERR_DTYPE;
   if (!fp8 && (q_descale || k_descale || v_descale)) return GQA_ERR_DTYPE;
   if (!q || !k || !v || !out) return GQA_ERR_NULL;
   if (fp8 && (!q_descale || !k_descale || !v_descale)) return GQA_ERR_NULL;
@@ -580,18 +590,47 @@ gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, co
   if (((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
         reinterpret_cast<uintptr_t>(v_descale)) & 3u) != 0)
     return GQA_ERR_ALIGN;
+  uint32_t* mask_tiles = nullptr;
+  if (with_workspace && mask) {
+    if (!workspace || workspace_bytes < prefill_mask_tiles_bytes(d->B, d->S_q, d->S_k, d->h_q, d->n_kv))
+      return GQA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return GQA_ERR_ALIGN;
+    mask_tiles = static_cast<uint32_t*>(workspace);
+  }
   if (bad_scale(scale)) return GQA_ERR_VALUE;
   const float sl2 = qk_scale_log2(scale);
   const hipError_t e =
       fp8 ? launch_prefill_fp8(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal, kv_lens, mask,
-                               q_descale, k_descale, v_descale, stream)
+                               q_descale, k_descale, v_descale, mask_tiles, stream)
           : launch_prefill_masked(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal,
-                                  kv_lens, mask, stream);
+                                  kv_lens, mask, mask_tiles, stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;
   }
   return GQA_OK;
+}
+
+}  // namespace
+
+gqa_status attn_prefill(const gqa_attn_desc* d, const void* q, const void* k, const void* v, const float* q_descale,
+                        const float* k_descale, const float* v_descale, const int32_t* kv_lens, const uint8_t* mask,
+                        float scale, void* out, hipStream_t stream) {
+  return prefill_general(d, q, k, v, q_descale, k_descale, v_descale, kv_lens, mask, scale, out, nullptr, 0, false,
+                         stream);
+}
+
+gqa_status attn_prefill_ws(const gqa_attn_desc* d, const void* q, const void* k, const void* v,
+                           const float* q_descale, const float* k_descale, const float* v_descale,
+                           const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return prefill_general(d, q, k, v, q_descale, k_descale, v_descale, kv_lens, mask, scale, out, workspace,
+                         workspace_bytes, true, stream);
+}
+
+size_t attn_prefill_workspace_bytes(const gqa_attn_desc* d) {
+  if (check_attn_desc(d, false) != GQA_OK) return 0;
+  return prefill_mask_tiles_bytes(d->B, d->S_q, d->S_k, d->h_q, d->n_kv);
 }
 
 gqa_status gqa_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
@@ -615,7 +654,7 @@ const char* gqa_status_string(gqa_status s) {
     case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: pointer not 16-byte aligned";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: HIP launch failed";
-    case GQA_ERR_VALUE: return "GQA_ERR_VALUE: scale not finite and > 0, or unknown flag bits";
+    case GQA_ERR_VALUE: return "GQA_ERR_VALUE: scale not finite and >= 0, or unknown flag bits";
     case GQA_ERR_SCRATCH:
       return "GQA_ERR_SCRATCH: the call needs more partial rows than the library's static scratch holds";
   }

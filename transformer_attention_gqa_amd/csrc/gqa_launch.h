@@ -71,15 +71,20 @@ hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hip
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S, int h_q, int n_kv, int D, hipStream_t stream);
 // General masks: S_q query rows, S_k keys, optional end-aligned causal rule,
-// key lengths [B] and dense mask [B][S_q][S_k] (nonzero = visible).
+// key lengths [B] and dense mask [B][S_q][S_k] (nonzero = visible).  With a
+// mask and mask_tiles (prefill_mask_tiles_bytes bytes), a pass over the mask
+// forms every row block's key-tile bitmaps there first; mask_tiles null: each
+// workgroup scans its own mask rows.
 hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
-                                 const uint8_t* mask, hipStream_t stream);
+                                 const uint8_t* mask, uint32_t* mask_tiles, hipStream_t stream);
 // fp8 (e4m3) q/k/v with per-(batch, head) descale factors, d = 64 or 128, general masks.
 hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                               int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                               const uint8_t* mask, const float* q_descale, const float* k_descale,
-                              const float* v_descale, hipStream_t stream);
+                              const float* v_descale, uint32_t* mask_tiles, hipStream_t stream);
+// Bytes of the key-tile bitmaps of all row blocks (see launch_prefill_masked).
+size_t prefill_mask_tiles_bytes(int B, int S_q, int S_k, int h_q, int n_kv);
 
 // Read-only stream over `bytes` (a multiple of 16) at `buf`: the measured HBM
 // read ceiling.  One workgroup of 512 threads per compute unit.

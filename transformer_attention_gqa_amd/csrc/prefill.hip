@@ -48,6 +48,11 @@ struct PrefillArgs {
   int causal;               // query r sees keys c <= r + S_k - S_q
   const int32_t* kv_lens;   // [B] or null: keys c >= kv_lens[b] are invisible and never read
   const uint8_t* mask;      // [B][S][S_k] or null: key c invisible to row r where 0
+  // with a mask: the row blocks' key-tile bitmaps, formed by a pass over the
+  // mask before the kernel (null: each workgroup scans its mask rows);
+  // [B][n_qb][2][mt_words] (visible, then fully visible)
+  const uint32_t* mask_tiles;
+  int mt_words;
   // fp8 kernel: q/k/v hold e4m3 codes; value = code * descale[b][head]
   const float* q_descale;   // [B][h_q]
   const float* k_descale;   // [B][n_kv]
@@ -63,6 +68,71 @@ constexpr int kBN = 64;  // keys per tile
 constexpr int kMaskGroupBlock = 4;
 constexpr int kNumXcd = 8;
 constexpr int kWaves = 8;  // wavefronts per workgroup
+
+// Key-tile bitmaps of one row block (BM rows from the block's first) under a
+// dense mask, into the workgroup's LDS words vis / full (kVisWords each): bit j
+// of vis is set when some mask byte of the rows over the keys of tile j is
+// nonzero, bit j of full when none of them is zero.  mrsrc covers the block's
+// mask rows; rows past nrows are not read.  Four lanes cover one row's 64
+// bytes of a tile, so a load instruction reads 16 rows x 64 consecutive bytes
+// (16 cache-line requests, not 64); a pass loads TPI tiles of all BM rows,
+// about 16 loads in flight.  Called by all kWaves waves of the workgroup.
+constexpr int kVisWords = 256;  // up to 8192 key tiles
+template <int BM>
+__device__ void scan_mask_tiles(__amdgpu_buffer_rsrc_t mrsrc, int n_tiles, int nrows, int SK, uint32_t* vis,
+                                uint32_t* full, int wave, int lane, int tid) {
+  for (int i = tid; i < kVisWords; i += kWaves * 64) {
+    vis[i] = 0u;
+    full[i] = 0u;
+  }
+  __syncthreads();
+  static_assert(kBN == 64, "the scan assumes 64-key tiles");
+  constexpr int NRG = BM / 16;                    // 16-row groups of the block
+  constexpr int TPI = NRG >= 16 ? 1 : 16 / NRG;  // tiles per wave and pass
+  for (int j0 = wave; j0 < n_tiles; j0 += TPI * kWaves) {
+    uint32_t any[TPI], zero[TPI];
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      any[u] = 0u;
+      zero[u] = 0u;
+    }
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) {
+      const int r = 16 * g + (lane >> 2);
+      if (r < nrows) {
+#pragma unroll
+        for (int u = 0; u < TPI; ++u) {
+          const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((j0 + u * kWaves) * kBN + 16 * (lane & 3));
+          const u32x4 mv = buffer_load_x4(mrsrc, off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            any[u] |= mv[e];
+            zero[u] |= (mv[e] - 0x01010101u) & ~mv[e] & 0x80808080u;  // nonzero iff a byte is 0
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      const int j = j0 + u * kWaves;
+      const bool v = __builtin_amdgcn_ballot_w64(any[u] != 0u) != 0;
+      const bool f = __builtin_amdgcn_ballot_w64(zero[u] != 0u) == 0;
+      if (j < n_tiles && lane == 0) {
+        if (v) atomicOr(&vis[j >> 5], 1u << (j & 31));
+        if (f) atomicOr(&full[j >> 5], 1u << (j & 31));
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Key tiles a row block [blk0, row_end) must consider: those holding keys
+// below the last row's visible prefix (the causal rule, end-aligned, and the
+// key length), before any dense mask.
+__device__ __forceinline__ int block_key_tiles(int row_end, int S, int SK, int kv_n, int causal) {
+  const int kend = causal ? max(min(kv_n, min(row_end - 1, S - 1) + 1 + SK - S), 0) : kv_n;
+  return (kend + kBN - 1) / kBN;
+}
 
 // GEN = false: causal self-attention, S_q = S_k, every key of a row's causal
 // range visible.  GEN = true: S_q and S_k independent, the causal rule
@@ -210,7 +280,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       return a.causal ? max(min(kv_n, min(row, S - 1) + 1 + SK - S), 0) : kv_n;
     }
   };
-  const int n_tiles = (kend_of(row_end - 1) + kBN - 1) / kBN;  // key tiles 0 .. n_tiles-1 (0: no visible key)
+  // key tiles 0 .. n_tiles-1 (0: no visible key)
+  const int n_tiles = GEN ? block_key_tiles(row_end, S, SK, kv_n, a.causal) : (kend_of(row_end - 1) + kBN - 1) / kBN;
   const int wave_kend = kend_of(row0 + 31);  // the wave's rows see keys below this
   const int wave_kmin = kend_of(row0);       // ... and all of them see keys below this
   const int lane_kend = kend_of(qrow);
@@ -333,59 +404,25 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // cannot see by the causal rule or the key length still count (a tile
   // visited for nothing, or masked needlessly, gives the same result).
   // Blocks with more tiles than the bitmaps hold visit every tile, masked.
-  constexpr int kVisWords = has_mask ? 256 : 1;  // up to 8192 key tiles
-  __shared__ uint32_t s_vis[kVisWords];
-  __shared__ uint32_t s_full[kVisWords];
+  constexpr int kVis = has_mask ? kVisWords : 1;
+  __shared__ uint32_t s_vis[kVis];
+  __shared__ uint32_t s_full[kVis];
   const bool skip_tiles = has_mask && n_tiles <= kVisWords * 32;
   int n_steps = n_tiles;  // key tiles the loop visits
   if (skip_tiles) {
-    for (int i = tid; i < kVisWords; i += kWaves * 64) {
-      s_vis[i] = 0u;
-      s_full[i] = 0u;
-    }
-    __syncthreads();
-    const int nrows = min(BM, S - blk0);
-    // four lanes cover one row's 64 bytes of a tile, so a load instruction
-    // reads 16 rows x 64 consecutive bytes (16 cache-line requests, not 64);
-    // a pass loads TPI tiles of all BM rows, about 16 loads in flight
-    static_assert(kBN == 64, "the scan assumes 64-key tiles");
-    constexpr int NRG = BM / 16;                    // 16-row groups of the block
-    constexpr int TPI = NRG >= 16 ? 1 : 16 / NRG;  // tiles per wave and pass
-    for (int j0 = wave; j0 < n_tiles; j0 += TPI * kWaves) {
-      uint32_t any[TPI], zero[TPI];
-#pragma unroll
-      for (int u = 0; u < TPI; ++u) {
-        any[u] = 0u;
-        zero[u] = 0u;
-      }
-#pragma unroll
-      for (int g = 0; g < NRG; ++g) {
-        const int r = 16 * g + (lane >> 2);
-        if (r < nrows) {
-#pragma unroll
-          for (int u = 0; u < TPI; ++u) {
-            const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((j0 + u * kWaves) * kBN + 16 * (lane & 3));
-            const u32x4 mv = buffer_load_x4(mrsrc, off);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              any[u] |= mv[e];
-              zero[u] |= (mv[e] - 0x01010101u) & ~mv[e] & 0x80808080u;  // nonzero iff a byte is 0
-            }
-          }
+    if constexpr (has_mask) {
+      if (a.mask_tiles) {
+        // formed by the pass over the mask before this kernel
+        const uint32_t* src = a.mask_tiles + ((size_t)b * a.n_qb + qb) * 2 * a.mt_words;
+        for (int i = tid; i < (n_tiles + 31) / 32; i += kWaves * 64) {
+          s_vis[i] = src[i];
+          s_full[i] = src[a.mt_words + i];
         }
-      }
-#pragma unroll
-      for (int u = 0; u < TPI; ++u) {
-        const int j = j0 + u * kWaves;
-        const bool vis = __builtin_amdgcn_ballot_w64(any[u] != 0u) != 0;
-        const bool full = __builtin_amdgcn_ballot_w64(zero[u] != 0u) == 0;
-        if (j < n_tiles && lane == 0) {
-          if (vis) atomicOr(&s_vis[j >> 5], 1u << (j & 31));
-          if (full) atomicOr(&s_full[j >> 5], 1u << (j & 31));
-        }
+        __syncthreads();
+      } else {
+        scan_mask_tiles<BM>(mrsrc, n_tiles, min(BM, S - blk0), SK, s_vis, s_full, wave, lane, tid);
       }
     }
-    __syncthreads();
     int cnt = 0;
     for (int i = lane; i < (n_tiles + 31) / 32; i += 64) cnt += __popc(s_vis[i]);
 #pragma unroll
@@ -718,6 +755,35 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_fp8_kernel(Prefill
   prefill_body<D, HC, true, true, MASK>(a);
 }
 
+// The key-tile bitmaps of every (batch entry, row block) under a dense mask,
+// formed once for all the K/V-head workgroups that share the block's mask
+// rows: one workgroup per row block (grid n_qb x B), the same scan as a
+// masked workgroup's own.  Blocks with more key tiles than the bitmaps hold
+// are skipped (their workgroups visit every tile).
+template <int BM>
+__global__ __launch_bounds__(kWaves * 64, 1) void gqa_mask_tiles_kernel(PrefillArgs a) {
+  __shared__ uint32_t vis[kVisWords];
+  __shared__ uint32_t full[kVisWords];
+  const int qb = blockIdx.x, b = blockIdx.y;
+  const int S = a.S, SK = a.S_k;
+  const int blk0 = qb * BM;
+  const int row_end = min(blk0 + BM, S);
+  const int kv_n = a.kv_lens ? min(max(a.kv_lens[b], 0), SK) : SK;
+  const int n_tiles = block_key_tiles(row_end, S, SK, kv_n, a.causal);
+  if (n_tiles == 0 || n_tiles > kVisWords * 32) return;  // uniform over the workgroup
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const __amdgpu_buffer_rsrc_t mrsrc =
+      make_rsrc(a.mask + ((size_t)b * S + blk0) * SK, (int)((unsigned)(row_end - blk0) * (unsigned)SK));
+  scan_mask_tiles<BM>(mrsrc, n_tiles, row_end - blk0, SK, vis, full, wave, lane, tid);
+  uint32_t* dst = const_cast<uint32_t*>(a.mask_tiles) + ((size_t)b * a.n_qb + qb) * 2 * a.mt_words;
+  for (int i = tid; i < (n_tiles + 31) / 32; i += kWaves * 64) {
+    dst[i] = vis[i];
+    dst[a.mt_words + i] = full[i];
+  }
+}
+
 static int gcd_int(int x, int y) {
   while (y) {
     const int t = x % y;
@@ -750,6 +816,8 @@ static PrefillArgs prefill_args(const void* q, const void* k, const void* v, voi
   a.causal = 1;
   a.kv_lens = nullptr;
   a.mask = nullptr;
+  a.mask_tiles = nullptr;
+  a.mt_words = 0;
   a.q_descale = nullptr;
   a.k_descale = nullptr;
   a.v_descale = nullptr;
@@ -777,9 +845,33 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   return hipGetLastError();
 }
 
+// Words per bitmap of one row block's key tiles (S_k keys, at most kVisWords).
+static int mask_tile_words(int S_k) { return min((S_k + kBN * 32 - 1) / (kBN * 32), kVisWords); }
+
+size_t prefill_mask_tiles_bytes(int B, int S_q, int S_k, int h_q, int n_kv) {
+  const int BM = 32 * (kWaves / gcd_int(h_q / n_kv, kWaves));
+  return (size_t)B * ((S_q + BM - 1) / BM) * 2 * mask_tile_words(S_k) * sizeof(uint32_t);
+}
+
+// With a mask and a bitmap buffer: the pass that forms every row block's
+// bitmaps, launched before the attention kernel on the same stream.
+static hipError_t launch_mask_tiles(PrefillArgs& a, uint32_t* mask_tiles, int HC, hipStream_t stream) {
+  if (!a.mask || !mask_tiles) return hipSuccess;
+  a.mask_tiles = mask_tiles;
+  a.mt_words = mask_tile_words(a.S_k);
+  const dim3 grid(a.n_qb, a.B), block(kWaves * 64);
+  switch (kWaves / HC) {
+    case 1: hipLaunchKernelGGL((gqa_mask_tiles_kernel<32>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gqa_mask_tiles_kernel<64>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gqa_mask_tiles_kernel<128>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((gqa_mask_tiles_kernel<256>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
-                                 const uint8_t* mask, hipStream_t stream) {
+                                 const uint8_t* mask, uint32_t* mask_tiles, hipStream_t stream) {
   const int HC = gcd_int(h_q / n_kv, kWaves);
   PrefillArgs a = prefill_args(q, k, v, out, qk_scale_log2, B, S_q, h_q, n_kv, HC);
   a.S_k = S_k;
@@ -787,6 +879,7 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
   a.kv_lens = kv_lens;
   a.mask = mask;
   if (mask) a.grp_block = kMaskGroupBlock;
+  if (const hipError_t e = launch_mask_tiles(a, mask_tiles, HC, stream); e != hipSuccess) return e;
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
 #define GQA_LAUNCH_PREFILL(DD, HH)                                                                       \
   do {                                                                                                   \
@@ -811,7 +904,7 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
 hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                               int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                               const uint8_t* mask, const float* q_descale, const float* k_descale,
-                              const float* v_descale, hipStream_t stream) {
+                              const float* v_descale, uint32_t* mask_tiles, hipStream_t stream) {
   const int HC = gcd_int(h_q / n_kv, kWaves);
   PrefillArgs a = prefill_args(q, k, v, out, qk_scale_log2, B, S_q, h_q, n_kv, HC);
   a.S_k = S_k;
@@ -822,6 +915,7 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void*
   a.k_descale = k_descale;
   a.v_descale = v_descale;
   if (mask) a.grp_block = kMaskGroupBlock;
+  if (const hipError_t e = launch_mask_tiles(a, mask_tiles, HC, stream); e != hipSuccess) return e;
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
 #define GQA_LAUNCH_FP8(DD, HH)                                                                          \
   do {                                                                                                  \
