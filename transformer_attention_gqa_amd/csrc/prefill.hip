@@ -43,6 +43,7 @@ struct PrefillArgs {
   int B, S, h_q, n_kv;  // S = query rows (S_q)
   int n_qb, n_hc, n_wg, n_wg_pad;
   int grp_block;            // groups (batch, K/V head, head chunk) interleaved per row block (1: none)
+  int batch_minor;          // groups numbered batch entry fastest (1) or K/V head chunk fastest (0)
   // general masks (the masked kernel only)
   int S_k;                  // keys per sequence
   int causal;               // query r sees keys c <= r + S_k - S_q
@@ -214,9 +215,19 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     grp = blk * a.grp_block + (r - qr * ng);
     qb = a.n_qb - 1 - qr;
   }
-  const int hc = grp % a.n_hc;
-  const int g = (grp / a.n_hc) % a.n_kv;
-  const int b = grp / (a.n_hc * a.n_kv);
+  // batch entry fastest: the groups one XCD takes come from every batch
+  // entry, so batch entries of unequal work (key lengths, documents) spread
+  // over all XCDs instead of loading the XCDs they land on
+  int hc, g, b;
+  if (a.batch_minor) {
+    b = grp % a.B;
+    hc = (grp / a.B) % a.n_hc;
+    g = grp / (a.B * a.n_hc);
+  } else {
+    hc = grp % a.n_hc;
+    g = (grp / a.n_hc) % a.n_kv;
+    b = grp / (a.n_hc * a.n_kv);
+  }
   const int G = a.h_q / a.n_kv;
 
   const int tid = threadIdx.x;
@@ -725,18 +736,43 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // ---- epilogue: O / l -> bf16, rows < S only
   const float lt = l + __shfl_xor(l, 32, 64);
   const float inv = lt > 0.f ? out_scale / lt : 0.f;  // fp8: the V descale folds in here
-  if (qrow < S) {
-    uint16_t* op = a.out + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D;
+  // Through LDS: a lane holds 8 bytes of each of 16 chunks of its row, so
+  // direct stores would touch 32 rows per instruction.  The wave writes its
+  // 32-row tile into its own LDS region (half a K/V buffer, free after the
+  // last step's barrier), in NPASS column slices when the region is smaller
+  // than the tile (fp8 buffers), 16-byte chunk c of row r at chunk position
+  // c ^ (r % CO), and stores whole row slices back, CO lanes per row, 16
+  // bytes each.
+  constexpr int OUT_BYTES = 32 * D * 2;                   // the wave's bf16 output tile
+  constexpr int REGION = OUT_BYTES < TILE_BYTES / 2 ? OUT_BYTES : TILE_BYTES / 2;
+  constexpr int NPASS = OUT_BYTES / REGION;
+  constexpr int DP = D / NPASS;                           // columns per pass
+  constexpr int CO = DP / 8;                              // 16-byte chunks per row slice
+  constexpr int RPS = 64 / CO;                            // rows per store instruction
+  static_assert(NPASS * REGION == OUT_BYTES && (NT / NPASS) * NPASS == NT, "output passes split the d tiles");
+  char* ep = (wave < 2 ? sk0 : wave < 4 ? sk1 : wave < 6 ? sv0 : sv1) + (wave & 1) * REGION;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  for (int ps = 0; ps < NPASS; ++ps) {
+#pragma unroll
+    for (int ntp = 0; ntp < NT / NPASS; ++ntp)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = 32 * nt + 8 * rq + 4 * h2;
+        const int nt = ps * (NT / NPASS) + ntp;
+        const int c = 4 * ntp + rq;  // chunk of d 32nt + 8rq .. +7 in this slice
         u32x2 w;
         w[0] = pack_bf16x2(o[nt][4 * rq + 0] * inv, o[nt][4 * rq + 1] * inv);
         w[1] = pack_bf16x2(o[nt][4 * rq + 2] * inv, o[nt][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+        *reinterpret_cast<u32x2*>(ep + l32 * (DP * 2) + ((c ^ (l32 % CO)) << 4) + 8 * h2) = w;
       }
+    const int c = lane % CO;
+#pragma unroll
+    for (int t = 0; t < 32 / RPS; ++t) {
+      const int r = RPS * t + lane / CO;
+      const u32x4 v = lds_load<u32x4>(ep + r * (DP * 2) + ((c ^ (r % CO)) << 4));
+      if (row0 + r < S)
+        *reinterpret_cast<u32x4*>(a.out + ((size_t)b * S + row0 + r) * q_row_stride + (size_t)head * D + ps * DP +
+                                  8 * c) = v;
+    }
   }
 }
 
@@ -812,6 +848,7 @@ static PrefillArgs prefill_args(const void* q, const void* k, const void* v, voi
   a.n_wg = B * n_kv * a.n_hc * a.n_qb;
   a.n_wg_pad = (a.n_wg + kNumXcd - 1) / kNumXcd * kNumXcd;
   a.grp_block = 1;
+  a.batch_minor = 0;
   a.S_k = S;
   a.causal = 1;
   a.kv_lens = nullptr;
@@ -869,6 +906,18 @@ static hipError_t launch_mask_tiles(PrefillArgs& a, uint32_t* mask_tiles, int HC
   return hipGetLastError();
 }
 
+// Work order of the general kernels.  Without a dense mask, groups go batch
+// entry fastest, which spreads batch entries of unequal key lengths over the
+// XCDs: padded workload (4 x 4096, key lengths 2597..3954, 32/8 heads) 913 ->
+// 811 us.  With a mask, a batch entry's groups run interleaved per row block
+// on one XCD, sharing its mask rows in L2; measured on the packed-document
+// workload, batch entry fastest lost there (with the bitmaps formed
+// beforehand: 276 -> 282 us, and 320 us with the interleave kept).
+static void set_work_order(PrefillArgs& a) {
+  a.grp_block = a.mask ? kMaskGroupBlock : 1;
+  a.batch_minor = a.mask ? 0 : 1;
+}
+
 hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                                  const uint8_t* mask, uint32_t* mask_tiles, hipStream_t stream) {
@@ -878,8 +927,8 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
   a.causal = causal;
   a.kv_lens = kv_lens;
   a.mask = mask;
-  if (mask) a.grp_block = kMaskGroupBlock;
   if (const hipError_t e = launch_mask_tiles(a, mask_tiles, HC, stream); e != hipSuccess) return e;
+  set_work_order(a);
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
 #define GQA_LAUNCH_PREFILL(DD, HH)                                                                       \
   do {                                                                                                   \
@@ -914,8 +963,8 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void*
   a.q_descale = q_descale;
   a.k_descale = k_descale;
   a.v_descale = v_descale;
-  if (mask) a.grp_block = kMaskGroupBlock;
   if (const hipError_t e = launch_mask_tiles(a, mask_tiles, HC, stream); e != hipSuccess) return e;
+  set_work_order(a);
   const dim3 grid(a.n_wg_pad), block(kWaves * 64);
 #define GQA_LAUNCH_FP8(DD, HH)                                                                          \
   do {                                                                                                  \
