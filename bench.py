@@ -592,8 +592,9 @@ def _workload_launches():
         out.append(((kname, targs, grid),
                     (f"prefill_masked:{wl.name}", wl.name, roofline.prefill_masked_flops(wl.h_q, wl.d_h, pairs),
                      "flops")))
-        if wl.mask:  # the pass over the mask: one workgroup of 512 per (row block, batch entry)
-            out.append((("gqa_mask_tiles_kernel", (str(bm),), -(-wl.S_q // bm) * wl.B * 512),
+        if wl.mask:  # the pass over the mask: one workgroup of 512 per (row block, batch entry, bitmap word)
+            words = min(-(-wl.S_k // (64 * 32)), 256)
+            out.append((("gqa_mask_tiles_kernel", (str(bm),), -(-wl.S_q // bm) * wl.B * words * 512),
                         (f"mask_tiles:{wl.name}", wl.name, None, None)))
     return out
 

@@ -74,55 +74,68 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // dense mask, into the workgroup's LDS words vis / full (kVisWords each): bit j
 // of vis is set when some mask byte of the rows over the keys of tile j is
 // nonzero, bit j of full when none of them is zero.  mrsrc covers the block's
-// mask rows; rows past nrows are not read.  Four lanes cover one row's 64
-// bytes of a tile, so a load instruction reads 16 rows x 64 consecutive bytes
-// (16 cache-line requests, not 64); a pass loads TPI tiles of all BM rows,
-// about 16 loads in flight.  Called by all kWaves waves of the workgroup.
+// mask rows; rows past nrows do not count.  Tiles j_begin .. j_end - 1 are
+// scanned (bits of other tiles stay clear).  The rows are read in order: a
+// load instruction covers 1 KiB of one row (16 tiles, four lanes a tile), each
+// wave takes BM / kWaves rows and issues the loads of two 16-tile segments of
+// all its rows before it uses any; the four lanes of a tile then combine by
+// shuffles, and the waves by LDS atomics (OR into vis, and into full as
+// "some byte is zero" bits, inverted at the end).  Called by all kWaves waves
+// of the workgroup.
 constexpr int kVisWords = 256;  // up to 8192 key tiles
 template <int BM>
-__device__ void scan_mask_tiles(__amdgpu_buffer_rsrc_t mrsrc, int n_tiles, int nrows, int SK, uint32_t* vis,
-                                uint32_t* full, int wave, int lane, int tid) {
+__device__ void scan_mask_tiles(__amdgpu_buffer_rsrc_t mrsrc, int j_begin, int j_end, int nrows, int SK,
+                                uint32_t* vis, uint32_t* full, int wave, int lane, int tid) {
   for (int i = tid; i < kVisWords; i += kWaves * 64) {
     vis[i] = 0u;
     full[i] = 0u;
   }
   __syncthreads();
   static_assert(kBN == 64, "the scan assumes 64-key tiles");
-  constexpr int NRG = BM / 16;                    // 16-row groups of the block
-  constexpr int TPI = NRG >= 16 ? 1 : 16 / NRG;  // tiles per wave and pass
-  for (int j0 = wave; j0 < n_tiles; j0 += TPI * kWaves) {
-    uint32_t any[TPI], zero[TPI];
+  constexpr int RPW = BM / kWaves;  // rows per wave
+  constexpr int RB = RPW < 8 ? RPW : 8;
+  const int s_end = (j_end + 15) >> 4;  // 16-tile segments
+  for (int s0 = j_begin >> 4; s0 < s_end; s0 += 2) {
+    uint32_t any[2] = {0u, 0u}, zero[2] = {0u, 0u};
+    // rows past nrows lie past the resource's range and read as zero: they
+    // are loaded like the others and only kept out of the zero test
+    for (int i0 = 0; i0 < RPW; i0 += RB) {  // RB rows' loads in flight at a time
 #pragma unroll
-    for (int u = 0; u < TPI; ++u) {
-      any[u] = 0u;
-      zero[u] = 0u;
-    }
+      for (int i = 0; i < RB; ++i) {
+        const int r = wave * RPW + i0 + i;
+        const uint32_t valid = r < nrows ? 0x80808080u : 0u;
 #pragma unroll
-    for (int g = 0; g < NRG; ++g) {
-      const int r = 16 * g + (lane >> 2);
-      if (r < nrows) {
-#pragma unroll
-        for (int u = 0; u < TPI; ++u) {
-          const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((j0 + u * kWaves) * kBN + 16 * (lane & 3));
-          const u32x4 mv = buffer_load_x4(mrsrc, off);
+        for (int u = 0; u < 2; ++u) {
+          const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((s0 + u) * 16 * kBN + 16 * lane);
+          const u32x4 mv = buffer_load_x4(mrsrc, off);  // past the last segment: unused
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             any[u] |= mv[e];
-            zero[u] |= (mv[e] - 0x01010101u) & ~mv[e] & 0x80808080u;  // nonzero iff a byte is 0
+            zero[u] |= (mv[e] - 0x01010101u) & ~mv[e] & valid;  // nonzero iff a byte is 0
           }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < TPI; ++u) {
-      const int j = j0 + u * kWaves;
-      const bool v = __builtin_amdgcn_ballot_w64(any[u] != 0u) != 0;
-      const bool f = __builtin_amdgcn_ballot_w64(zero[u] != 0u) == 0;
-      if (j < n_tiles && lane == 0) {
-        if (v) atomicOr(&vis[j >> 5], 1u << (j & 31));
-        if (f) atomicOr(&full[j >> 5], 1u << (j & 31));
+    for (int u = 0; u < 2; ++u) {
+      uint32_t av = any[u], zv = zero[u];
+      av |= __shfl_xor(av, 1, 64);
+      zv |= __shfl_xor(zv, 1, 64);
+      av |= __shfl_xor(av, 2, 64);
+      zv |= __shfl_xor(zv, 2, 64);
+      const int j = (s0 + u) * 16 + (lane >> 2);
+      if ((lane & 3) == 0 && j >= j_begin && j < j_end) {
+        if (av) atomicOr(&vis[j >> 5], 1u << (j & 31));
+        if (zv) atomicOr(&full[j >> 5], 1u << (j & 31));
       }
     }
+  }
+  __syncthreads();
+  // full held "some byte is zero": invert it over the scanned tiles
+  for (int i = tid; i < kVisWords; i += kWaves * 64) {
+    const int lo = max(j_begin - 32 * i, 0), hi = min(j_end - 32 * i, 32);
+    const uint32_t range = lo >= hi ? 0u : (hi == 32 ? ~0u : (1u << hi) - 1u) & ~((1u << lo) - 1u);
+    full[i] = ~full[i] & range;
   }
   __syncthreads();
 }
@@ -431,7 +444,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
         }
         __syncthreads();
       } else {
-        scan_mask_tiles<BM>(mrsrc, n_tiles, min(BM, S - blk0), SK, s_vis, s_full, wave, lane, tid);
+        scan_mask_tiles<BM>(mrsrc, 0, n_tiles, min(BM, S - blk0), SK, s_vis, s_full, wave, lane, tid);
       }
     }
     int cnt = 0;
@@ -793,30 +806,33 @@ __global__ __launch_bounds__(kWaves * 64, 1) void gqa_prefill_fp8_kernel(Prefill
 
 // The key-tile bitmaps of every (batch entry, row block) under a dense mask,
 // formed once for all the K/V-head workgroups that share the block's mask
-// rows: one workgroup per row block (grid n_qb x B), the same scan as a
-// masked workgroup's own.  Blocks with more key tiles than the bitmaps hold
-// are skipped (their workgroups visit every tile).
+// rows: one workgroup per row block and 32-tile word of its bitmaps (grid
+// n_qb x B x words), the same scan as a masked workgroup's own over that
+// word's tiles.  Blocks with more key tiles than the bitmaps hold are
+// skipped (their workgroups visit every tile).
 template <int BM>
 __global__ __launch_bounds__(kWaves * 64, 1) void gqa_mask_tiles_kernel(PrefillArgs a) {
   __shared__ uint32_t vis[kVisWords];
   __shared__ uint32_t full[kVisWords];
-  const int qb = blockIdx.x, b = blockIdx.y;
+  const int qb = blockIdx.x, b = blockIdx.y, word = blockIdx.z;
   const int S = a.S, SK = a.S_k;
   const int blk0 = qb * BM;
   const int row_end = min(blk0 + BM, S);
   const int kv_n = a.kv_lens ? min(max(a.kv_lens[b], 0), SK) : SK;
   const int n_tiles = block_key_tiles(row_end, S, SK, kv_n, a.causal);
-  if (n_tiles == 0 || n_tiles > kVisWords * 32) return;  // uniform over the workgroup
+  // uniform over the workgroup
+  if (n_tiles == 0 || n_tiles > kVisWords * 32 || 32 * word >= n_tiles) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const __amdgpu_buffer_rsrc_t mrsrc =
       make_rsrc(a.mask + ((size_t)b * S + blk0) * SK, (int)((unsigned)(row_end - blk0) * (unsigned)SK));
-  scan_mask_tiles<BM>(mrsrc, n_tiles, row_end - blk0, SK, vis, full, wave, lane, tid);
-  uint32_t* dst = const_cast<uint32_t*>(a.mask_tiles) + ((size_t)b * a.n_qb + qb) * 2 * a.mt_words;
-  for (int i = tid; i < (n_tiles + 31) / 32; i += kWaves * 64) {
-    dst[i] = vis[i];
-    dst[a.mt_words + i] = full[i];
+  scan_mask_tiles<BM>(mrsrc, 32 * word, min(n_tiles, 32 * word + 32), row_end - blk0, SK, vis, full, wave, lane,
+                      tid);
+  if (tid == 0) {
+    uint32_t* dst = const_cast<uint32_t*>(a.mask_tiles) + ((size_t)b * a.n_qb + qb) * 2 * a.mt_words;
+    dst[word] = vis[word];
+    dst[a.mt_words + word] = full[word];
   }
 }
 
@@ -896,7 +912,7 @@ static hipError_t launch_mask_tiles(PrefillArgs& a, uint32_t* mask_tiles, int HC
   if (!a.mask || !mask_tiles) return hipSuccess;
   a.mask_tiles = mask_tiles;
   a.mt_words = mask_tile_words(a.S_k);
-  const dim3 grid(a.n_qb, a.B), block(kWaves * 64);
+  const dim3 grid(a.n_qb, a.B, a.mt_words), block(kWaves * 64);
   switch (kWaves / HC) {
     case 1: hipLaunchKernelGGL((gqa_mask_tiles_kernel<32>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((gqa_mask_tiles_kernel<64>), grid, block, 0, stream, a); break;
