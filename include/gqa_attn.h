@@ -368,8 +368,9 @@ gqa_status attn_prefill_ws(const gqa_attn_desc* d, const void* q, const void* k,
                            const int32_t* kv_lens, const uint8_t* mask, float scale, void* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes attn_prefill_ws needs for a dense mask (host only): 2 bits
- * per (row block, key tile); 0 for an invalid descriptor. */
+/* Workspace bytes attn_prefill_ws needs for a dense mask (host only): per
+ * (batch entry, row block), two bitmaps of one bit per 64-key tile in 32-bit
+ * words (at most 256 words each); 0 for an invalid descriptor. */
 size_t attn_prefill_workspace_bytes(const gqa_attn_desc* d);
 
 /* -------------------------------------------------------- measurement --
