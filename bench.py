@@ -507,6 +507,9 @@ def kernel_identity(name):
     return base.split("::")[-1].strip(), targs
 
 
+PREFILL_PERSISTENT_WGS = 256  # the prefill kernels without a dense mask launch one workgroup per CU of an MI355X
+
+
 def _workload_launches():
     """[((kernel, template args, grid threads), (counter key, workload, algorithmic bytes or flops, unit))].
 
@@ -573,7 +576,7 @@ def _workload_launches():
         hc = math.gcd(G, 8)
         bm = 32 * (8 // hc)
         n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S // bm))
-        grid = -(-n_wg // 8) * 8 * 512
+        grid = min(-(-n_wg // 8) * 8, PREFILL_PERSISTENT_WGS) * 512  # one workgroup per CU, looping over row blocks
         out.append((("gqa_prefill_causal_kernel", (str(wl.d_h), str(hc)), grid),
                     (f"prefill_causal:{wl.name}", wl.name, roofline.prefill_causal_flops(wl.B, wl.S, wl.h_q, wl.d_h),
                      "flops")))
@@ -582,7 +585,8 @@ def _workload_launches():
         hc = math.gcd(G, 8)
         bm = 32 * (8 // hc)
         n_wg = wl.B * wl.n_kv * (G // hc) * (-(-wl.S_q // bm))
-        grid = -(-n_wg // 8) * 8 * 512
+        grid = -(-n_wg // 8) * 8  # with a dense mask one workgroup per row block, else one per CU
+        grid = (grid if wl.mask else min(grid, PREFILL_PERSISTENT_WGS)) * 512
         lens = inputs.draw_lengths(wl.B, *wl.kv_lens, wl.seed) if wl.kv_lens else None
         mask = inputs.draw_mask(wl.mask, wl.B, wl.S_q, wl.S_k, wl.seed, wl.doc_lens) if wl.mask else None
         pairs = roofline.visible_pairs(wl.B, wl.S_q, wl.S_k, wl.causal, lens, mask)

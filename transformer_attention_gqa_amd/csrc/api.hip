@@ -462,7 +462,7 @@ gqa_status attn_prefill_causal(const gqa_prefill_desc* d, const void* q, const v
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return GQA_ERR_ALIGN;
   if (bad_scale(scale)) return GQA_ERR_VALUE;
   hipError_t e = launch_prefill_causal(q, k, v, out, qk_scale_log2(scale), d->B, d->S, d->h_q, d->n_kv, d->d_h,
-                                       stream);
+                                       device_compute_units(), stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;
@@ -601,9 +601,9 @@ gqa_status prefill_general(const gqa_attn_desc* d, const void* q, const void* k,
   const float sl2 = qk_scale_log2(scale);
   const hipError_t e =
       fp8 ? launch_prefill_fp8(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal, kv_lens, mask,
-                               q_descale, k_descale, v_descale, mask_tiles, stream)
+                               q_descale, k_descale, v_descale, mask_tiles, device_compute_units(), stream)
           : launch_prefill_masked(q, k, v, out, sl2, d->B, d->S_q, d->S_k, d->h_q, d->n_kv, d->d_h, d->causal,
-                                  kv_lens, mask, mask_tiles, stream);
+                                  kv_lens, mask, mask_tiles, device_compute_units(), stream);
   if (e != hipSuccess) {
     record_hip_error(e);
     return GQA_ERR_HIP;

@@ -69,7 +69,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int D, int hb, int kind, int
 hipError_t launch_mla_decode_split(const MlaArgs& a, int D, int hb, int W, hipStream_t stream);
 hipError_t launch_decode_combine(const CombineArgs& c, int D, bool out_bf16, hipStream_t stream);
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
-                                 int S, int h_q, int n_kv, int D, hipStream_t stream);
+                                 int S, int h_q, int n_kv, int D, int n_cu, hipStream_t stream);
 // General masks: S_q query rows, S_k keys, optional end-aligned causal rule,
 // key lengths [B] and dense mask [B][S_q][S_k] (nonzero = visible).  With a
 // mask and mask_tiles (prefill_mask_tiles_bytes bytes), a pass over the mask
@@ -77,12 +77,12 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
 // workgroup scans its own mask rows.
 hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
-                                 const uint8_t* mask, uint32_t* mask_tiles, hipStream_t stream);
+                                 const uint8_t* mask, uint32_t* mask_tiles, int n_cu, hipStream_t stream);
 // fp8 (e4m3) q/k/v with per-(batch, head) descale factors, d = 64 or 128, general masks.
 hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                               int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                               const uint8_t* mask, const float* q_descale, const float* k_descale,
-                              const float* v_descale, uint32_t* mask_tiles, hipStream_t stream);
+                              const float* v_descale, uint32_t* mask_tiles, int n_cu, hipStream_t stream);
 // Bytes of the key-tile bitmaps of all row blocks (see launch_prefill_masked).
 size_t prefill_mask_tiles_bytes(int B, int S_q, int S_k, int h_q, int n_kv);
 

@@ -204,83 +204,153 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   __shared__ __attribute__((aligned(16))) char sm0[MASK_BYTES];
   __shared__ __attribute__((aligned(16))) char sm1[MASK_BYTES];
 
-  // ---- XCD-aware, heavy-first workgroup -> work mapping
-  const int n = blockIdx.x;
-  const int per_xcd = a.n_wg_pad / kNumXcd;
-  const int wl = (n % kNumXcd) * per_xcd + n / kNumXcd;
-  if (wl >= a.n_wg) return;
-  // groups (batch, K/V head, head chunk) are taken grp_block at a time; inside
-  // such a block the row blocks run heaviest first with the block's groups
-  // interleaved, so workgroups that read the same rows of a dense mask (every
-  // group of a batch entry does) run side by side on one XCD and share them
-  // in its L2.  grp_block = 1 keeps each group's row blocks together, which
-  // keeps its K/V in L2.
-  int grp, qb;
-  if (a.grp_block <= 1) {
-    grp = wl / a.n_qb;
-    qb = a.n_qb - 1 - (wl - grp * a.n_qb);
-  } else {
-    const int span = a.grp_block * a.n_qb;
-    const int blk = wl / span;
-    const int r = wl - blk * span;
-    const int ng = min(a.grp_block, a.n_wg / a.n_qb - blk * a.grp_block);  // groups in this block
-    const int qr = r / ng;
-    grp = blk * a.grp_block + (r - qr * ng);
-    qb = a.n_qb - 1 - qr;
-  }
-  // batch entry fastest: the groups one XCD takes come from every batch
-  // entry, so batch entries of unequal work (key lengths, documents) spread
-  // over all XCDs instead of loading the XCDs they land on
-  int hc, g, b;
-  if (a.batch_minor) {
-    b = grp % a.B;
-    hc = (grp / a.B) % a.n_hc;
-    g = grp / (a.B * a.n_hc);
-  } else {
-    hc = grp % a.n_hc;
-    g = (grp / a.n_hc) % a.n_kv;
-    b = grp / (a.n_hc * a.n_kv);
-  }
-  const int G = a.h_q / a.n_kv;
-
+  // Without a dense mask a workgroup loops over several row blocks (one per
+  // compute unit is launched) and issues the next block's first K/V tile and
+  // its Q rows during the current block's last step, so neither the launch of
+  // a new workgroup nor those first loads sit between two blocks.
+  constexpr bool PERSIST = !(GEN && MASK);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar addresses and M0
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
-  const int head = g * G + hc * HC + wave / RB;
-  const int row0 = qb * BM + (wave % RB) * 32;
-  const int qrow = row0 + l32;  // this lane's query row
   const int S = a.S;                     // query rows
   const int SK = GEN ? a.S_k : a.S;      // keys
   const size_t q_row_stride = (size_t)a.h_q * D;   // elements between consecutive tokens of q/out
   const size_t kv_row_bytes = (size_t)a.n_kv * ROWB;
+  const int G = a.h_q / a.n_kv;
+
+  // ---- XCD-aware, heavy-first work order.  Item wl (a row block of one
+  // group) is numbered so that each XCD's share [x * per_xcd, (x+1) *
+  // per_xcd) runs heaviest first.  Groups (batch, K/V head, head chunk) are
+  // taken grp_block at a time; inside such a block the row blocks run
+  // heaviest first with the block's groups interleaved, so workgroups that
+  // read the same rows of a dense mask (every group of a batch entry does)
+  // run side by side on one XCD and share them in its L2.  grp_block = 1
+  // keeps each group's row blocks together, which keeps its K/V in L2.
+  auto item_of = [&](int wl) {
+    int grp, qb;
+    if (a.grp_block <= 1) {
+      grp = wl / a.n_qb;
+      qb = a.n_qb - 1 - (wl - grp * a.n_qb);
+    } else {
+      const int span = a.grp_block * a.n_qb;
+      const int blk = wl / span;
+      const int r = wl - blk * span;
+      const int ng = min(a.grp_block, a.n_wg / a.n_qb - blk * a.grp_block);  // groups in this block
+      const int qr = r / ng;
+      grp = blk * a.grp_block + (r - qr * ng);
+      qb = a.n_qb - 1 - qr;
+    }
+    // batch entry fastest: the groups one XCD takes come from every batch
+    // entry, so batch entries of unequal work (key lengths) spread over all
+    // XCDs instead of loading the XCDs they land on
+    const int b = a.batch_minor ? grp % a.B : grp / (a.n_hc * a.n_kv);
+    const int hc = a.batch_minor ? (grp / a.B) % a.n_hc : grp % a.n_hc;
+    const int g = a.batch_minor ? grp / (a.B * a.n_hc) : (grp / a.n_hc) % a.n_kv;
+    return int4{b, g, hc, qb};
+  };
+  // Workgroup n runs on XCD n % 8 and is the c-th of the C there; it takes
+  // the XCD's items c, 2C - 1 - c, 2C + c, ... (one per round, alternating
+  // direction, so the heavy-first order spreads evenly).  With one
+  // workgroup per item (C = per_xcd) that is item c alone.
+  const int per_xcd = a.n_wg_pad / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd, cw = blockIdx.x / kNumXcd, C = gridDim.x / kNumXcd;
+  int round = 0;
+  auto next_wl = [&]() {  // the workgroup's next item, or -1
+    for (;;) {
+      const int idx = round * C + ((round & 1) ? C - 1 - cw : cw);
+      ++round;
+      if (idx >= per_xcd) return -1;
+      const int wl = xcd * per_xcd + idx;
+      if (wl < a.n_wg) return wl;
+    }
+  };
 
   // ---- Q fragments (B operand of S^T = K Q^T).  bf16: Q[qrow][16ks + 8h2 ..
   // +7]; fp8: Q[qrow][64ks + 32h2 .. +31] (the K fragments take the same k order)
   u32x4 qf[F8 ? 1 : KS];
   i32x8 qf8[F8 ? KS8 : 1];
-  float qk_log2 = a.qk_scale_log2, out_scale = 1.0f;
-  if constexpr (!F8) {
-    const uint16_t* qp = a.q + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D + 8 * h2;
+  // rows past S load row S - 1 (every lane issues the same loads) and are
+  // zeroed by zero_q_past_end once the loads have landed
+  auto load_q = [&](int b, int qrow, int head) {
+    const int qr = min(qrow, S - 1);
+    if constexpr (!F8) {
+      const uint16_t* qp = a.q + ((size_t)b * S + qr) * q_row_stride + (size_t)head * D + 8 * h2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow < S) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      qf[ks] = v;
-    }
-  } else {
-    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D +
-                     32 * h2;
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+    } else {
+      const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)b * S + qr) * q_row_stride +
+                       (size_t)head * D + 32 * h2;
 #pragma unroll
-    for (int ks = 0; ks < KS8; ++ks) {
-      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (qrow < S) {
-        lo = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
-        hi = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
+      for (int ks = 0; ks < KS8; ++ks) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(qp + 64 * ks);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 16);
+        qf8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
-      qf8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
+  };
+  auto zero_q_past_end = [&](int qrow) {
+    if (qrow < S) return;
+    if constexpr (!F8) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks) qf8[ks] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
+  // The next item's Q rows (persistent kernels) go straight into LDS, 32
+  // rows per wave, during the current item's last step: 16-byte chunk c of
+  // row r at chunk position c ^ (r % QCH), so the fragment reads spread over
+  // the banks.  Rows past S are past the copy's buffer range and read as 0.
+  constexpr int QROWB = D * EB;    // bytes of one head's row of Q
+  constexpr int QCH = QROWB / 16;  // 16-byte chunks per row
+  constexpr int RPQ = 64 / QCH;    // rows per copy instruction
+  __shared__ __attribute__((aligned(16))) char sq[PERSIST ? kWaves * 32 * QROWB : 16];
+  char* const sq_w = sq + (PERSIST ? wave * 32 * QROWB : 0);
+  auto dma_q = [&](int b_n, int row0_n, int head_n) {
+    const int nvalid = min(32, S - row0_n);
+    const unsigned q_row_bytes = (unsigned)(q_row_stride * EB);
+    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)b_n * S + row0_n) * q_row_bytes + (size_t)head_n * QROWB;
+    const auto rs = make_rsrc(nvalid > 0 ? qb : reinterpret_cast<const char*>(a.q),
+                              nvalid > 0 ? (int)((unsigned)(nvalid - 1) * q_row_bytes + QROWB) : 0);
+    const int rl = lane / QCH, p = lane % QCH;
+#pragma unroll
+    for (int u = 0; u < 32 / RPQ; ++u) {
+      const int r = RPQ * u + rl;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sq_w + RPQ * u * QROWB), 16,
+                                               (unsigned)r * q_row_bytes + (unsigned)((p ^ (r % QCH)) << 4), 0, 0, 0);
+    }
+  };
+  auto q_from_lds = [&]() {
+    const char* qr = sq_w + l32 * QROWB;
+    const int qs = l32 % QCH;
+    if constexpr (!F8) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = lds_load<u32x4>(qr + (((2 * ks + h2) ^ qs) << 4));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks) {
+        const u32x4 lo = lds_load<u32x4>(qr + (((4 * ks + 2 * h2) ^ qs) << 4));
+        const u32x4 hi = lds_load<u32x4>(qr + (((4 * ks + 2 * h2 + 1) ^ qs) << 4));
+        qf8[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    }
+  };
+
+  // One row block (item wl).  pref: its Q and first K/V tile (in buffer pair
+  // par) were issued by the previous item.  Returns the buffer pair of the
+  // next item's first tile if this item issued it (with that item's Q), else
+  // -1.
+  auto run_item = [&](const int wl, const int wl_n, const bool pref, const int par) __attribute__((always_inline)) -> int {
+  const int4 it = item_of(wl);
+  const int b = it.x, g = it.y, hc = it.z, qb = it.w;
+  const int head = g * G + hc * HC + wave / RB;
+  const int row0 = qb * BM + (wave % RB) * 32;
+  const int qrow = row0 + l32;  // this lane's query row
+  float qk_log2 = a.qk_scale_log2, out_scale = 1.0f;
+  if constexpr (F8) {
     // a zero descale (an all-zero head quantised by absmax) would make the
     // score factor 0 and turn the -inf of a hidden key into NaN; the smallest
     // normal float keeps hidden keys at -inf and every visible score at zero
@@ -288,6 +358,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     qk_log2 = fmaxf(qk_log2 * (a.q_descale[(size_t)b * a.h_q + head] * a.k_descale[(size_t)b * a.n_kv + g]),
                     __FLT_MIN__);
     out_scale = a.v_descale[(size_t)b * a.n_kv + g];
+  }
+  if (pref) {
+    q_from_lds();
+  } else {
+    load_q(b, qrow, head);
+    zero_q_past_end(qrow);
   }
 
   const int row_end = min(qb * BM + BM, S);        // exclusive, over the whole workgroup
@@ -349,23 +425,24 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   // Raw buffer loads to LDS count only on the vector-memory counter, which
   // leaves the LDS counter to the LDS reads: the compiler can then wait for
   // the reads a product needs instead of all of them.
-  auto tile_rsrc = [&](const char* base, int key0) {
-    const int nvalid = min(kBN, kv_n - key0);  // >= 1 for a visited tile
+  auto tile_rsrc = [&](const char* base, int kvn, int key0) {
+    const int nvalid = min(kBN, kvn - key0);  // >= 1 for a visited tile
     return make_rsrc(base + (size_t)key0 * kv_row_bytes,
                      (int)((unsigned)(nvalid - 1) * (unsigned)kv_row_bytes + ROWB));
   };
-  auto dma_tile = [&](int j, char* kdst, char* vdst) {
+  // tile j of the K/V rows at (kb, vb), key length kvn
+  auto dma_tile_of = [&](const char* kb, const char* vb, int kvn, int j, char* kdst, char* vdst) {
     const int key0 = j * kBN;
     if constexpr (SPLIT_KV) {
       // waves 0 .. kWaves/2 - 1 load K, the others V
       const bool is_k = wave < kWaves / 2;
-      const auto rs = tile_rsrc(is_k ? kbase : vbase, key0);
+      const auto rs = tile_rsrc(is_k ? kb : vb, kvn, key0);
       char* dst = is_k ? kdst : vdst;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + ins_row0(0) * ROWB), 16, dma_off[0], 0, 0, 0);
       return;
     }
-    const auto rk = tile_rsrc(kbase, key0);
-    const auto rv = tile_rsrc(vbase, key0);
+    const auto rk = tile_rsrc(kb, kvn, key0);
+    const auto rv = tile_rsrc(vb, kvn, key0);
 #pragma unroll
     for (int u = 0; u < NINS; ++u) {
       const int r0 = (u * kWaves + wave) * RPI;  // first tile row of this instruction
@@ -373,6 +450,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + r0 * ROWB), 16, dma_off[u], 0, 0, 0);
     }
   };
+  auto dma_tile = [&](int j, char* kdst, char* vdst) { dma_tile_of(kbase, vbase, kv_n, j, kdst, vdst); };
   auto dma_wait = [&]() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   f32x16 o[NT];
@@ -478,22 +556,56 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) *reinterpret_cast<u32x2*>(op + 32 * nt + 8 * rq + 4 * h2) = u32x2{0u, 0u};
     }
-    return;
+    return -1;
+  }
+  // the next item (persistent kernels): its first tile and Q are issued in
+  // this item's last step when it has any key to visit (no dense mask here,
+  // so it visits tiles 0 .. n_tiles - 1)
+  bool pf = false;
+  const char* kbase_n = nullptr;
+  const char* vbase_n = nullptr;
+  int kv_n_n = SK, b_n = 0, head_n = 0, row0_n = 0;
+  if constexpr (PERSIST) {
+    if (wl_n >= 0) {
+      const int4 it_n = item_of(wl_n);
+      b_n = it_n.x;
+      const int g_n = it_n.y, hc_n = it_n.z, qb_n = it_n.w;
+      if constexpr (GEN) {
+        if (a.kv_lens) kv_n_n = min(max(a.kv_lens[b_n], 0), SK);
+      }
+      const int row_end_n = min(qb_n * BM + BM, S);
+      const int n_tiles_n = GEN ? block_key_tiles(row_end_n, S, SK, kv_n_n, a.causal) : (row_end_n + kBN - 1) / kBN;
+      pf = n_tiles_n > 0;
+      head_n = g_n * G + hc_n * HC + wave / RB;
+      row0_n = qb_n * BM + (wave % RB) * 32;
+      kbase_n = reinterpret_cast<const char*>(a.k) + ((size_t)b_n * SK * a.n_kv + g_n) * ROWB;
+      vbase_n = reinterpret_cast<const char*>(a.v) + ((size_t)b_n * SK * a.n_kv + g_n) * ROWB;
+    }
   }
   const int j_first = next_tile_of(-1);
-  dma_tile(j_first, sk0, sv0);
-  if (masked_tile(j_first)) dma_mask(j_first, sm0);
-  dma_wait();
-  __syncthreads();
+  const int p0 = pref ? par : 0;  // buffer pair of the first tile
+  if (!pref) {
+    dma_tile(j_first, sk0, sv0);
+    if (masked_tile(j_first)) dma_mask(j_first, sm0);
+    dma_wait();
+    __syncthreads();
+  }
 
   // step k visits key tile j: compute from (kt, vt) while the next visited
   // tile fills (kn, vn); returns that next tile
   auto tile_step = [&](int k, int j, const char* kt, const char* vt, const char* mt, char* kn, char* vn, char* mn) {
     // the other buffer was last read in step k-1, before its closing barrier
     const int jn = next_tile_of(j);
-    if (k + 1 < n_steps) {
+    const bool last = k + 1 == n_steps;
+    if (!last) {
       dma_tile(jn, kn, vn);
       if (masked_tile(jn)) dma_mask(jn, mn);
+    } else if (PERSIST && pf) {
+      // the next item's first tile and Q (this wave's Q reads of sq_w have
+      // returned: its registers fed this item's first products)
+      dma_tile_of(kbase_n, vbase_n, kv_n_n, 0, kn, vn);
+      __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
+      dma_q(b_n, row0_n, head_n);
     }
     const bool tmask = masked_tile(j);  // the mask tile of j is in mt
     const int key0 = j * kBN;
@@ -701,12 +813,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
       // order; the V^T fragment of product i + 2 is read while product i runs
       // (three fragments in flight), so no product waits for the latency of
       // its own LDS reads
-      u32x4 pf[4];
+      u32x4 pw[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const f32x16& sp = sacc[p >> 1];
         const int rb = 8 * (p & 1);
-        pf[p] = u32x4{pack_bf16x2(sp[rb + 0], sp[rb + 1]), pack_bf16x2(sp[rb + 2], sp[rb + 3]),
+        pw[p] = u32x4{pack_bf16x2(sp[rb + 0], sp[rb + 1]), pack_bf16x2(sp[rb + 2], sp[rb + 3]),
                       pack_bf16x2(sp[rb + 4], sp[rb + 5]), pack_bf16x2(sp[rb + 6], sp[rb + 7])};
       }
       const int gi = lane >> 4, s16 = lane & 15;
@@ -731,7 +843,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
           vq[(i + 2) % 3] = vfrag(i + 2);
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the reads for product i + 2,
         }
-        o[i % NT] = mfma32(vq[i % 3], pf[i / NT], o[i % NT]);
+        o[i % NT] = mfma32(vq[i % 3], pw[i / NT], o[i % NT]);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // then product i
       }
       }
@@ -740,10 +852,12 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
     __syncthreads();
     return jn;
   };
+  // step k reads pair (k + p0) & 1: v = k + p0 counts pairs of steps, the
+  // first of which is skipped when the first tile is in pair 1
   int j = j_first;
-  for (int k = 0; k < n_steps; k += 2) {
-    j = tile_step(k, j, sk0, sv0, sm0, sk1, sv1, sm1);
-    if (k + 1 < n_steps) j = tile_step(k + 1, j, sk1, sv1, sm1, sk0, sv0, sm0);
+  for (int v = 0; v < n_steps + p0; v += 2) {
+    if (v >= p0) j = tile_step(v - p0, j, sk0, sv0, sm0, sk1, sv1, sm1);
+    if (v + 1 < n_steps + p0) j = tile_step(v + 1 - p0, j, sk1, sv1, sm1, sk0, sv0, sm0);
   }
 
   // ---- epilogue: O / l -> bf16, rows < S only
@@ -751,41 +865,83 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a) {
   const float inv = lt > 0.f ? out_scale / lt : 0.f;  // fp8: the V descale folds in here
   // Through LDS: a lane holds 8 bytes of each of 16 chunks of its row, so
   // direct stores would touch 32 rows per instruction.  The wave writes its
-  // 32-row tile into its own LDS region (half a K/V buffer, free after the
-  // last step's barrier), in NPASS column slices when the region is smaller
-  // than the tile (fp8 buffers), 16-byte chunk c of row r at chunk position
-  // c ^ (r % CO), and stores whole row slices back, CO lanes per row, 16
-  // bytes each.
-  constexpr int OUT_BYTES = 32 * D * 2;                   // the wave's bf16 output tile
-  constexpr int REGION = OUT_BYTES < TILE_BYTES / 2 ? OUT_BYTES : TILE_BYTES / 2;
+  // 32-row tile into its own LDS region and stores whole row slices back, CO
+  // lanes per row, 16 bytes each (16-byte chunk c of row r at chunk position
+  // c ^ (r % CO)), in NPASS column slices when the region is smaller than
+  // the tile.  The regions are free after the last step's barrier: with a
+  // next item the output goes through the buffer pair the last step read (the
+  // other holds the next item's first tile), four waves to a buffer;
+  // otherwise through both pairs, two waves to a buffer.
+  constexpr int OUT_BYTES = 32 * D * 2;  // the wave's bf16 output tile
+  constexpr int WPB = PERSIST ? 4 : 2;   // waves per buffer
+  constexpr int REGION = OUT_BYTES < TILE_BYTES / WPB ? OUT_BYTES : TILE_BYTES / WPB;
   constexpr int NPASS = OUT_BYTES / REGION;
-  constexpr int DP = D / NPASS;                           // columns per pass
-  constexpr int CO = DP / 8;                              // 16-byte chunks per row slice
-  constexpr int RPS = 64 / CO;                            // rows per store instruction
-  static_assert(NPASS * REGION == OUT_BYTES && (NT / NPASS) * NPASS == NT, "output passes split the d tiles");
-  char* ep = (wave < 2 ? sk0 : wave < 4 ? sk1 : wave < 6 ? sv0 : sv1) + (wave & 1) * REGION;
+  if constexpr (NPASS <= NT) {
+    constexpr int DP = D / NPASS;  // columns per pass
+    constexpr int CO = DP / 8;     // 16-byte chunks per row slice
+    constexpr int RPS = 64 / CO;   // rows per store instruction
+    static_assert(NPASS * REGION == OUT_BYTES && (NT / NPASS) * NPASS == NT, "output passes split the d tiles");
+    char* ep;
+    if constexpr (PERSIST) {
+      const int y = (n_steps - 1 + p0) & 1;  // the pair the last step read
+      ep = (wave < 4 ? (y ? sk1 : sk0) : (y ? sv1 : sv0)) + (wave & 3) * REGION;
+    } else {
+      ep = (wave < 2 ? sk0 : wave < 4 ? sk1 : wave < 6 ? sv0 : sv1) + (wave & 1) * REGION;
+    }
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
+    for (int ps = 0; ps < NPASS; ++ps) {
 #pragma unroll
-    for (int ntp = 0; ntp < NT / NPASS; ++ntp)
+      for (int ntp = 0; ntp < NT / NPASS; ++ntp)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int nt = ps * (NT / NPASS) + ntp;
+          const int c = 4 * ntp + rq;  // chunk of d 32nt + 8rq .. +7 in this slice
+          u32x2 w;
+          w[0] = pack_bf16x2(o[nt][4 * rq + 0] * inv, o[nt][4 * rq + 1] * inv);
+          w[1] = pack_bf16x2(o[nt][4 * rq + 2] * inv, o[nt][4 * rq + 3] * inv);
+          *reinterpret_cast<u32x2*>(ep + l32 * (DP * 2) + ((c ^ (l32 % CO)) << 4) + 8 * h2) = w;
+        }
+      const int c = lane % CO;
+#pragma unroll
+      for (int t = 0; t < 32 / RPS; ++t) {
+        const int r = RPS * t + lane / CO;
+        const u32x4 v = lds_load<u32x4>(ep + r * (DP * 2) + ((c ^ (r % CO)) << 4));
+        if (row0 + r < S)
+          *reinterpret_cast<u32x4*>(a.out + ((size_t)b * S + row0 + r) * q_row_stride + (size_t)head * D + ps * DP +
+                                    8 * c) = v;
+      }
+    }
+  } else if (qrow < S) {  // fp8 at d = 64 with a next item: regions too small, direct stores
+    uint16_t* op = a.out + ((size_t)b * S + qrow) * q_row_stride + (size_t)head * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int nt = ps * (NT / NPASS) + ntp;
-        const int c = 4 * ntp + rq;  // chunk of d 32nt + 8rq .. +7 in this slice
         u32x2 w;
         w[0] = pack_bf16x2(o[nt][4 * rq + 0] * inv, o[nt][4 * rq + 1] * inv);
         w[1] = pack_bf16x2(o[nt][4 * rq + 2] * inv, o[nt][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(ep + l32 * (DP * 2) + ((c ^ (l32 % CO)) << 4) + 8 * h2) = w;
+        *reinterpret_cast<u32x2*>(op + 32 * nt + 8 * rq + 4 * h2) = w;
       }
-    const int c = lane % CO;
-#pragma unroll
-    for (int t = 0; t < 32 / RPS; ++t) {
-      const int r = RPS * t + lane / CO;
-      const u32x4 v = lds_load<u32x4>(ep + r * (DP * 2) + ((c ^ (r % CO)) << 4));
-      if (row0 + r < S)
-        *reinterpret_cast<u32x4*>(a.out + ((size_t)b * S + row0 + r) * q_row_stride + (size_t)head * D + ps * DP +
-                                  8 * c) = v;
+  }
+  if constexpr (PERSIST) {
+    if (wl_n >= 0) {
+      // the next item's first step refills the pair read here
+      __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ __volatile__("" ::: "memory");
     }
+  }
+  return pf ? ((n_steps + p0) & 1) : -1;
+  };  // run_item
+
+  bool pref = false;
+  int par = 0;
+  for (int wl = next_wl(); wl >= 0;) {
+    const int wl_n = PERSIST ? next_wl() : -1;
+    const int np = run_item(wl, wl_n, pref, par);
+    pref = np >= 0;
+    par = pref ? np : 0;
+    wl = wl_n;
   }
 }
 
@@ -845,6 +1001,14 @@ static int gcd_int(int x, int y) {
   return x;
 }
 
+// Workgroups of a kernel without a dense mask: one per compute unit (a
+// multiple of the 8 XCDs), each looping over its share of the row blocks,
+// or one per row block when there are fewer.
+static int persistent_grid(const PrefillArgs& a, int n_cu) {
+  const int per_cu = max(n_cu / kNumXcd, 1) * kNumXcd;
+  return min(a.n_wg_pad, per_cu);
+}
+
 static PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* out, float qk_scale_log2,
                                 int B, int S, int h_q, int n_kv, int HC) {
   const int G = h_q / n_kv;
@@ -878,10 +1042,10 @@ static PrefillArgs prefill_args(const void* q, const void* k, const void* v, voi
 }
 
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
-                                 int S, int h_q, int n_kv, int D, hipStream_t stream) {
+                                 int S, int h_q, int n_kv, int D, int n_cu, hipStream_t stream) {
   const int HC = gcd_int(h_q / n_kv, kWaves);
   const PrefillArgs a = prefill_args(q, k, v, out, qk_scale_log2, B, S, h_q, n_kv, HC);
-  const dim3 grid(a.n_wg_pad), block(kWaves * 64);
+  const dim3 grid(persistent_grid(a, n_cu)), block(kWaves * 64);
 #define GQA_LAUNCH_PREFILL(DD, HH) hipLaunchKernelGGL((gqa_prefill_causal_kernel<DD, HH>), grid, block, 0, stream, a)
   if (D == 128) {
     if (HC == 8) GQA_LAUNCH_PREFILL(128, 8);
@@ -936,7 +1100,7 @@ static void set_work_order(PrefillArgs& a) {
 
 hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                                  int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
-                                 const uint8_t* mask, uint32_t* mask_tiles, hipStream_t stream) {
+                                 const uint8_t* mask, uint32_t* mask_tiles, int n_cu, hipStream_t stream) {
   const int HC = gcd_int(h_q / n_kv, kWaves);
   PrefillArgs a = prefill_args(q, k, v, out, qk_scale_log2, B, S_q, h_q, n_kv, HC);
   a.S_k = S_k;
@@ -945,7 +1109,7 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
   a.mask = mask;
   if (const hipError_t e = launch_mask_tiles(a, mask_tiles, HC, stream); e != hipSuccess) return e;
   set_work_order(a);
-  const dim3 grid(a.n_wg_pad), block(kWaves * 64);
+  const dim3 grid(mask ? a.n_wg_pad : persistent_grid(a, n_cu)), block(kWaves * 64);
 #define GQA_LAUNCH_PREFILL(DD, HH)                                                                       \
   do {                                                                                                   \
     if (mask) hipLaunchKernelGGL((gqa_prefill_masked_kernel<DD, HH, true>), grid, block, 0, stream, a);  \
@@ -969,7 +1133,7 @@ hipError_t launch_prefill_masked(const void* q, const void* k, const void* v, vo
 hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void* out, float qk_scale_log2, int B,
                               int S_q, int S_k, int h_q, int n_kv, int D, int causal, const int32_t* kv_lens,
                               const uint8_t* mask, const float* q_descale, const float* k_descale,
-                              const float* v_descale, uint32_t* mask_tiles, hipStream_t stream) {
+                              const float* v_descale, uint32_t* mask_tiles, int n_cu, hipStream_t stream) {
   const int HC = gcd_int(h_q / n_kv, kWaves);
   PrefillArgs a = prefill_args(q, k, v, out, qk_scale_log2, B, S_q, h_q, n_kv, HC);
   a.S_k = S_k;
@@ -981,7 +1145,7 @@ hipError_t launch_prefill_fp8(const void* q, const void* k, const void* v, void*
   a.v_descale = v_descale;
   if (const hipError_t e = launch_mask_tiles(a, mask_tiles, HC, stream); e != hipSuccess) return e;
   set_work_order(a);
-  const dim3 grid(a.n_wg_pad), block(kWaves * 64);
+  const dim3 grid(mask ? a.n_wg_pad : persistent_grid(a, n_cu)), block(kWaves * 64);
 #define GQA_LAUNCH_FP8(DD, HH)                                                                          \
   do {                                                                                                  \
     if (mask) hipLaunchKernelGGL((gqa_prefill_fp8_kernel<DD, HH, true>), grid, block, 0, stream, a);    \
