@@ -160,3 +160,20 @@ def test_full_size_workload_every_block():
     print(f"[prefill-full] max abs err {err:.3e}", flush=True)
     assert err <= TOL, f"max abs err {err}"
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("B,S,h_q,n_kv,d", [(96, 100, 16, 4, 128), (40, 300, 8, 8, 64), (300, 40, 8, 1, 128)])
+def test_workgroups_take_several_row_blocks(B, S, h_q, n_kv, d):
+    """More row blocks than compute units (600-768 here): a workgroup takes
+    several, and each next block's first K/V tile and Q rows arrive during the
+    current block's last step, in either buffer pair (blocks of one and two
+    tiles alternate), with rows past the sequence end in the last block.
+    Every output element against the oracle."""
+    w = pwl(B, S, h_q, n_kv, d, seed=B + S)
+    inp = inputs.make_prefill_inputs(w, device=DEV)
+    print(f"[prefill] {w}", flush=True)
+    out = run(inp)
+    pu.sync()
+    ref = oracle.prefill_causal(*pu.prefill_f64(inp), w.scale)
+    err = pu.max_err(out, ref)
+    assert err <= TOL, f"max abs err {err}"

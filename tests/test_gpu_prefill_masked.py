@@ -271,3 +271,19 @@ def test_full_size_mask_prepass_equals_in_kernel_scan(name):
     b = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, mask_prepass=False, **args)
     pu.sync()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp8", 128), ("fp8", 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_workgroups_take_several_row_blocks(dtype, d, causal):
+    """Without a dense mask a workgroup takes several row blocks (512 here,
+    more than the compute units) and starts the next one's loads early; key
+    lengths include zeros, so blocks with no visible key sit between blocks
+    that have keys in a workgroup's list, and more keys than queries."""
+    B = 128
+    lens = np.random.default_rng(11).integers(0, 151, B)
+    lens[::7] = 0
+    w = wl(B, 70, 150, 8, 2, d, causal, seed=600 + d, dtype=dtype)
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=lens.tolist(), poison_padding=True)
+    out = check(inp)
+    assert torch.count_nonzero(out[0]) == 0
