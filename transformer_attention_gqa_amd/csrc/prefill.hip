@@ -78,7 +78,8 @@ constexpr int kWaves = 8;  // wavefronts per workgroup
 // scanned (bits of other tiles stay clear).  The rows are read in order: a
 // load instruction covers 1 KiB of one row (16 tiles, four lanes a tile), each
 // wave takes BM / kWaves rows and issues the loads of two 16-tile segments of
-// all its rows before it uses any; the four lanes of a tile then combine by
+// all its rows before it uses any (lanes of tiles past the range load
+// nothing); the four lanes of a tile then combine by
 // shuffles, and the waves by LDS atomics (OR into vis, and into full as
 // "some byte is zero" bits, inverted at the end).  Called by all kWaves waves
 // of the workgroup.
@@ -107,7 +108,9 @@ __device__ void scan_mask_tiles(__amdgpu_buffer_rsrc_t mrsrc, int j_begin, int j
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const unsigned off = (unsigned)r * (unsigned)SK + (unsigned)((s0 + u) * 16 * kBN + 16 * lane);
-          const u32x4 mv = buffer_load_x4(mrsrc, off);  // past the last segment: unused
+          // lanes of tiles past the range load nothing
+          u32x4 mv = {0u, 0u, 0u, 0u};
+          if ((s0 + u) * 16 + (lane >> 2) < j_end) mv = buffer_load_x4(mrsrc, off);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             any[u] |= mv[e];
