@@ -125,6 +125,35 @@ def test_paged_decode_graph_replays():
             assert pu.max_err(got, pu.oracle_decode_full(step.base)) <= pu.TOL["bf16"]
 
 
+def test_mla_decode_graph_replays():
+    w = inputs.MlaWorkload("graph", B=5, h_q=32, d_c=512, S_max=500, lens=(1, 500), seed=645)
+    static = inputs.make_mla_inputs(w, device=DEV)
+    ws = torch.empty(binding.attn_decode_mla_workspace_bytes(binding.mla_desc(static.q, static.c_kv, 0)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(static.q)
+
+    def call():
+        binding.attn_decode_mla(static.q, static.c_kv, static.seq_lens, w.scale, out=out, workspace=ws)
+
+    g = capture(call)
+    for r in range(REPLAYS):
+        step = inputs.make_mla_inputs(w, device=DEV, seed=w.seed + 1 + r)
+        print(f"[graph-mla] replay {r} lens={step.seq_lens.tolist()}", flush=True)
+        for name in ("q", "c_kv", "seq_lens"):
+            getattr(static, name).copy_(getattr(step, name))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = binding.attn_decode_mla(step.q, step.c_kv, step.seq_lens, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(got), bits(ref)), f"replay {r} differs from the eager call"
+        if r == 0:
+            want = oracle.mla_decode(pu.to_f64(step.q), pu.to_f64(step.c_kv), step.seq_lens.cpu().numpy(), w.scale)
+            assert pu.max_err(got, want) <= pu.TOL["bf16"]
+
+
 def test_causal_prefill_graph_replays():
     w = inputs.PrefillWorkload("graph", B=2, S=700, h_q=16, n_kv=4, d_h=128, seed=650)
     static = inputs.make_prefill_inputs(w, device=DEV)
