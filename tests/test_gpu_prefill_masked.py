@@ -106,6 +106,29 @@ def test_dense_masks(causal, kind):
     assert torch.count_nonzero(out[0, 5]) == 0 and torch.count_nonzero(out[1, 200]) == 0
 
 
+def test_more_key_tiles_than_the_bitmaps_hold():
+    """524,588 keys (8,197 tiles of 64, more than the 8,192 the key-tile
+    bitmaps hold): both entry points then visit every tile with the
+    per-element mask.  Each row sees eight scattered keys, one of them in the
+    last 300 (past the bitmaps' range), so the outputs are averages of a few
+    value rows and a dropped or misplaced tile shows."""
+    S_q, S_k = 40, 8192 * 64 + 300
+    w = wl(1, S_q, S_k, 2, 1, 64, True, seed=445)
+    g = torch.Generator().manual_seed(445)
+    m = torch.zeros((1, S_q, S_k), dtype=torch.uint8)
+    cols = torch.randint(0, S_k - 300, (S_q, 7), generator=g)
+    m[0, torch.arange(S_q)[:, None], cols] = 1
+    m[0, torch.arange(S_q), S_k - 300 + torch.randint(0, 300 - S_q, (S_q,), generator=g)] = 1
+    inp = inputs.make_masked_prefill_inputs(w, device=DEV, mask=m)
+    print(f"[prefill_masked] {w} (scattered visible keys)", flush=True)
+    a = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, causal=True, mask=inp.mask)
+    b = binding.attn_prefill(inp.q, inp.k, inp.v, w.scale, causal=True, mask=inp.mask, mask_prepass=False)
+    pu.sync()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert float(a.float().abs().mean()) > 0.1  # averages of a few rows, not of many
+    compare(inp, a)
+
+
 def test_mask_with_more_keys_than_queries_d64():
     w = wl(2, 96, 300, 4, 4, 64, True, seed=440, mask="random")
     check(inputs.make_masked_prefill_inputs(w, device=DEV, kv_lens=[300, 250]))
